@@ -1,0 +1,51 @@
+"""Oracle for the verify pass's linear layers, in fp64 (test infrastructure).
+
+The verify pass feeds the K+1 positions of every sequence through each target
+linear in one read of the weights: the activations form an [M x d_in] tile
+with M = B*(K+1) rows, and each linear computes y = x . W^T with W stored as
+[d_out][d_in] ("What Actually Happens During Speculative Decoding in LLMs":
+a [5 x d] matrix multiplied against the weights instead of a [1 x d] vector;
+"Speculative Decoding: Guess Several Tokens, Check Them in One Pass", Step 1).
+
+Inputs are bfloat16 bit patterns (uint16). Widening bf16 -> fp64 is exact and
+every bf16*bf16 product is exact in fp64, so the only error is the fp64
+summation (relative error below d_in * 2^-53).
+"""
+
+import numpy as np
+
+
+def bf16_to_f64(bits):
+    """Exact value of bfloat16 bit patterns, as float64.
+
+    A bfloat16 is the upper half of an IEEE float32: placing the 16 bits in
+    the high half of a 32-bit word gives the float32 with the same value.
+    """
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def linear(x_bits, w_bits, block_bytes=64 << 20):
+    """y[m][n] = sum_k x[m][k] * w[n][k] in float64.
+
+    x_bits: uint16 [M][d_in] bf16 activations (one row per verify position).
+    w_bits: uint16 [d_out][d_in] bf16 weights (nn.Linear layout).
+    Returns float64 [M][d_out].
+
+    The weights are widened one block of rows at a time so that a 1 GB bf16
+    matrix never becomes a 4 GB fp64 copy; each block is a plain fp64 matrix
+    product (a library primitive), with no other reordering.
+    """
+    x_bits = np.asarray(x_bits)
+    w_bits = np.asarray(w_bits)
+    if x_bits.ndim != 2 or w_bits.ndim != 2 or x_bits.shape[1] != w_bits.shape[1]:
+        raise ValueError(f"shape mismatch: x {x_bits.shape}, w {w_bits.shape}")
+    x = bf16_to_f64(x_bits)
+    m, d_in = x.shape
+    d_out = w_bits.shape[0]
+    y = np.empty((m, d_out), dtype=np.float64)
+    rows = max(1, block_bytes // (8 * max(d_in, 1)))
+    for n0 in range(0, d_out, rows):
+        w = bf16_to_f64(w_bits[n0:n0 + rows])
+        y[:, n0:n0 + rows] = x @ w.T
+    return y
