@@ -1,0 +1,205 @@
+/*
+ * spec_verify.h -- C ABI of libspecverify.so: the verification step of
+ * speculative decoding on one AMD Instinct MI355X (gfx950).
+ *
+ * One verify step of speculative decoding feeds K+1 positions per sequence
+ * (the last accepted token plus K draft tokens) through the target's linear
+ * layers in a single read of the weights, then runs speculative sampling at
+ * every position: softmax the target logits p and the draft logits q, accept
+ * draft token x with probability min(1, p(x)/q(x)), stop at the first
+ * rejection and resample there from norm(max(0, p - q)), or draw a bonus
+ * token from p_{K+1} if every draft survived ("Speculative Decoding: Two
+ * Models, One Voice", The idea, steps 1-3; "Speculative Decoding: Guess
+ * Several Tokens, Check Them in One Pass", Steps 1-3).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every data pointer is a DEVICE pointer to row-major, contiguous memory
+ *   owned by the caller. The library allocates no memory, keeps no state
+ *   beyond a per-device property cache and a thread-local error string, and
+ *   never synchronizes: work is queued on `stream` (a hipStream_t; NULL is
+ *   the null stream) and outputs are valid once the caller has synchronized
+ *   that stream. Every call can be captured into a HIP graph.
+ * - bf16 data are passed as uint16_t bit patterns (IEEE bfloat16).
+ * - Rows and indices: B sequences, K draft tokens (1 <= K <= 64), V the
+ *   vocabulary. Target rows are [B][K+1][V]: row j of sequence b is the
+ *   target's distribution for the slot after the last accepted token and the
+ *   drafts x_1..x_j. Draft rows are [B][K][V]: row j is q_{j+1}, the
+ *   distribution draft token x_{j+1} was drawn from.
+ * - Randomness is supplied by the caller as uniforms in [0, 1):
+ *   u_accept[b][j] drives the accept test of draft j; u_sample[b][j] drives
+ *   the sample that ends the round at row j (j = number of accepted drafts),
+ *   and is the only sample uniform consumed per sequence.
+ * - Arguments are validated on the host before any HIP call; a failing call
+ *   launches nothing. Device data are not validated on the host: a draft
+ *   token outside [0, V) is treated as rejected (it cannot have been
+ *   proposed), an n_accepted outside [0, K] yields token -1, and a row with
+ *   no positive weight yields token -1. Device faults surface at the
+ *   caller's synchronize. No C++ exception crosses this ABI.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+
+/* Status codes. */
+#define SPEC_OK 0
+#define SPEC_ERR_INVALID_ARGUMENT (-1) /* null required pointer, bad size or enum */
+#define SPEC_ERR_ALIGNMENT (-2)        /* a pointer lacks the required alignment */
+#define SPEC_ERR_UNSUPPORTED (-3)      /* current device is not gfx950 */
+#define SPEC_ERR_WORKSPACE (-4)        /* workspace too small or misaligned */
+#define SPEC_ERR_HIP (-5)              /* HIP runtime error; see spec_last_error() */
+
+/* Output element types of spec_verify_gemm. */
+#define SPEC_F32 0
+#define SPEC_BF16 1
+
+/* ABI version of the loaded library (SPEC_ABI_VERSION at build time). */
+int spec_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* spec_status_string(int status);
+
+/* Message of the last failing call made by this thread ("" if none). The
+ * pointer stays valid until the thread's next library call. */
+const char* spec_last_error(void);
+
+/*
+ * spec_verify_gemm -- one linear layer of the verify pass.
+ *
+ * y[M][d_out] = x[M][d_in] . w[d_out][d_in]^T with bf16 products and fp32
+ * accumulation, reading w exactly once for all M = B*(K+1) rows
+ * ("What Actually Happens During Speculative Decoding in LLMs": the weights
+ * are loaded once and multiplied by a [5 x d] matrix instead of a [1 x d]
+ * vector; "Speculative Decoding: Guess Several Tokens", Step 1).
+ *
+ *   x      bf16 [M][d_in], 16-byte aligned.
+ *   w      bf16 [d_out][d_in] (nn.Linear layout), 16-byte aligned.
+ *   y      [M][d_out], fp32 (y_dtype = SPEC_F32, 4-byte aligned) or bf16
+ *          rounded to nearest even (SPEC_BF16, 2-byte aligned).
+ *   Limits: 1 <= M <= 65536, 8 <= d_in <= 2^20 with d_in % 8 == 0,
+ *   1 <= d_out <= 2^24.
+ * Small M runs a vector-ALU weight-streaming kernel; M above a measured
+ * crossover runs a bf16 MFMA kernel. Deterministic: the same inputs give
+ * bitwise identical outputs.
+ */
+int spec_verify_gemm(const uint16_t* x, const uint16_t* w, void* y, int y_dtype,
+                     int M, int d_in, int d_out, void* stream);
+
+/*
+ * spec_softmax -- p = softmax(logits) per row, T = 1.
+ *
+ * ("Speculative Decoding: Two Models, One Voice", Implementing it against a
+ * real model: p = softmax(target logits), q = softmax(draft logits).)
+ *
+ *   logits      fp32 [rows][V].
+ *   probs       fp32 [rows][V] or NULL: exp(l - max) / sumexp.
+ *   row_max     fp32 [rows] or NULL: max_v l[v].
+ *   row_sumexp  fp32 [rows] or NULL: sum_v exp(l[v] - max).
+ * One pass over each row keeps a running max and a rescaled running sum; a
+ * second pass writes probs when requested. Whichever outputs are non-NULL
+ * are written. 1 <= rows <= 2^24, 1 <= V <= 2^26.
+ */
+int spec_softmax(const float* logits, int rows, int V, float* probs,
+                 float* row_max, float* row_sumexp, void* stream);
+
+/*
+ * spec_accept_scan -- the accept test and the first rejection.
+ *
+ * For each sequence b and draft j: ratio = p_j(x_j) / q_j(x_j) (+inf if
+ * q_j(x_j) = 0 < p_j(x_j); 0 if both are 0), accepted iff u_accept[b][j] <
+ * ratio, which happens with probability min(1, p/q) ("Speculative
+ * Decoding: Two Models, One Voice", The idea, step 3). n_accepted[b] is the
+ * index of the first rejected draft, or K: later drafts are discarded, so the
+ * accepted tokens form a prefix (same page, The rule that makes it exact).
+ *
+ *   p_probs       fp32 [B][K+1][V]   target probabilities.
+ *   q_probs       fp32 [B][K][V]     draft probabilities.
+ *   draft_tokens  int32 [B][K].
+ *   u_accept      fp32 [B][K].
+ *   n_accepted    int32 [B] (out).
+ *   accept_mask   uint8 [B][K] or NULL (out): 1 where the test passed,
+ *                 including positions after the first rejection.
+ * The ratio is evaluated in fp64. 1 <= B <= 2^20, 1 <= K <= 64, V >= 1.
+ */
+int spec_accept_scan(const float* p_probs, const float* q_probs,
+                     const int32_t* draft_tokens, const float* u_accept,
+                     int B, int K, int V, int32_t* n_accepted,
+                     uint8_t* accept_mask, void* stream);
+
+/*
+ * spec_residual_sample -- the token that ends the round.
+ *
+ * With n = n_accepted[b]: if n < K the token is drawn from
+ * norm(max(0, p_n - q_n)) with u = u_sample[b][n]; if n = K it is the bonus
+ * token drawn from p_K with u = u_sample[b][K] ("Speculative Decoding: Two
+ * Models, One Voice", The idea, step 3). Inverse CDF in ascending token id:
+ * the token is the smallest y whose running weight sum exceeds u * Z (Z the
+ * total weight). If the residual has no mass the draw falls back to p_n and
+ * zero_residual[b] is set ("What Actually Happens During Speculative
+ * Decoding in LLMs", the reference sampler's guard; "Speculative Decoding:
+ * The Algebra and the Proof" warns that p = q leaves nothing to normalise).
+ * Weights and running sums are fp64.
+ *
+ *   p_probs, q_probs  as for spec_accept_scan.
+ *   n_accepted        int32 [B].
+ *   u_sample          fp32 [B][K+1].
+ *   token             int32 [B] (out).
+ *   zero_residual     uint8 [B] or NULL (out).
+ * 1 <= B <= 2^20, 1 <= K <= 64, 1 <= V <= 2^26.
+ */
+int spec_residual_sample(const float* p_probs, const float* q_probs,
+                         const int32_t* n_accepted, const float* u_sample,
+                         int B, int K, int V, int32_t* token,
+                         uint8_t* zero_residual, void* stream);
+
+/* Bytes of device workspace spec_verify needs for (B, K, V); 0 on invalid
+ * arguments. */
+size_t spec_verify_workspace_bytes(int B, int K, int V);
+
+/*
+ * spec_verify -- the whole verify step after the stack: lm-head, softmax,
+ * accept scan, residual or bonus sample, emit.
+ *
+ *   hidden        bf16 [B*(K+1)][d] or NULL; 16-byte aligned.
+ *   lm_head       bf16 [V][d] or NULL; 16-byte aligned. When both are given,
+ *                 target_logits = hidden . lm_head^T (fp32) is computed
+ *                 first; when both are NULL, target_logits is an input.
+ *   d             hidden size (ignored when lm_head is NULL).
+ *   target_logits fp32 [B][K+1][V] (out or in, see above; left readable).
+ *   draft_logits  fp32 [B][K][V].
+ *   draft_tokens  int32 [B][K].
+ *   u_accept      fp32 [B][K].
+ *   u_sample      fp32 [B][K+1].
+ *   out_tokens    int32 [B][K+1] (out): the accepted drafts, then the
+ *                 sampled token, then -1 padding.
+ *   n_emitted     int32 [B] (out): n_accepted + 1, between 1 and K+1
+ *                 ("Speculative Decoding: Two Models, One Voice", Appendix
+ *                 tool 2: every round emits N + 1 tokens).
+ *   workspace     device memory of at least spec_verify_workspace_bytes(B,
+ *                 K, V), 256-byte aligned; its contents are scratch.
+ * Target and draft probabilities are never materialised: per-row max and
+ * sum of exponentials are kept in the workspace and probabilities of the
+ * few tokens the rule touches are evaluated in fp64 from the logits.
+ * Limits as for the calls above, with V <= 2^26 and d as d_in of
+ * spec_verify_gemm.
+ */
+int spec_verify(const uint16_t* hidden, const uint16_t* lm_head, int d,
+                float* target_logits, const float* draft_logits,
+                const int32_t* draft_tokens, const float* u_accept,
+                const float* u_sample, int B, int K, int V,
+                int32_t* out_tokens, int32_t* n_emitted, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

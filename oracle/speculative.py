@@ -31,6 +31,9 @@ design notes of the repository):
 * zero residual mass: fall back to p itself and flag it (the wpnews
   sampler's guard; "The Algebra and the Proof" warns of the division by zero
   when p = q);
+* invalid inputs: a draft token outside the vocabulary is rejected (it
+  cannot have been proposed), a row with no positive weight draws token -1,
+  and a number of accepted drafts outside [0, K] draws token -1;
 * inverse-CDF sampling in ascending token id: the token is the smallest y
   whose cumulative weight exceeds u * Z. The pages fix only the law of the
   sampled token, not this map from u to a token id: parity unpinned by the
@@ -78,7 +81,9 @@ def accept_test(P, Q, tokens, u_accept):
     margin = np.zeros(K, dtype=np.float64)
     for j in range(K):
         x = int(tokens[j])
-        r = accept_ratio(P[j][x], Q[j][x])
+        V = len(P[j])
+        # a token outside the vocabulary cannot have been proposed: rejected
+        r = accept_ratio(P[j][x], Q[j][x]) if 0 <= x < V else 0.0
         u = float(u_accept[j])
         ratio[j] = r
         accept[j] = u < r
@@ -123,9 +128,11 @@ def inverse_cdf(weights, u):
 
     Returns (token, margin) where margin = min(T - C[y-1], C[y] - T) / Z is
     the distance of T = u * Z to the nearest edge of the chosen cell,
-    relative to the total mass.
+    relative to the total mass. Weights with no positive entry give -1.
     """
     w = np.asarray(weights, dtype=np.float64)
+    if not np.any(w > 0.0):
+        return -1, 0.0  # nothing to draw from
     c = np.cumsum(w)
     z = float(c[-1])
     t = float(u) * z
@@ -245,7 +252,11 @@ def sample_batch(P, Q, n_accepted, u_sample):
     mar = np.zeros(B, dtype=np.float64)
     zero = np.zeros(B, dtype=bool)
     for b in range(B):
-        tok[b], mar[b], zero[b] = sample_row(P[b], Q[b], int(n_accepted[b]), u_sample[b])
+        n = int(n_accepted[b])
+        if not 0 <= n <= len(Q[b]):
+            tok[b] = -1  # not a number of accepted drafts
+            continue
+        tok[b], mar[b], zero[b] = sample_row(P[b], Q[b], n, u_sample[b])
     return tok, mar, zero
 
 

@@ -1,0 +1,228 @@
+"""Python binding of libspecverify.so, the MI355X verify step of speculative
+decoding.
+
+Argument marshalling only: every call passes device pointers of caller-owned
+torch tensors and torch's current HIP stream to the C ABI declared in
+include/spec_verify.h; all computation runs in the library's HIP kernels.
+Importing this package fails if the library has not been built
+(``python -m speculative_decoding_verification_gemm_amd.build``); there is no
+fallback.
+"""
+
+import ctypes
+import os
+
+# torch ships its own HIP runtime under the same soname (libamdhip64.so.7) as
+# the system one this library links against; whichever is loaded first serves
+# the whole process. Device pointers and streams come from torch, so torch's
+# runtime must be the one loaded: import torch before opening the library.
+import torch  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing; build it with "
+        "`python -m speculative_decoding_verification_gemm_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+SPEC_OK = 0
+SPEC_ERR_INVALID_ARGUMENT = -1
+SPEC_ERR_ALIGNMENT = -2
+SPEC_ERR_UNSUPPORTED = -3
+SPEC_ERR_WORKSPACE = -4
+SPEC_ERR_HIP = -5
+SPEC_F32 = 0
+SPEC_BF16 = 1
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_z = ctypes.c_size_t
+
+# name -> (restype, argtypes), exactly as declared in include/spec_verify.h
+SIGNATURES = {
+    "spec_abi_version": (_i, []),
+    "spec_status_string": (ctypes.c_char_p, [_i]),
+    "spec_last_error": (ctypes.c_char_p, []),
+    "spec_verify_gemm": (_i, [_p, _p, _p, _i, _i, _i, _i, _p]),
+    "spec_softmax": (_i, [_p, _i, _i, _p, _p, _p, _p]),
+    "spec_accept_scan": (_i, [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p]),
+    "spec_residual_sample": (_i, [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p]),
+    "spec_verify_workspace_bytes": (_z, [_i, _i, _i]),
+    "spec_verify": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _z, _p]),
+}
+for _name, (_res, _args) in SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class SpecVerifyError(RuntimeError):
+    """A libspecverify call returned a non-zero status."""
+
+    def __init__(self, code, message):
+        super().__init__(f"{lib.spec_status_string(code).decode()}: {message}")
+        self.code = code
+
+
+def check(status):
+    if status != SPEC_OK:
+        raise SpecVerifyError(status, lib.spec_last_error().decode())
+
+
+def abi_version():
+    return lib.spec_abi_version()
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, dtype, name, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t
+
+
+def verify_gemm(x, w, out=None, out_dtype=None):
+    """y[M][d_out] = x[M][d_in] . w[d_out][d_in]^T (bf16 in, fp32 accumulate).
+
+    out_dtype: torch.float32 (default) or torch.bfloat16."""
+    torch = _torch()
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w, torch.bfloat16, "w", 2)
+    M, d_in = x.shape
+    d_out = w.shape[0]
+    if w.shape[1] != d_in:
+        raise ValueError(f"x {tuple(x.shape)} and w {tuple(w.shape)} disagree on d_in")
+    if out is None:
+        out = torch.empty((M, d_out), dtype=out_dtype or torch.float32, device=x.device)
+    _need(out, out.dtype, "out", 2)
+    if tuple(out.shape) != (M, d_out):
+        raise ValueError(f"out must be {(M, d_out)}, got {tuple(out.shape)}")
+    code = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16}.get(out.dtype)
+    if code is None:
+        raise TypeError("out must be float32 or bfloat16")
+    check(lib.spec_verify_gemm(_ptr(x), _ptr(w), _ptr(out), code, M, d_in, d_out, _stream()))
+    return out
+
+
+def softmax(logits, probs=True, stats=True):
+    """Row softmax of fp32 logits [..., V]: (probs or None, row_max, row_sumexp)
+    (the last two None unless stats)."""
+    torch = _torch()
+    _need(logits, torch.float32, "logits")
+    V = logits.shape[-1]
+    rows = logits.numel() // V
+    p = torch.empty_like(logits) if probs else None
+    mx = torch.empty(logits.shape[:-1], dtype=torch.float32, device=logits.device) if stats else None
+    se = torch.empty_like(mx) if stats else None
+    check(lib.spec_softmax(_ptr(logits), rows, V, _ptr(p), _ptr(mx), _ptr(se), _stream()))
+    return p, mx, se
+
+
+def accept_scan(p_probs, q_probs, draft_tokens, u_accept, with_mask=True):
+    """(n_accepted int32 [B], accept_mask uint8 [B][K] or None)."""
+    torch = _torch()
+    _need(p_probs, torch.float32, "p_probs", 3)
+    _need(q_probs, torch.float32, "q_probs", 3)
+    _need(draft_tokens, torch.int32, "draft_tokens", 2)
+    _need(u_accept, torch.float32, "u_accept", 2)
+    B, K1, V = p_probs.shape
+    K = K1 - 1
+    if tuple(q_probs.shape) != (B, K, V) or tuple(draft_tokens.shape) != (B, K) \
+            or tuple(u_accept.shape) != (B, K):
+        raise ValueError("inconsistent shapes")
+    n = torch.empty(B, dtype=torch.int32, device=p_probs.device)
+    mask = torch.empty((B, K), dtype=torch.uint8, device=p_probs.device) if with_mask else None
+    check(lib.spec_accept_scan(_ptr(p_probs), _ptr(q_probs), _ptr(draft_tokens), _ptr(u_accept),
+                               B, K, V, _ptr(n), _ptr(mask), _stream()))
+    return n, mask
+
+
+def residual_sample(p_probs, q_probs, n_accepted, u_sample):
+    """(token int32 [B], zero_residual uint8 [B])."""
+    torch = _torch()
+    _need(p_probs, torch.float32, "p_probs", 3)
+    _need(q_probs, torch.float32, "q_probs", 3)
+    _need(n_accepted, torch.int32, "n_accepted", 1)
+    _need(u_sample, torch.float32, "u_sample", 2)
+    B, K1, V = p_probs.shape
+    K = K1 - 1
+    if tuple(q_probs.shape) != (B, K, V) or tuple(n_accepted.shape) != (B,) \
+            or tuple(u_sample.shape) != (B, K1):
+        raise ValueError("inconsistent shapes")
+    tok = torch.empty(B, dtype=torch.int32, device=p_probs.device)
+    zero = torch.empty(B, dtype=torch.uint8, device=p_probs.device)
+    check(lib.spec_residual_sample(_ptr(p_probs), _ptr(q_probs), _ptr(n_accepted),
+                                   _ptr(u_sample), B, K, V, _ptr(tok), _ptr(zero), _stream()))
+    return tok, zero
+
+
+def workspace_bytes(B, K, V):
+    return lib.spec_verify_workspace_bytes(B, K, V)
+
+
+def new_workspace(B, K, V, device="cuda"):
+    """A device buffer of spec_verify_workspace_bytes(B, K, V) bytes (torch's
+    allocator returns 256-byte aligned blocks)."""
+    torch = _torch()
+    n = workspace_bytes(B, K, V)
+    if n == 0:
+        raise ValueError(f"invalid (B, K, V) = {(B, K, V)}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
+           hidden=None, lm_head=None, workspace=None, out_tokens=None, n_emitted=None):
+    """The verify step after the stack. With hidden [B*(K+1)][d] and lm_head
+    [V][d] (bf16), target_logits [B][K+1][V] is written first; otherwise it
+    is an input. Returns (out_tokens int32 [B][K+1], n_emitted int32 [B])."""
+    torch = _torch()
+    _need(target_logits, torch.float32, "target_logits", 3)
+    _need(draft_logits, torch.float32, "draft_logits", 3)
+    _need(draft_tokens, torch.int32, "draft_tokens", 2)
+    _need(u_accept, torch.float32, "u_accept", 2)
+    _need(u_sample, torch.float32, "u_sample", 2)
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    d = 0
+    if lm_head is not None:
+        _need(lm_head, torch.bfloat16, "lm_head", 2)
+        _need(hidden, torch.bfloat16, "hidden", 2)
+        d = lm_head.shape[1]
+        if tuple(lm_head.shape) != (V, d) or tuple(hidden.shape) != (B * K1, d):
+            raise ValueError("hidden / lm_head shapes disagree with the logits")
+    if workspace is None:
+        workspace = new_workspace(B, K, V, target_logits.device)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K1), dtype=torch.int32, device=target_logits.device)
+    if n_emitted is None:
+        n_emitted = torch.empty(B, dtype=torch.int32, device=target_logits.device)
+    check(lib.spec_verify(_ptr(hidden), _ptr(lm_head), d, _ptr(target_logits),
+                          _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
+                          _ptr(u_sample), B, K, V, _ptr(out_tokens), _ptr(n_emitted),
+                          _ptr(workspace), workspace.numel(), _stream()))
+    return out_tokens, n_emitted

@@ -1,0 +1,231 @@
+// C ABI of libspecverify: argument validation, device check and dispatch.
+// Every argument is checked before the first HIP call, so a failing call
+// launches nothing and the checks run on hosts without a GPU.
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/spec_verify.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Per-device answer to "is this a gfx950?": 0 unknown, 1 yes, -1 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SPEC_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SPEC_ERR_UNSUPPORTED, "device index %d", dev);
+  int ok = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (ok == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(SPEC_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_arch_ok[dev].store(ok, std::memory_order_relaxed);
+  }
+  if (ok < 0) return fail(SPEC_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return SPEC_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SPEC_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return SPEC_OK;
+}
+
+constexpr int kMaxM = 65536;
+constexpr int kMaxDin = 1 << 20;
+constexpr int kMaxDout = 1 << 24;
+constexpr int kMaxRows = 1 << 24;
+constexpr int kMaxV = 1 << 26;
+constexpr int kMaxB = 1 << 20;
+constexpr int kMaxK = 64;
+// fused-stage grid bound: rows * chunks of 4096 entries
+constexpr size_t kMaxVerifyBlocks = (size_t)1 << 22;
+
+int check_gemm_args(const uint16_t* x, const uint16_t* w, const void* y, int y_dtype, int M,
+                    int d_in, int d_out) {
+  if (!x || !w || !y) return fail(SPEC_ERR_INVALID_ARGUMENT, "null pointer (x, w or y)");
+  if (y_dtype != SPEC_F32 && y_dtype != SPEC_BF16)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "y_dtype %d is neither SPEC_F32 nor SPEC_BF16", y_dtype);
+  if (M < 1 || M > kMaxM) return fail(SPEC_ERR_INVALID_ARGUMENT, "M=%d outside [1, %d]", M, kMaxM);
+  if (d_in < 8 || d_in > kMaxDin || d_in % 8 != 0)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "d_in=%d must be a multiple of 8 in [8, %d]", d_in,
+                kMaxDin);
+  if (d_out < 1 || d_out > kMaxDout)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "d_out=%d outside [1, %d]", d_out, kMaxDout);
+  if (!aligned(x, 16) || !aligned(w, 16))
+    return fail(SPEC_ERR_ALIGNMENT, "x and w must be 16-byte aligned");
+  if (!aligned(y, y_dtype == SPEC_F32 ? 4 : 2))
+    return fail(SPEC_ERR_ALIGNMENT, "y is not aligned to its element size");
+  return SPEC_OK;
+}
+
+int check_bkv(int B, int K, int V) {
+  if (B < 1 || B > kMaxB) return fail(SPEC_ERR_INVALID_ARGUMENT, "B=%d outside [1, %d]", B, kMaxB);
+  if (K < 1 || K > kMaxK) return fail(SPEC_ERR_INVALID_ARGUMENT, "K=%d outside [1, %d]", K, kMaxK);
+  if (V < 1 || V > kMaxV) return fail(SPEC_ERR_INVALID_ARGUMENT, "V=%d outside [1, %d]", V, kMaxV);
+  return SPEC_OK;
+}
+
+int run_gemm(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M, int d_in,
+             int d_out, hipStream_t s) {
+  hipError_t e = (M <= specv::kMaxStreamM)
+                     ? specv::launch_gemm_stream(x, w, y, out_bf16, M, d_in, d_out, s)
+                     : specv::launch_gemm_mfma(x, w, y, out_bf16, M, d_in, d_out, s);
+  return launched(e, "spec_verify_gemm");
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_abi_version(void) { return SPEC_ABI_VERSION; }
+
+const char* spec_status_string(int status) {
+  switch (status) {
+    case SPEC_OK: return "SPEC_OK";
+    case SPEC_ERR_INVALID_ARGUMENT: return "SPEC_ERR_INVALID_ARGUMENT";
+    case SPEC_ERR_ALIGNMENT: return "SPEC_ERR_ALIGNMENT";
+    case SPEC_ERR_UNSUPPORTED: return "SPEC_ERR_UNSUPPORTED";
+    case SPEC_ERR_WORKSPACE: return "SPEC_ERR_WORKSPACE";
+    case SPEC_ERR_HIP: return "SPEC_ERR_HIP";
+    default: return "SPEC_ERR_UNKNOWN";
+  }
+}
+
+const char* spec_last_error(void) { return g_err; }
+
+int spec_verify_gemm(const uint16_t* x, const uint16_t* w, void* y, int y_dtype, int M, int d_in,
+                     int d_out, void* stream) {
+  clear_error();
+  int rc = check_gemm_args(x, w, y, y_dtype, M, d_in, d_out);
+  if (rc != SPEC_OK) return rc;
+  if ((rc = check_device()) != SPEC_OK) return rc;
+  return run_gemm(x, w, y, y_dtype == SPEC_BF16, M, d_in, d_out,
+                  static_cast<hipStream_t>(stream));
+}
+
+int spec_softmax(const float* logits, int rows, int V, float* probs, float* row_max,
+                 float* row_sumexp, void* stream) {
+  clear_error();
+  if (!logits) return fail(SPEC_ERR_INVALID_ARGUMENT, "null logits");
+  if (rows < 1 || rows > kMaxRows)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "rows=%d outside [1, %d]", rows, kMaxRows);
+  if (V < 1 || V > kMaxV) return fail(SPEC_ERR_INVALID_ARGUMENT, "V=%d outside [1, %d]", V, kMaxV);
+  if (!aligned(logits, 4) || (probs && !aligned(probs, 4)) || (row_max && !aligned(row_max, 4)) ||
+      (row_sumexp && !aligned(row_sumexp, 4)))
+    return fail(SPEC_ERR_ALIGNMENT, "fp32 arrays must be 4-byte aligned");
+  if (!probs && !row_max && !row_sumexp) return SPEC_OK;
+  int rc = check_device();
+  if (rc != SPEC_OK) return rc;
+  return launched(specv::launch_softmax_rows(logits, rows, V, probs, row_max, row_sumexp,
+                                             static_cast<hipStream_t>(stream)),
+                  "spec_softmax");
+}
+
+int spec_accept_scan(const float* p_probs, const float* q_probs, const int32_t* draft_tokens,
+                     const float* u_accept, int B, int K, int V, int32_t* n_accepted,
+                     uint8_t* accept_mask, void* stream) {
+  clear_error();
+  if (!p_probs || !q_probs || !draft_tokens || !u_accept || !n_accepted)
+    return fail(SPEC_ERR_INVALID_ARGUMENT,
+                "null pointer (p_probs, q_probs, draft_tokens, u_accept or n_accepted)");
+  int rc = check_bkv(B, K, V);
+  if (rc != SPEC_OK) return rc;
+  if (!aligned(p_probs, 4) || !aligned(q_probs, 4) || !aligned(draft_tokens, 4) ||
+      !aligned(u_accept, 4) || !aligned(n_accepted, 4))
+    return fail(SPEC_ERR_ALIGNMENT, "32-bit arrays must be 4-byte aligned");
+  if ((rc = check_device()) != SPEC_OK) return rc;
+  return launched(specv::launch_accept_probs(p_probs, q_probs, draft_tokens, u_accept, B, K, V,
+                                             n_accepted, accept_mask,
+                                             static_cast<hipStream_t>(stream)),
+                  "spec_accept_scan");
+}
+
+int spec_residual_sample(const float* p_probs, const float* q_probs, const int32_t* n_accepted,
+                         const float* u_sample, int B, int K, int V, int32_t* token,
+                         uint8_t* zero_residual, void* stream) {
+  clear_error();
+  if (!p_probs || !q_probs || !n_accepted || !u_sample || !token)
+    return fail(SPEC_ERR_INVALID_ARGUMENT,
+                "null pointer (p_probs, q_probs, n_accepted, u_sample or token)");
+  int rc = check_bkv(B, K, V);
+  if (rc != SPEC_OK) return rc;
+  if (!aligned(p_probs, 4) || !aligned(q_probs, 4) || !aligned(n_accepted, 4) ||
+      !aligned(u_sample, 4) || !aligned(token, 4))
+    return fail(SPEC_ERR_ALIGNMENT, "32-bit arrays must be 4-byte aligned");
+  if ((rc = check_device()) != SPEC_OK) return rc;
+  return launched(specv::launch_sample_probs(p_probs, q_probs, n_accepted, u_sample, B, K, V,
+                                             token, zero_residual,
+                                             static_cast<hipStream_t>(stream)),
+                  "spec_residual_sample");
+}
+
+size_t spec_verify_workspace_bytes(int B, int K, int V) {
+  if (B < 1 || B > kMaxB || K < 1 || K > kMaxK || V < 1 || V > kMaxV) return 0;
+  return specv::verify_workspace_bytes(B, K, V);
+}
+
+int spec_verify(const uint16_t* hidden, const uint16_t* lm_head, int d, float* target_logits,
+                const float* draft_logits, const int32_t* draft_tokens, const float* u_accept,
+                const float* u_sample, int B, int K, int V, int32_t* out_tokens,
+                int32_t* n_emitted, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (!target_logits || !draft_logits || !draft_tokens || !u_accept || !u_sample || !out_tokens ||
+      !n_emitted || !workspace)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "null required pointer");
+  if ((hidden == nullptr) != (lm_head == nullptr))
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "hidden and lm_head must be both given or both NULL");
+  int rc = check_bkv(B, K, V);
+  if (rc != SPEC_OK) return rc;
+  const size_t chunks = ((size_t)V + 4095) / 4096;
+  if ((size_t)B * (2 * K + 1) * chunks > kMaxVerifyBlocks)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "B*(2K+1)*ceil(V/4096) exceeds %zu", kMaxVerifyBlocks);
+  const int M = B * (K + 1);
+  if (lm_head) {
+    if (M > kMaxM) return fail(SPEC_ERR_INVALID_ARGUMENT, "B*(K+1)=%d exceeds %d", M, kMaxM);
+    if ((rc = check_gemm_args(hidden, lm_head, target_logits, SPEC_F32, M, d, V)) != SPEC_OK)
+      return rc;
+  }
+  if (!aligned(target_logits, 4) || !aligned(draft_logits, 4) || !aligned(draft_tokens, 4) ||
+      !aligned(u_accept, 4) || !aligned(u_sample, 4) || !aligned(out_tokens, 4) ||
+      !aligned(n_emitted, 4))
+    return fail(SPEC_ERR_ALIGNMENT, "32-bit arrays must be 4-byte aligned");
+  const size_t need = specv::verify_workspace_bytes(B, K, V);
+  if (workspace_bytes < need)
+    return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if ((rc = check_device()) != SPEC_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (lm_head && (rc = run_gemm(hidden, lm_head, target_logits, false, M, d, V, s)) != SPEC_OK)
+    return rc;
+  return launched(specv::launch_verify_sampling(target_logits, draft_logits, draft_tokens, u_accept,
+                                                u_sample, B, K, V, out_tokens, n_emitted,
+                                                workspace, s),
+                  "spec_verify sampling");
+}
+
+}  // extern "C"

@@ -1,0 +1,599 @@
+// Speculative sampling at every verified position: softmax, the accept test
+// min(1, p/q) with the first rejection, and the residual / bonus draw.
+//
+// ("Speculative Decoding: Two Models, One Voice", The idea, step 3, and The
+// rule that makes it exact; "Speculative Decoding: Guess Several Tokens,
+// Check Them in One Pass", Step 3.)
+//
+// Row conventions (per sequence b, K drafts): target rows [B][K+1][V], draft
+// rows [B][K][V]; u_accept[b][j] drives the test of draft j and
+// u_sample[b][n] the draw that ends the round after n acceptances.
+//
+// Precision. Acceptance ratios and every weight of the final draw are fp64;
+// running sums of the inverse CDF are fp64 in a fixed order, so results are
+// deterministic. On the fused path (spec_verify) probabilities are never
+// stored: per-row max and fp64 sum of exponentials are kept and each needed
+// probability is exp(l - max) / sum evaluated in fp64 from the fp32 logit.
+
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace specv {
+
+constexpr int kChunk = 4096;       // vocabulary entries per sampling chunk
+constexpr int kScanThreads = 256;  // threads per chunk; 16 entries each
+constexpr int kPerThread = kChunk / kScanThreads;
+
+// ---------------------------------------------------------------------------
+// Stage softmax: one workgroup per row
+// ---------------------------------------------------------------------------
+
+constexpr int kSoftmaxThreads = 512;
+
+template <bool VEC>
+__global__ __launch_bounds__(kSoftmaxThreads) void softmax_rows_kernel(
+    const float* __restrict__ logits, int V, float* __restrict__ probs,
+    float* __restrict__ row_max, float* __restrict__ row_sumexp) {
+  __shared__ double red_d[kSoftmaxThreads / kWave];
+  __shared__ float red_f[kSoftmaxThreads / kWave];
+  const int tid = threadIdx.x;
+  const size_t row = blockIdx.x;
+  const float* l = logits + row * (size_t)V;
+
+  // One pass: running max m and running sum s of exp(l - m), rescaled
+  // whenever the max grows.
+  float m = -INFINITY;
+  double s = 0.0;
+  if (VEC) {
+    const f32x4* l4 = reinterpret_cast<const f32x4*>(l);
+    for (int i = tid; i < V / 4; i += kSoftmaxThreads) {
+      const f32x4 v = l4[i];
+      const float mx = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+      if (mx > m) {
+        s *= (double)expf(m - mx);
+        m = mx;
+      }
+      s += (double)(expf(v.x - m) + expf(v.y - m)) + (double)(expf(v.z - m) + expf(v.w - m));
+    }
+  } else {
+    for (int i = tid; i < V; i += kSoftmaxThreads) {
+      const float v = l[i];
+      if (v > m) {
+        s *= (double)expf(m - v);
+        m = v;
+      }
+      s += (double)expf(v - m);
+    }
+  }
+  const float M = block_max_f32<kSoftmaxThreads>(m, red_f);
+  const double part = (s > 0.0) ? s * (double)expf(m - M) : 0.0;
+  const double S = block_sum_f64<kSoftmaxThreads>(part, red_d);
+  if (tid == 0) {
+    if (row_max) row_max[row] = M;
+    if (row_sumexp) row_sumexp[row] = (float)S;
+  }
+  if (probs) {
+    float* p = probs + row * (size_t)V;
+    if (VEC) {
+      const f32x4* l4 = reinterpret_cast<const f32x4*>(l);
+      f32x4* p4 = reinterpret_cast<f32x4*>(p);
+      for (int i = tid; i < V / 4; i += kSoftmaxThreads) {
+        const f32x4 v = l4[i];
+        p4[i] = f32x4{(float)((double)expf(v.x - M) / S), (float)((double)expf(v.y - M) / S),
+                      (float)((double)expf(v.z - M) / S), (float)((double)expf(v.w - M) / S)};
+      }
+    } else {
+      for (int i = tid; i < V; i += kSoftmaxThreads) p[i] = (float)((double)expf(l[i] - M) / S);
+    }
+  }
+}
+
+hipError_t launch_softmax_rows(const float* logits, int rows, int V, float* probs, float* row_max,
+                               float* row_sumexp, hipStream_t s) {
+  const bool vec = (V % 4 == 0) && ((uintptr_t)logits % 16 == 0) &&
+                   (probs == nullptr || (uintptr_t)probs % 16 == 0);
+  if (vec)
+    hipLaunchKernelGGL(softmax_rows_kernel<true>, dim3(rows), dim3(kSoftmaxThreads), 0, s, logits,
+                       V, probs, row_max, row_sumexp);
+  else
+    hipLaunchKernelGGL(softmax_rows_kernel<false>, dim3(rows), dim3(kSoftmaxThreads), 0, s,
+                       logits, V, probs, row_max, row_sumexp);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Accept test and first rejection (wave ballot)
+// ---------------------------------------------------------------------------
+
+// ratio = p/q with q = 0 giving +inf when p > 0 and 0 otherwise; the test
+// u < ratio accepts with probability min(1, p/q).
+__device__ __forceinline__ bool accept_decision(double p, double q, float u) {
+  double ratio;
+  if (q > 0.0)
+    ratio = p / q;
+  else
+    ratio = (p > 0.0) ? INFINITY : 0.0;
+  return (double)u < ratio;
+}
+
+// n_accepted = index of the first lane in [0, K) whose test failed, or K.
+__device__ __forceinline__ int first_rejection(bool acc, int K) {
+  const unsigned long long mask = __ballot(acc);
+  const unsigned long long rejected = ~mask;
+  int n = rejected ? (__ffsll((long long)rejected) - 1) : kWave;
+  return n < K ? n : K;
+}
+
+// One wave per sequence on probabilities.
+__global__ __launch_bounds__(kWave) void accept_probs_kernel(
+    const float* __restrict__ p, const float* __restrict__ q, const int32_t* __restrict__ tokens,
+    const float* __restrict__ u_accept, int K, int V, int32_t* __restrict__ n_accepted,
+    uint8_t* __restrict__ mask) {
+  const int b = blockIdx.x, j = threadIdx.x;
+  bool acc = false;
+  if (j < K) {
+    const int x = tokens[(size_t)b * K + j];
+    if (x >= 0 && x < V) {
+      const double pp = p[((size_t)b * (K + 1) + j) * V + x];
+      const double qq = q[((size_t)b * K + j) * V + x];
+      acc = accept_decision(pp, qq, u_accept[(size_t)b * K + j]);
+    }
+    if (mask) mask[(size_t)b * K + j] = acc ? 1 : 0;
+  }
+  const int n = first_rejection(acc, K);
+  if (j == 0) n_accepted[b] = n;
+}
+
+hipError_t launch_accept_probs(const float* p, const float* q, const int32_t* tokens,
+                               const float* u_accept, int B, int K, int V, int32_t* n_accepted,
+                               uint8_t* mask, hipStream_t s) {
+  hipLaunchKernelGGL(accept_probs_kernel, dim3(B), dim3(kWave), 0, s, p, q, tokens, u_accept, K,
+                     V, n_accepted, mask);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Inverse-CDF draw over one chunk
+// ---------------------------------------------------------------------------
+
+// Weights of one sampling row. residual: max(0, p - q); otherwise p.
+struct ProbWeights {
+  const float* p;
+  const float* q;  // null for a plain draw from p
+  __device__ __forceinline__ double operator()(int v) const {
+    const double pv = p[v];
+    if (!q) return pv;
+    const double r = pv - (double)q[v];
+    return r > 0.0 ? r : 0.0;
+  }
+};
+
+struct LogitWeights {
+  const float* lp;
+  const float* lq;  // null for a plain draw from p
+  double mp, sp, mq, sq;
+  __device__ __forceinline__ double operator()(int v) const {
+    const double pv = exp((double)lp[v] - mp) / sp;
+    if (!lq) return pv;
+    const double r = pv - exp((double)lq[v] - mq) / sq;
+    return r > 0.0 ? r : 0.0;
+  }
+};
+
+// Fixed-order fp64 sum of the weights of chunk c (256 threads x 16 entries).
+template <class Wt>
+__device__ double chunk_sum(const Wt& wt, int c, int V, double* red) {
+  const int v0 = c * kChunk + threadIdx.x * kPerThread;
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i)
+    if (v0 + i < V) t += wt(v0 + i);
+  return block_sum_f64<kScanThreads>(t, red);
+}
+
+// Smallest token y in chunk c with w[y] > 0 and base + C_chunk[y] > T, where
+// C_chunk is the running sum inside the chunk; if rounding leaves no such y,
+// the largest y in the chunk with w[y] > 0; -1 if the chunk has no weight.
+template <class Wt>
+__device__ int chunk_draw(const Wt& wt, int c, int V, double base, double T, double* red_d,
+                          int* red_i) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int v0 = c * kChunk + tid * kPerThread;
+  double w[kPerThread];
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    w[i] = (v0 + i < V) ? wt(v0 + i) : 0.0;
+    t += w[i];
+  }
+  // exclusive scan of the per-thread sums: wave inclusive scan, then waves
+  double inc = t;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double y = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += y;
+  }
+  if (lane == kWave - 1) red_d[wave] = inc;
+  __syncthreads();
+  double before = 0.0;
+  for (int k = 0; k < wave; ++k) before += red_d[k];
+  __syncthreads();
+  double run = base + (before + (inc - t));
+  int cand = 0x7fffffff, last = -1;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    if (w[i] > 0.0) {
+      run += w[i];
+      if (cand == 0x7fffffff && run > T) cand = v0 + i;
+      last = v0 + i;
+    }
+  }
+  // block min of cand, block max of last
+  for (int o = 32; o > 0; o >>= 1) {
+    cand = min(cand, __shfl_xor(cand, o, kWave));
+    last = max(last, __shfl_xor(last, o, kWave));
+  }
+  if (lane == 0) {
+    red_i[wave] = cand;
+    red_i[kScanThreads / kWave + wave] = last;
+  }
+  __syncthreads();
+  int bc = red_i[0], bl = red_i[kScanThreads / kWave];
+  for (int k = 1; k < kScanThreads / kWave; ++k) {
+    bc = min(bc, red_i[k]);
+    bl = max(bl, red_i[kScanThreads / kWave + k]);
+  }
+  __syncthreads();
+  return bc != 0x7fffffff ? bc : bl;
+}
+
+// Picks the chunk that holds T given the chunk sums sc[0..C) (read through
+// `sum_of`), in ascending order. Returns the chunk and its base.
+template <class SumOf>
+__device__ __forceinline__ int pick_chunk(const SumOf& sum_of, int C, double T, double* base) {
+  double run = 0.0;
+  int last_pos = -1;
+  double last_base = 0.0;
+  for (int c = 0; c < C; ++c) {
+    const double sc = sum_of(c);
+    if (sc > 0.0) {
+      if (run + sc > T) {
+        *base = run;
+        return c;
+      }
+      last_pos = c;
+      last_base = run;
+    }
+    run += sc;
+  }
+  *base = last_base;
+  return last_pos;
+}
+
+// ---------------------------------------------------------------------------
+// Stage draw on probabilities: one workgroup per sequence
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kScanThreads) void sample_probs_kernel(
+    const float* __restrict__ p, const float* __restrict__ q, const int32_t* __restrict__ n_acc,
+    const float* __restrict__ u_sample, int K, int V, int32_t* __restrict__ token,
+    uint8_t* __restrict__ zero_residual) {
+  __shared__ double red_d[kScanThreads / kWave];
+  __shared__ int red_i[2 * kScanThreads / kWave];
+  const int b = blockIdx.x;
+  const int n = n_acc[b];
+  if (n < 0 || n > K) {
+    if (threadIdx.x == 0) {
+      token[b] = -1;
+      if (zero_residual) zero_residual[b] = 0;
+    }
+    return;
+  }
+  const int C = (V + kChunk - 1) / kChunk;
+  const float* prow = p + ((size_t)b * (K + 1) + n) * V;
+  ProbWeights wt{prow, n < K ? q + ((size_t)b * K + n) * V : nullptr};
+  // total mass, chunk by chunk in ascending order
+  double Z = 0.0;
+  for (int c = 0; c < C; ++c) Z += chunk_sum(wt, c, V, red_d);
+  bool zero = false;
+  if (!(Z > 0.0) && wt.q) {  // empty residual: fall back to p
+    zero = true;
+    wt.q = nullptr;
+    Z = 0.0;
+    for (int c = 0; c < C; ++c) Z += chunk_sum(wt, c, V, red_d);
+  }
+  int y = -1;
+  if (Z > 0.0) {
+    const double T = (double)u_sample[(size_t)b * (K + 1) + n] * Z;
+    // second pass: running chunk sums (identical values) up to the crossing
+    double run = 0.0, base = 0.0;
+    int cc = -1;
+    double last_base = 0.0;
+    int last_c = -1;
+    for (int c = 0; c < C; ++c) {
+      const double sc = chunk_sum(wt, c, V, red_d);
+      if (sc > 0.0) {
+        if (run + sc > T) {
+          cc = c;
+          base = run;
+          break;
+        }
+        last_c = c;
+        last_base = run;
+      }
+      run += sc;
+    }
+    if (cc < 0) {
+      cc = last_c;
+      base = last_base;
+    }
+    if (cc >= 0) y = chunk_draw(wt, cc, V, base, T, red_d, red_i);
+  }
+  if (threadIdx.x == 0) {
+    token[b] = y;
+    if (zero_residual) zero_residual[b] = zero ? 1 : 0;
+  }
+}
+
+hipError_t launch_sample_probs(const float* p, const float* q, const int32_t* n_accepted,
+                               const float* u_sample, int B, int K, int V, int32_t* token,
+                               uint8_t* zero_residual, hipStream_t s) {
+  hipLaunchKernelGGL(sample_probs_kernel, dim3(B), dim3(kScanThreads), 0, s, p, q, n_accepted,
+                     u_sample, K, V, token, zero_residual);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused sampling stage of spec_verify (logits in)
+// ---------------------------------------------------------------------------
+//
+// 1. stats_partial  grid R*C: per chunk of a row, max and fp64 sum of
+//                   exp(l - max); R = B*(K+1) target rows then B*K draft rows.
+// 2. verify_accept  grid B, one wave: combine the chunk partials of the
+//                   sequence's 2K+1 rows into (max, sum) in a fixed order,
+//                   then the accept test and the first rejection.
+// 3. resid_partial  grid B*C: chunk sums of the terminating row's
+//                   weights (the residual, and p for the empty-residual
+//                   fallback).
+// 4. verify_draw    grid B: pick the chunk, draw inside it, emit.
+
+struct VerifyWs {
+  float* pmax;    // [R][C]
+  double* psum;   // [R][C]
+  float* fmax;    // [R]
+  double* fsum;   // [R]
+  int32_t* nacc;  // [B]
+  double* rsum;   // [B][C] residual (or bonus p) chunk sums
+  double* qsum;   // [B][C] p chunk sums for the empty-residual fallback
+};
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static VerifyWs carve(void* base, int B, int K, int V, size_t* total) {
+  const size_t R = (size_t)B * (2 * K + 1);
+  const size_t C = (V + kChunk - 1) / kChunk;
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  VerifyWs ws;
+  ws.pmax = reinterpret_cast<float*>(p + off);
+  off = align256(off + R * C * sizeof(float));
+  ws.psum = reinterpret_cast<double*>(p + off);
+  off = align256(off + R * C * sizeof(double));
+  ws.fmax = reinterpret_cast<float*>(p + off);
+  off = align256(off + R * sizeof(float));
+  ws.fsum = reinterpret_cast<double*>(p + off);
+  off = align256(off + R * sizeof(double));
+  ws.nacc = reinterpret_cast<int32_t*>(p + off);
+  off = align256(off + (size_t)B * sizeof(int32_t));
+  ws.rsum = reinterpret_cast<double*>(p + off);
+  off = align256(off + (size_t)B * C * sizeof(double));
+  ws.qsum = reinterpret_cast<double*>(p + off);
+  off = align256(off + (size_t)B * C * sizeof(double));
+  if (total) *total = off;
+  return ws;
+}
+
+size_t verify_workspace_bytes(int B, int K, int V) {
+  size_t total = 0;
+  carve(nullptr, B, K, V, &total);
+  return total;
+}
+
+// logits row of the fused layout: target rows first, then draft rows
+__device__ __forceinline__ const float* verify_row(const float* tl, const float* dl, int row,
+                                                   int B, int K, int V) {
+  const int n_target = B * (K + 1);
+  return row < n_target ? tl + (size_t)row * V : dl + (size_t)(row - n_target) * V;
+}
+
+__global__ __launch_bounds__(kScanThreads) void stats_partial_kernel(const float* __restrict__ tl,
+                                                                     const float* __restrict__ dl,
+                                                                     int B, int K, int V,
+                                                                     VerifyWs ws) {
+  __shared__ double red_d[kScanThreads / kWave];
+  __shared__ float red_f[kScanThreads / kWave];
+  const int C = (V + kChunk - 1) / kChunk;
+  const int row = blockIdx.x / C, c = blockIdx.x - row * C;
+  const float* l = verify_row(tl, dl, row, B, K, V);
+  const int v0 = c * kChunk + threadIdx.x * kPerThread;
+  float x[kPerThread];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    x[i] = (v0 + i < V) ? l[v0 + i] : -INFINITY;
+    m = fmaxf(m, x[i]);
+  }
+  const float cm = block_max_f32<kScanThreads>(m, red_f);
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i)
+    if (v0 + i < V) s += exp((double)x[i] - (double)cm);
+  const double cs = block_sum_f64<kScanThreads>(s, red_d);
+  if (threadIdx.x == 0) {
+    ws.pmax[(size_t)row * C + c] = cm;
+    ws.psum[(size_t)row * C + c] = cs;
+  }
+}
+
+__global__ __launch_bounds__(kWave) void verify_accept_kernel(
+    const float* __restrict__ tl, const float* __restrict__ dl, const int32_t* __restrict__ tokens,
+    const float* __restrict__ u_accept, int B, int K, int V, VerifyWs ws) {
+  __shared__ float smax[2 * 64 + 1];
+  __shared__ double ssum[2 * 64 + 1];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int C = (V + kChunk - 1) / kChunk;
+  // local index i: 0..K target rows, K+1..2K draft rows
+  for (int i = lane; i < 2 * K + 1; i += kWave) {
+    const int row = i <= K ? b * (K + 1) + i : B * (K + 1) + b * K + (i - K - 1);
+    float M = -INFINITY;
+    for (int c = 0; c < C; ++c) M = fmaxf(M, ws.pmax[(size_t)row * C + c]);
+    double S = 0.0;
+    for (int c = 0; c < C; ++c)
+      S += ws.psum[(size_t)row * C + c] * exp((double)ws.pmax[(size_t)row * C + c] - (double)M);
+    ws.fmax[row] = M;
+    ws.fsum[row] = S;
+    smax[i] = M;
+    ssum[i] = S;
+  }
+  __syncthreads();
+  bool acc = false;
+  if (lane < K) {
+    const int x = tokens[(size_t)b * K + lane];
+    if (x >= 0 && x < V) {
+      const int trow = b * (K + 1) + lane, drow = b * K + lane;
+      const double pp = exp((double)tl[(size_t)trow * V + x] - (double)smax[lane]) / ssum[lane];
+      const double qq =
+          exp((double)dl[(size_t)drow * V + x] - (double)smax[K + 1 + lane]) / ssum[K + 1 + lane];
+      acc = accept_decision(pp, qq, u_accept[(size_t)b * K + lane]);
+    }
+  }
+  const int n = first_rejection(acc, K);
+  if (lane == 0) ws.nacc[b] = n;
+}
+
+__device__ __forceinline__ LogitWeights verify_weights(const float* tl, const float* dl, int b,
+                                                       int n, int B, int K, int V,
+                                                       const VerifyWs& ws, bool with_q) {
+  const int trow = b * (K + 1) + n;
+  LogitWeights w;
+  w.lp = tl + (size_t)trow * V;
+  w.mp = ws.fmax[trow];
+  w.sp = ws.fsum[trow];
+  if (with_q && n < K) {
+    const int drow = B * (K + 1) + b * K + n;
+    w.lq = dl + (size_t)(b * K + n) * V;
+    w.mq = ws.fmax[drow];
+    w.sq = ws.fsum[drow];
+  } else {
+    w.lq = nullptr;
+    w.mq = 0.0;
+    w.sq = 1.0;
+  }
+  return w;
+}
+
+__global__ __launch_bounds__(kScanThreads) void resid_partial_kernel(
+    const float* __restrict__ tl, const float* __restrict__ dl, int B, int K, int V, VerifyWs ws) {
+  __shared__ double red_d[kScanThreads / kWave];
+  const int C = (V + kChunk - 1) / kChunk;
+  const int b = blockIdx.x / C, c = blockIdx.x - b * C;
+  const int n = ws.nacc[b];
+  const LogitWeights w = verify_weights(tl, dl, b, n, B, K, V, ws, true);
+  const int v0 = c * kChunk + threadIdx.x * kPerThread;
+  double tr = 0.0, tp = 0.0;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int v = v0 + i;
+    if (v < V) {
+      const double pv = exp((double)w.lp[v] - w.mp) / w.sp;
+      tp += pv;
+      if (w.lq) {
+        const double r = pv - exp((double)w.lq[v] - w.mq) / w.sq;
+        tr += r > 0.0 ? r : 0.0;
+      }
+    }
+  }
+  if (!w.lq) tr = tp;
+  tr = block_sum_f64<kScanThreads>(tr, red_d);
+  tp = block_sum_f64<kScanThreads>(tp, red_d);
+  if (threadIdx.x == 0) {
+    ws.rsum[(size_t)b * C + c] = tr;
+    ws.qsum[(size_t)b * C + c] = tp;
+  }
+}
+
+__global__ __launch_bounds__(kScanThreads) void verify_draw_kernel(
+    const float* __restrict__ tl, const float* __restrict__ dl, const int32_t* __restrict__ tokens,
+    const float* __restrict__ u_sample, int B, int K, int V, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ n_emitted, VerifyWs ws) {
+  __shared__ double red_d[kScanThreads / kWave];
+  __shared__ int red_i[2 * kScanThreads / kWave];
+  __shared__ double s_base, s_T;
+  __shared__ int s_chunk, s_use_p;
+  const int b = blockIdx.x;
+  const int C = (V + kChunk - 1) / kChunk;
+  const int n = ws.nacc[b];
+  if (threadIdx.x == 0) {
+    const double* rs = ws.rsum + (size_t)b * C;
+    const double* ps = ws.qsum + (size_t)b * C;
+    double Z = 0.0;
+    for (int c = 0; c < C; ++c) Z += rs[c];
+    int use_p = 0;
+    if (!(Z > 0.0)) {  // empty residual: fall back to p of the same row
+      use_p = 1;
+      Z = 0.0;
+      for (int c = 0; c < C; ++c) Z += ps[c];
+    }
+    const double T = (double)u_sample[(size_t)b * (K + 1) + n] * Z;
+    double base = 0.0;
+    int chunk = -1;
+    if (Z > 0.0) {
+      if (use_p)
+        chunk = pick_chunk([&](int c) { return ps[c]; }, C, T, &base);
+      else
+        chunk = pick_chunk([&](int c) { return rs[c]; }, C, T, &base);
+    }
+    s_base = base;
+    s_T = T;
+    s_chunk = chunk;
+    s_use_p = use_p;
+  }
+  __syncthreads();
+  const int chunk = s_chunk;
+  int y = -1;
+  if (chunk >= 0) {
+    const LogitWeights w = verify_weights(tl, dl, b, n, B, K, V, ws, !s_use_p);
+    y = chunk_draw(w, chunk, V, s_base, s_T, red_d, red_i);
+  }
+  for (int j = threadIdx.x; j < K + 1; j += kScanThreads) {
+    int32_t t = -1;
+    if (j < n)
+      t = tokens[(size_t)b * K + j];
+    else if (j == n)
+      t = y;
+    out_tokens[(size_t)b * (K + 1) + j] = t;
+  }
+  if (threadIdx.x == 0) n_emitted[b] = n + 1;
+}
+
+hipError_t launch_verify_sampling(const float* tl, const float* dl, const int32_t* tokens,
+                                  const float* u_accept, const float* u_sample, int B, int K, int V,
+                                  int32_t* out_tokens, int32_t* n_emitted, void* workspace,
+                                  hipStream_t s) {
+  const VerifyWs ws = carve(workspace, B, K, V, nullptr);
+  const int C = (V + kChunk - 1) / kChunk;
+  const int R = B * (2 * K + 1);
+  hipLaunchKernelGGL(stats_partial_kernel, dim3(R * C), dim3(kScanThreads), 0, s, tl, dl, B, K, V,
+                     ws);
+  hipLaunchKernelGGL(verify_accept_kernel, dim3(B), dim3(kWave), 0, s, tl, dl, tokens, u_accept,
+                     B, K, V, ws);
+  hipLaunchKernelGGL(resid_partial_kernel, dim3(B * C), dim3(kScanThreads), 0, s, tl, dl, B, K, V,
+                     ws);
+  hipLaunchKernelGGL(verify_draw_kernel, dim3(B), dim3(kScanThreads), 0, s, tl, dl, tokens,
+                     u_sample, B, K, V, out_tokens, n_emitted, ws);
+  return hipGetLastError();
+}
+
+}  // namespace specv

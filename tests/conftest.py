@@ -23,3 +23,23 @@ def golden():
         with open(os.path.join(GOLDEN, name)) as f:
             return json.load(f)
     return load
+
+
+@pytest.fixture(scope="session")
+def sv():
+    """The binding of libspecverify.so; builds the library first if it is absent."""
+    from speculative_decoding_verification_gemm_amd import build as _build
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    import speculative_decoding_verification_gemm_amd as mod
+    return mod
+
+
+@pytest.fixture(scope="session")
+def dev(sv):
+    """cuda:0, which must be an MI355X for the gpu-marked tests."""
+    import torch
+    assert torch.cuda.is_available(), "gpu-marked test needs a GPU"
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    assert name.startswith("gfx950"), f"needs gfx950, found {name}"
+    return torch.device("cuda:0")

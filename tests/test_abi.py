@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports every call include/spec_verify.h
+declares, and rejects bad arguments before any HIP call (CPU only: no call
+here reaches the device)."""
+
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+A = 0x10000          # a 256-byte aligned stand-in address; never dereferenced
+MIS = 0x10001        # misaligned stand-in
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(sv):
+    names = declared_functions()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(sv.lib, n), n
+
+
+def test_binding_covers_exactly_the_header(sv):
+    assert sorted(sv.SIGNATURES) == declared_functions()
+
+
+def test_version_and_status_strings(sv):
+    assert sv.abi_version() == 1
+    for code, name in [(0, b"SPEC_OK"), (-1, b"SPEC_ERR_INVALID_ARGUMENT"),
+                       (-2, b"SPEC_ERR_ALIGNMENT"), (-3, b"SPEC_ERR_UNSUPPORTED"),
+                       (-4, b"SPEC_ERR_WORKSPACE"), (-5, b"SPEC_ERR_HIP")]:
+        assert sv.lib.spec_status_string(code) == name
+
+
+GEMM_BAD = [
+    ((None, A, A, 0, 5, 4096, 4096), -1),
+    ((A, None, A, 0, 5, 4096, 4096), -1),
+    ((A, A, None, 0, 5, 4096, 4096), -1),
+    ((A, A, A, 7, 5, 4096, 4096), -1),
+    ((A, A, A, 0, 0, 4096, 4096), -1),
+    ((A, A, A, 0, 65537, 4096, 4096), -1),
+    ((A, A, A, 0, 5, 4100, 4096), -1),
+    ((A, A, A, 0, 5, 0, 4096), -1),
+    ((A, A, A, 0, 5, (1 << 20) + 8, 4096), -1),
+    ((A, A, A, 0, 5, 4096, 0), -1),
+    ((A, A, A, 0, 5, 4096, (1 << 24) + 1), -1),
+    ((A + 8, A, A, 0, 5, 4096, 4096), -2),
+    ((A, A + 8, A, 0, 5, 4096, 4096), -2),
+    ((A, A, A + 2, 0, 5, 4096, 4096), -2),
+    ((A, A, MIS, 1, 5, 4096, 4096), -2),
+]
+
+
+@pytest.mark.parametrize("args,code", GEMM_BAD)
+def test_gemm_rejects(sv, args, code):
+    assert sv.lib.spec_verify_gemm(*args, None) == code
+    assert sv.lib.spec_last_error()
+
+
+def test_softmax_rejects(sv):
+    f = sv.lib.spec_softmax
+    assert f(None, 1, 10, A, A, A, None) == -1
+    assert f(A, 0, 10, A, A, A, None) == -1
+    assert f(A, 1, 0, A, A, A, None) == -1
+    assert f(A, 1, (1 << 26) + 1, A, A, A, None) == -1
+    assert f(MIS, 1, 10, A, A, A, None) == -2
+    assert f(A, 1, 10, MIS, None, None, None) == -2
+    # nothing requested: a no-op that succeeds without touching the device
+    assert f(A, 3, 10, None, None, None, None) == 0
+
+
+@pytest.mark.parametrize("B,K,V,code", [(0, 4, 10, -1), (1, 0, 10, -1), (1, 65, 10, -1),
+                                        (1, 4, 0, -1), ((1 << 20) + 1, 4, 10, -1)])
+def test_accept_and_sample_reject_sizes(sv, B, K, V, code):
+    assert sv.lib.spec_accept_scan(A, A, A, A, B, K, V, A, None, None) == code
+    assert sv.lib.spec_residual_sample(A, A, A, A, B, K, V, A, None, None) == code
+
+
+def test_accept_and_sample_reject_pointers(sv):
+    assert sv.lib.spec_accept_scan(A, A, None, A, 1, 4, 10, A, None, None) == -1
+    assert sv.lib.spec_accept_scan(A, A, A, A, 1, 4, 10, None, None, None) == -1
+    assert sv.lib.spec_accept_scan(A, MIS, A, A, 1, 4, 10, A, None, None) == -2
+    assert sv.lib.spec_residual_sample(A, A, None, A, 1, 4, 10, A, None, None) == -1
+    assert sv.lib.spec_residual_sample(A, A, A, A, 1, 4, 10, None, None, None) == -1
+    assert sv.lib.spec_residual_sample(A, A, A, MIS, 1, 4, 10, A, None, None) == -2
+
+
+def test_workspace_bytes(sv):
+    f = sv.lib.spec_verify_workspace_bytes
+    assert f(0, 4, 10) == 0 and f(1, 0, 10) == 0 and f(1, 65, 10) == 0 and f(1, 4, 0) == 0
+    a, b = f(1, 4, 128256), f(64, 8, 128256)
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+
+
+def _verify(sv, hidden=None, lm=None, d=0, B=1, K=4, V=1000, ws=A, wsb=None, tl=A):
+    if wsb is None:
+        wsb = sv.lib.spec_verify_workspace_bytes(B, K, V)
+    return sv.lib.spec_verify(hidden, lm, d, tl, A, A, A, A, B, K, V, A, A, ws, wsb, None)
+
+
+def test_verify_rejects(sv):
+    assert _verify(sv, tl=None) == -1
+    assert _verify(sv, ws=None) == -1
+    assert _verify(sv, hidden=A) == -1                       # lm_head missing
+    assert _verify(sv, lm=A) == -1                           # hidden missing
+    assert _verify(sv, K=65) == -1
+    assert _verify(sv, hidden=A, lm=A, d=12) == -1           # d % 8 != 0
+    assert _verify(sv, hidden=A + 8, lm=A, d=256) == -2
+    assert _verify(sv, B=20000, K=4, V=1000, hidden=A, lm=A, d=256) == -1  # M > 65536
+    assert _verify(sv, B=1 << 20, K=64, V=1 << 20) == -1     # grid bound
+    assert _verify(sv, wsb=100) == -4
+    assert _verify(sv, ws=A + 16) == -4

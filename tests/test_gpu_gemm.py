@@ -1,0 +1,143 @@
+"""GPU parity of spec_verify_gemm against the fp64 oracle.
+
+Tolerance: max |y - y_ref| / max(|y_ref|, rms of the reference row) <= 2e-2
+(bf16 inputs, fp32 accumulation). fp32 outputs must also meet 1e-3, a bound
+derived from fp32 accumulation (a few d_in^(1/2) * 2^-24 of the row scale);
+a dropped segment of the reduction (1/32 of d_in) would miss it by far.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+TOL_F32 = 1e-3
+
+
+def rel_err(y, ref):
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    return float(np.max(np.abs(y - ref) / np.maximum(np.abs(ref), rms)))
+
+
+def run_host(sv, dev, x_bits, w_bits, out_dtype):
+    import torch
+    from synth import device as sd
+    x = sd.from_bits(x_bits, dev)
+    w = sd.from_bits(w_bits, dev)
+    y = sv.verify_gemm(x, w, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def check(y, ref, out_dtype, what):
+    import torch
+    e = rel_err(y, ref)
+    print(f"{what}: rel err {e:.3e}", flush=True)
+    assert e <= TOL, what
+    if out_dtype == torch.float32:
+        assert e <= TOL_F32, what
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_tiny_linear(sv, dev, out):
+    import torch
+    d = synth.tiny(1)
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    y = run_host(sv, dev, d["x_bits"], d["w_bits"], od)
+    check(y, oracle.linear(d["x_bits"], d["w_bits"]), od, f"tiny {out}")
+
+
+# ragged d_in (not a multiple of the 128-element segment) and d_out (not a
+# multiple of the rows per workgroup); 9000 spans several activation chunks
+@pytest.mark.parametrize("M", list(range(1, 17)))
+@pytest.mark.parametrize("d_in,d_out", [(1032, 777), (9000, 300)])
+def test_stream_kernel_every_m(sv, dev, M, d_in, d_out):
+    import torch
+    x, w = synth.linear_inputs(100 + M, f"stream{d_in}", M, d_in, d_out)
+    y = run_host(sv, dev, x, w, torch.float32)
+    check(y, oracle.linear(x, w), torch.float32, f"stream M={M} {d_in}->{d_out}")
+
+
+@pytest.mark.parametrize("M", [17, 20, 33, 64, 80, 130, 320])
+def test_mfma_kernel(sv, dev, M):
+    import torch
+    x, w = synth.linear_inputs(200 + M, "mfma", M, 1032, 777)
+    for od in (torch.float32, torch.bfloat16):
+        y = run_host(sv, dev, x, w, od)
+        check(y, oracle.linear(x, w), od, f"mfma M={M} {od}")
+
+
+def test_edge_shapes(sv, dev):
+    import torch
+    for M, d_in, d_out in [(1, 8, 1), (5, 8, 3), (16, 16, 1), (17, 8, 1), (2, 2048 + 8, 65)]:
+        x, w = synth.linear_inputs(7, f"edge{M}.{d_in}.{d_out}", M, d_in, d_out)
+        y = run_host(sv, dev, x, w, torch.float32)
+        check(y, oracle.linear(x, w), torch.float32, f"edge {M}x{d_in}->{d_out}")
+
+
+def sampled_full_size(sv, dev, M, d_in, d_out, seed, out_dtype, n_rows=48):
+    """Full-size linear on the device; the oracle checks a sample of output
+    columns (first and last 8 plus random ones)."""
+    import torch
+    from synth import device as sd
+    w = sd.normal_bf16((d_out, d_in), synth.WEIGHT_STD, seed, dev)
+    x = sd.normal_bf16((M, d_in), 1.0, seed + 1, dev)
+    y = sv.verify_gemm(x, w, out_dtype=out_dtype)
+    rng = np.random.default_rng(seed)
+    cols = np.unique(np.concatenate([np.arange(8), np.arange(d_out - 8, d_out),
+                                     rng.integers(0, d_out, n_rows)]))
+    idx = torch.from_numpy(cols).to(dev)
+    w_rows = sd.to_bits(w.index_select(0, idx))
+    x_bits = sd.to_bits(x)
+    y_s = y.index_select(1, idx).float().cpu().numpy().astype(np.float64)
+    del w, y
+    torch.cuda.empty_cache()
+    return y_s, oracle.linear(x_bits, w_rows)
+
+
+LLAMA8B = [(4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096)]
+LLAMA70B = [(8192, 10240), (8192, 8192), (8192, 57344), (28672, 8192)]
+
+
+@pytest.mark.parametrize("d_in,d_out", LLAMA8B + LLAMA70B)
+def test_full_size_stack_linears_m5(sv, dev, d_in, d_out):
+    import torch
+    y, ref = sampled_full_size(sv, dev, 5, d_in, d_out, d_in + d_out, torch.bfloat16)
+    check(y, ref, torch.bfloat16, f"M=5 {d_in}->{d_out} bf16")
+
+
+@pytest.mark.parametrize("d_in", [4096, 8192])
+def test_full_size_lm_head_m5(sv, dev, d_in):
+    import torch
+    y, ref = sampled_full_size(sv, dev, 5, d_in, 128256, 77 + d_in, torch.float32, n_rows=200)
+    check(y, ref, torch.float32, f"lm-head {d_in}->128256")
+
+
+@pytest.mark.parametrize("M", [20, 80, 320, 1280])
+@pytest.mark.parametrize("d_in,d_out", [(4096, 28672), (14336, 4096)])
+def test_batch_sweep_shapes(sv, dev, M, d_in, d_out):
+    import torch
+    y, ref = sampled_full_size(sv, dev, M, d_in, d_out, 31 * M + d_in, torch.bfloat16)
+    check(y, ref, torch.bfloat16, f"sweep M={M} {d_in}->{d_out}")
+
+
+def test_batch_sweep_lm_head_m1280(sv, dev):
+    import torch
+    y, ref = sampled_full_size(sv, dev, 1280, 4096, 128256, 5, torch.float32)
+    check(y, ref, torch.float32, "sweep M=1280 lm-head")
+
+
+@pytest.mark.parametrize("M", [5, 80])
+def test_deterministic(sv, dev, M):
+    import torch
+    from synth import device as sd
+    w = sd.normal_bf16((6144, 4096), 0.02, 3, dev)
+    x = sd.normal_bf16((M, 4096), 1.0, 4, dev)
+    a = sv.verify_gemm(x, w)
+    b = sv.verify_gemm(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

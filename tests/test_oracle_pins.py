@@ -416,3 +416,14 @@ def test_monte_carlo_three_token_acceptance(golden):
     assert abs(acc.mean() - a) < 4 * math.sqrt(a * (1 - a) / R)
     emp = np.bincount(out, minlength=3) / R
     assert np.all(np.abs(emp - p) < 4 * np.sqrt(p * (1 - p) / R))
+
+
+def test_invalid_inputs_have_defined_results():
+    P = [np.array([0.5, 0.5])] * 2
+    Q = [np.array([0.5, 0.5])]
+    for bad in (-1, 2):
+        acc, ratio, _ = oracle.accept_test(P, Q, [bad], [0.0])
+        assert not acc[0] and ratio[0] == 0.0
+    assert oracle.inverse_cdf(np.zeros(4), 0.3)[0] == -1
+    tok, _, _ = spec.sample_batch(np.array([P]), np.array([Q]), [2], [[0.5, 0.5]])
+    assert tok[0] == -1
