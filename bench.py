@@ -1,0 +1,330 @@
+"""Verify-step benchmark on one MI355X.
+
+One step is the whole hot path of a speculative-decoding verify pass over
+synthetic Llama-shaped inputs already resident in HBM:
+
+  1. the target's linear stack over M = B*(K+1) positions: per layer QKV,
+     O, gate/up and down, each a spec_verify_gemm that reads its bf16
+     weights once (bf16 outputs);
+  2. the lm-head (spec_verify_gemm, fp32 logits over the vocabulary);
+  3. the sampling stage (spec_verify on those logits): softmax statistics,
+     accept test and first rejection, residual or bonus draw, emit.
+
+Each phase is captured once in a HIP graph; a timed step replays the two
+graphs back to back with HIP events between them on the same stream.
+Prints one JSON line (see README-level docs in the design doc for the fields).
+
+    python bench.py [--steps K] [--warmup W] [--workload llama8b|llama70b]
+                    [--batch B] [--no-graph] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA
+K_DRAFT = 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=["llama8b", "llama70b"], default="llama8b")
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="one spec_verify_gemm launch per linear instead of one chain launch")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=2026)
+    return ap.parse_args()
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "speculative_decoding_verification_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name):
+    """HBM traffic per launch measured with rocprofv3 counters, if it was
+    taken on the current kernel source (profiles/<name>.txt)."""
+    path = os.path.join(ROOT, "profiles", name + ".txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Workload:
+    """Device-resident inputs of one verify step."""
+
+    def __init__(self, stack, B, K, seed, dev):
+        import torch
+        import synth
+        from synth import device as sd
+
+        self.stack, self.B, self.K, self.dev = stack, B, K, dev
+        self.M = B * (K + 1)
+        self.linears = []  # (name, x, w, y)
+        for i, (name, d_in, d_out) in enumerate(stack.all_linears()[:-1]):
+            w = sd.normal_bf16((d_out, d_in), synth.WEIGHT_STD, seed * 1000 + 2 * i, dev)
+            x = sd.normal_bf16((self.M, d_in), 1.0, seed * 1000 + 2 * i + 1, dev)
+            y = torch.empty((self.M, d_out), dtype=torch.bfloat16, device=dev)
+            self.linears.append((name, x, w, y))
+        V, d = stack.vocab, stack.hidden
+        self.V = V
+        self.lm_head = sd.normal_bf16((V, d), synth.WEIGHT_STD, seed * 7 + 1, dev)
+        self.hidden = sd.normal_bf16((self.M, d), 1.0, seed * 7 + 2, dev)
+        self.target_logits = torch.empty((B, K + 1, V), dtype=torch.float32, device=dev)
+        self.out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        self.n_emitted = torch.empty(B, dtype=torch.int32, device=dev)
+        self.u_accept = sd.uniform_f32((B, K), seed * 7 + 3, dev)
+        self.u_sample = sd.uniform_f32((B, K + 1), seed * 7 + 4, dev)
+        torch.cuda.synchronize()
+
+    def make_drafts(self, sv, sigma, seed):
+        """Draft logits = the lm-head's logits + sigma * N(0,1); draft tokens
+        from the draft distributions (Gumbel-max)."""
+        import torch
+        from synth import device as sd
+        sv.verify_gemm(self.hidden, self.lm_head, out=self.target_logits.view(self.M, self.V))
+        tl = self.target_logits[:, :self.K, :]
+        self.draft_logits = (tl + sd.normal_f32(tl.shape, sigma, seed * 7 + 5, self.dev)).contiguous()
+        self.draft_tokens = sd.gumbel_max_tokens(self.draft_logits, seed * 7 + 6)
+        self.workspace = sv.new_workspace(self.B, self.K, self.V, self.dev)
+        torch.cuda.synchronize()
+
+    def make_chain(self, sv):
+        """All stack linears and the lm-head as one chain (one launch)."""
+        lin = [(x, w, y) for _, x, w, y in self.linears]
+        lin.append((self.hidden, self.lm_head, self.target_logits.view(self.M, self.V)))
+        self.chain = sv.Chain(lin, self.dev)
+
+    def gemm_phase(self, sv):
+        if getattr(self, "chain", None) is not None:
+            self.chain.run()
+            return
+        for _, x, w, y in self.linears:
+            sv.verify_gemm(x, w, out=y)
+        sv.verify_gemm(self.hidden, self.lm_head, out=self.target_logits.view(self.M, self.V))
+
+    def sampling_phase(self, sv):
+        sv.verify(self.target_logits, self.draft_logits, self.draft_tokens, self.u_accept,
+                  self.u_sample, workspace=self.workspace, out_tokens=self.out_tokens,
+                  n_emitted=self.n_emitted)
+
+    def gemm_bytes(self):
+        """Algorithmic HBM bytes of the GEMM phase: every weight once, every
+        activation once, every output once (bf16 stack outputs, fp32 logits)."""
+        total = 0
+        for _, x, w, y in self.linears:
+            total += 2 * w.numel() + 2 * x.numel() + 2 * y.numel()
+        total += 2 * self.lm_head.numel() + 2 * self.hidden.numel() + 4 * self.target_logits.numel()
+        return total
+
+    def gemm_flops(self):
+        n = sum(2 * x.shape[0] * w.numel() for _, x, w, _ in self.linears)
+        return n + 2 * self.M * self.lm_head.numel()
+
+    def n_gemm_launches(self):
+        if getattr(self, "chain", None) is not None:
+            return 1
+        return len(self.linears) + 1
+
+
+def cpu_baseline(wl, sample_layers=None):
+    """The fp64 oracle on the host cores, on a bounded sample of the same
+    step: the first layer's linears, the lm-head and the sampling stage on
+    the GPU step's inputs; the remaining layers are scaled from the first."""
+    import numpy as np
+    import oracle
+    from synth import device as sd
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    per_layer = len(wl.stack.linears)
+    if sample_layers is None:
+        sample_layers = wl.stack.layers
+    t_layer = 0.0
+    for name, x, w, _ in wl.linears[:per_layer * sample_layers]:
+        xb, wb = sd.to_bits(x), sd.to_bits(w)
+        t0 = time.perf_counter()
+        oracle.linear(xb, wb)
+        t_layer += time.perf_counter() - t0
+    t_layer /= sample_layers
+    xb, wb = sd.to_bits(wl.hidden), sd.to_bits(wl.lm_head)
+    t0 = time.perf_counter()
+    logits = oracle.linear(xb, wb).astype(np.float32).reshape(wl.B, wl.K + 1, wl.V)
+    t_lm = time.perf_counter() - t0
+    dl = wl.draft_logits.cpu().numpy()
+    toks = wl.draft_tokens.cpu().numpy()
+    ua, us = wl.u_accept.cpu().numpy(), wl.u_sample.cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.verify_batch(logits, dl, toks, ua, us)
+    t_samp = time.perf_counter() - t0
+    t_step = t_layer * wl.stack.layers + t_lm + t_samp
+    return {
+        "value": wl.M / t_step,
+        "unit": "positions/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{sample_layers} of {wl.stack.layers} layers ({per_layer} linears each, "
+                   f"{t_layer:.2f} s/layer, scaled x{wl.stack.layers}) + lm-head "
+                   f"({t_lm:.2f} s) + sampling stage ({t_samp:.3f} s); fp64 numpy, "
+                   f"BLAS threads={threads}, numpy conversion single-threaded"),
+        "s_per_step": t_step,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import speculative_decoding_verification_gemm_amd as sv
+
+    dev = torch.device("cuda:0")
+    stack = {"llama8b": synth.LLAMA_8B, "llama70b": synth.LLAMA_70B_16L}[args.workload]
+    key = {"llama8b": "llama8b_lm_head", "llama70b": "llama70b_lm_head"}[args.workload]
+    B, K = args.batch, K_DRAFT
+    wl = Workload(stack, B, K, args.seed, dev)
+    wl.make_drafts(sv, synth.draft_noise_sigma(key, 0.8), args.seed)
+    use_chain = not args.no_chain and wl.M <= 16
+    if use_chain:
+        wl.make_chain(sv)
+
+    # eager pass (also initialises the library's per-device state)
+    wl.gemm_phase(sv)
+    wl.sampling_phase(sv)
+    torch.cuda.synchronize()
+
+    if args.no_graph:
+        run_gemm = lambda: wl.gemm_phase(sv)  # noqa: E731
+        run_samp = lambda: wl.sampling_phase(sv)  # noqa: E731
+    else:
+        g_gemm, g_samp = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_gemm):
+            wl.gemm_phase(sv)
+        with torch.cuda.graph(g_samp):
+            wl.sampling_phase(sv)
+        torch.cuda.synchronize()
+        run_gemm, run_samp = g_gemm.replay, g_samp.replay
+
+    for _ in range(args.warmup):
+        run_gemm()
+        run_samp()
+    torch.cuda.synchronize()
+
+    n = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    emitted = torch.zeros(B, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        ev[i][0].record()
+        run_gemm()
+        ev[i][1].record()
+        run_samp()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_gemm = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    t_samp = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    t_step = sorted(e[0].elapsed_time(e[2]) for e in ev)
+    emitted += wl.n_emitted.long()
+    med = lambda a: a[len(a) // 2]  # noqa: E731
+    ms_step = sum(t_step) / n
+    ms_gemm = sum(t_gemm) / n
+    ms_samp = sum(t_samp) / n
+
+    gemm_bytes = wl.gemm_bytes()
+    launches = wl.n_gemm_launches()
+    achieved = gemm_bytes / (ms_gemm * 1e-3) / 1e9
+    traffic = load_traffic(f"traffic_gemm_stream_{args.workload}_b{B}")
+
+    line = {
+        "metric": f"verified positions/s at K={K} ({stack.name} shapes)",
+        "value": wl.M / (ms_step * 1e-3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) bf16 weights, "
+                "draft logits = target logits + calibrated noise, alpha~0.8)",
+        "config": {
+            "workload": (f"{stack.name} verify step: {stack.layers} layers x (QKV, O, gate/up, "
+                         f"down) + lm-head {stack.hidden}->{stack.vocab} + sampling"),
+            "global_batch": B,
+            "draft_tokens_K": K,
+            "positions_M": wl.M,
+            "vocab": wl.V,
+            "graph": not args.no_graph,
+            "gemm_launch": "chain" if use_chain else "per-linear",
+        },
+        "pct_hbm_peak_in_verify": 100.0 * achieved / HBM_PEAK_GBS,
+        "ms_gemm_phase": ms_gemm,
+        "ms_sampling_phase": ms_samp,
+        "sampling_share": ms_samp / ms_step,
+        "ms_step_p10_p50_p90": [t_step[n // 10], med(t_step), t_step[(9 * n) // 10]],
+        "wall_s": wall,
+        "mean_emitted_per_sequence_last_step": float(emitted.float().mean()),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": ("gemm_stream chain (all stack linears + lm-head in one launch)" if use_chain
+                       else "gemm_stream per linear (stack linears + lm-head)"),
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": gemm_bytes / launches,
+            "launches_per_step": launches,
+            "avg_launch_ms": ms_gemm / launches,
+            "gemm_tflops": wl.gemm_flops() / (ms_gemm * 1e-3) / 1e12,
+        },
+        "cpu_baseline": None,
+    }
+    if use_chain:
+        err = wl.chain.error()
+        if err:
+            print(f"chain reported device error {err}", file=sys.stderr)
+            sys.exit(3)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -94,6 +94,68 @@ int spec_verify_gemm(const uint16_t* x, const uint16_t* w, void* y, int y_dtype,
                      int M, int d_in, int d_out, void* stream);
 
 /*
+ * spec_linear -- one linear of a chain (see spec_chain_prepare).
+ *   x        bf16 [M][d_in], 16-byte aligned (read only after the previous
+ *            linear of the chain has completed, so it may be that linear's y).
+ *   w        bf16 [d_out][d_in], 16-byte aligned.
+ *   y        [M][d_out], fp32 or bf16 as y_dtype says.
+ *   d_in, d_out, y_dtype  as for spec_verify_gemm; reserved must be 0.
+ */
+typedef struct spec_linear {
+  const uint16_t* x;
+  const uint16_t* w;
+  void* y;
+  int32_t d_in;
+  int32_t d_out;
+  int32_t y_dtype;
+  int32_t reserved;
+} spec_linear;
+
+/* Bytes of chain workspace for n linears; 0 if n is out of range. */
+size_t spec_chain_workspace_bytes(int n);
+
+/*
+ * spec_chain_prepare -- validate a chain of n linears over the same M rows
+ * and record it in `workspace` (device memory, 256-byte aligned, at least
+ * spec_chain_workspace_bytes(n) bytes, owned by the caller and not used for
+ * anything else while the chain is in use).
+ *
+ * `linears` is a HOST array; every descriptor is checked as spec_verify_gemm
+ * checks its arguments. The call is synchronous (it copies the descriptors
+ * to the device and resets the workspace's counters) and must not be
+ * captured in a graph. 1 <= n <= 4096, 1 <= M <= 16 (the weight-streaming
+ * regime).
+ */
+int spec_chain_prepare(const spec_linear* linears, int n, int M, void* workspace,
+                       size_t workspace_bytes);
+
+/*
+ * spec_verify_gemm_chain -- run a prepared chain in one launch.
+ *
+ * Computes every linear of the chain in order, each exactly as
+ * spec_verify_gemm would, in ONE pass that streams all weights: the K+1
+ * verify positions cross the whole linear stack with a single read of every
+ * weight ("What Actually Happens During Speculative Decoding in LLMs": the
+ * weights are loaded once for all candidate positions). Linear i+1 reads its
+ * x only after linear i's y is complete and visible (device-scope
+ * release/acquire), as the next layer of a forward pass would; weight loads
+ * of linear i+1, which depend on nothing, start before that point. n and M
+ * must be those given to spec_chain_prepare (checked on the device: a
+ * mismatch computes nothing and sets bit 1 of spec_chain_error). The call
+ * is asynchronous and capturable; launches that use the same workspace must
+ * be ordered (same stream).
+ */
+int spec_verify_gemm_chain(int n, int M, void* workspace, void* stream);
+
+/*
+ * spec_chain_error -- read and clear the device-side error word of a chain
+ * workspace (synchronous). *error receives 0 if all is well; bit 0: a
+ * workgroup gave up waiting at a barrier (its outputs are not valid); bit 1:
+ * a launch did not match the prepared plan.
+ */
+int spec_chain_error(void* workspace, int* error);
+
+/*
  * spec_softmax -- p = softmax(logits) per row, T = 1.
  *
  * ("Speculative Decoding: Two Models, One Voice", Implementing it against a

@@ -51,12 +51,23 @@ SIGNATURES = {
     "spec_accept_scan": (_i, [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p]),
     "spec_residual_sample": (_i, [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p]),
     "spec_verify_workspace_bytes": (_z, [_i, _i, _i]),
+    "spec_chain_workspace_bytes": (_z, [_i]),
+    "spec_chain_prepare": (_i, [_p, _i, _i, _p, _z]),
+    "spec_verify_gemm_chain": (_i, [_i, _i, _p, _p]),
+    "spec_chain_error": (_i, [_p, ctypes.POINTER(ctypes.c_int)]),
     "spec_verify": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _z, _p]),
 }
 for _name, (_res, _args) in SIGNATURES.items():
     _fn = getattr(lib, _name)
     _fn.restype = _res
     _fn.argtypes = _args
+
+
+class SpecLinear(ctypes.Structure):
+    """spec_linear of include/spec_verify.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("w", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("y_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -226,3 +237,47 @@ def verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
                           _ptr(u_sample), B, K, V, _ptr(out_tokens), _ptr(n_emitted),
                           _ptr(workspace), workspace.numel(), _stream()))
     return out_tokens, n_emitted
+
+
+class Chain:
+    """A prepared chain of linears (spec_chain_prepare) and its workspace.
+
+    linears: list of (x, w, y) device tensors, x bf16 [M][d_in], w bf16
+    [d_out][d_in], y fp32 or bf16 [M][d_out]. The tensors must stay alive
+    while the chain is used."""
+
+    def __init__(self, linears, device="cuda"):
+        torch = _torch()
+        if not linears:
+            raise ValueError("empty chain")
+        M = linears[0][0].shape[0]
+        descs = (SpecLinear * len(linears))()
+        for i, (x, w, y) in enumerate(linears):
+            _need(x, torch.bfloat16, f"x[{i}]", 2)
+            _need(w, torch.bfloat16, f"w[{i}]", 2)
+            _need(y, y.dtype, f"y[{i}]", 2)
+            code = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16}.get(y.dtype)
+            if code is None:
+                raise TypeError(f"y[{i}] must be float32 or bfloat16")
+            if x.shape[0] != M or tuple(y.shape) != (M, w.shape[0]) or x.shape[1] != w.shape[1]:
+                raise ValueError(f"linear {i}: shapes x {tuple(x.shape)}, w {tuple(w.shape)}, "
+                                 f"y {tuple(y.shape)} disagree")
+            descs[i] = SpecLinear(x.data_ptr(), w.data_ptr(), y.data_ptr(), x.shape[1],
+                                  w.shape[0], code, 0)
+        self.n, self.M = len(linears), M
+        self.keep = list(linears)
+        nbytes = lib.spec_chain_workspace_bytes(self.n)
+        if nbytes == 0:
+            raise ValueError(f"chain of {self.n} linears is out of range")
+        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        torch.cuda.synchronize()
+        check(lib.spec_chain_prepare(descs, self.n, self.M, _ptr(self.workspace), nbytes))
+
+    def run(self):
+        check(lib.spec_verify_gemm_chain(self.n, self.M, _ptr(self.workspace), _stream()))
+
+    def error(self):
+        """Read and clear the device-side error word (synchronous)."""
+        e = ctypes.c_int(0)
+        check(lib.spec_chain_error(_ptr(self.workspace), ctypes.byref(e)))
+        return e.value

@@ -5,7 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+#include <stddef.h>
 
 #include <atomic>
 
@@ -28,11 +30,13 @@ void clear_error() { g_err[0] = '\0'; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Per-device answer to "is this a gfx950?": 0 unknown, 1 yes, -1 no.
+// Per-device answer to "is this a gfx950?" (0 unknown, 1 yes, -1 no) and
+// its compute-unit count.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];
+std::atomic<int> g_cus[kMaxDevices];
 
-int check_device() {
+int check_device(int* cus = nullptr) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(SPEC_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -43,11 +47,32 @@ int check_device() {
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess)
       return fail(SPEC_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    g_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1,
+                     std::memory_order_relaxed);
     ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
     g_arch_ok[dev].store(ok, std::memory_order_relaxed);
   }
   if (ok < 0) return fail(SPEC_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  if (cus) *cus = g_cus[dev].load(std::memory_order_relaxed);
   return SPEC_OK;
+}
+
+// Resident workgroups per CU for the streaming kernel: the occupancy limit,
+// capped at 2 (measured best for the Llama-shaped linears); the
+// SPECV_STREAM_WGS_PER_CU environment variable overrides the cap.
+std::atomic<int> g_stream_occ[17];
+int stream_wgs_per_cu(int M) {
+  int occ = g_stream_occ[M].load(std::memory_order_relaxed);
+  if (occ == 0) {
+    occ = specv::stream_max_wgs_per_cu(M);
+    g_stream_occ[M].store(occ, std::memory_order_relaxed);
+  }
+  int cap = 2;
+  if (const char* env = getenv("SPECV_STREAM_WGS_PER_CU")) {
+    const int v = atoi(env);
+    if (v > 0) cap = v;
+  }
+  return occ < cap ? occ : cap;
 }
 
 int launched(hipError_t e, const char* what) {
@@ -91,11 +116,23 @@ int check_bkv(int B, int K, int V) {
 }
 
 int run_gemm(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M, int d_in,
-             int d_out, hipStream_t s) {
-  hipError_t e = (M <= specv::kMaxStreamM)
-                     ? specv::launch_gemm_stream(x, w, y, out_bf16, M, d_in, d_out, s)
-                     : specv::launch_gemm_mfma(x, w, y, out_bf16, M, d_in, d_out, s);
+             int d_out, int cus, hipStream_t s) {
+  hipError_t e;
+  if (M <= specv::kMaxStreamM)
+    e = specv::launch_gemm_stream(x, w, y, out_bf16, M, d_in, d_out, cus * stream_wgs_per_cu(M), s);
+  else
+    e = specv::launch_gemm_mfma(x, w, y, out_bf16, M, d_in, d_out, s);
   return launched(e, "spec_verify_gemm");
+}
+
+constexpr int kMaxChain = 4096;
+
+size_t chain_counts_offset() { return sizeof(specv::ChainSync); }
+size_t chain_desc_offset(int n) {
+  return (chain_counts_offset() + specv::chain_counts_bytes(n) + 63) & ~(size_t)63;
+}
+size_t chain_bytes(int n) {
+  return (chain_desc_offset(n) + (size_t)n * sizeof(specv::StreamLinear) + 255) & ~(size_t)255;
 }
 
 }  // namespace
@@ -123,9 +160,103 @@ int spec_verify_gemm(const uint16_t* x, const uint16_t* w, void* y, int y_dtype,
   clear_error();
   int rc = check_gemm_args(x, w, y, y_dtype, M, d_in, d_out);
   if (rc != SPEC_OK) return rc;
-  if ((rc = check_device()) != SPEC_OK) return rc;
-  return run_gemm(x, w, y, y_dtype == SPEC_BF16, M, d_in, d_out,
+  int cus = 0;
+  if ((rc = check_device(&cus)) != SPEC_OK) return rc;
+  return run_gemm(x, w, y, y_dtype == SPEC_BF16, M, d_in, d_out, cus,
                   static_cast<hipStream_t>(stream));
+}
+
+size_t spec_chain_workspace_bytes(int n) {
+  if (n < 1 || n > kMaxChain) return 0;
+  return chain_bytes(n);
+}
+
+int spec_chain_prepare(const spec_linear* linears, int n, int M, void* workspace,
+                       size_t workspace_bytes) {
+  clear_error();
+  if (!linears || !workspace) return fail(SPEC_ERR_INVALID_ARGUMENT, "null linears or workspace");
+  if (n < 1 || n > kMaxChain)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "n=%d outside [1, %d]", n, kMaxChain);
+  if (M < 1 || M > specv::kMaxStreamM)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "chain M=%d outside [1, %d]", M, specv::kMaxStreamM);
+  for (int i = 0; i < n; ++i) {
+    const spec_linear& d = linears[i];
+    int rc = check_gemm_args(d.x, d.w, d.y, d.y_dtype, M, d.d_in, d.d_out);
+    if (rc != SPEC_OK) {
+      char msg[512];
+      snprintf(msg, sizeof(msg), "linear %d: %s", i, g_err);
+      return fail(rc, "%s", msg);
+    }
+    if (d.reserved != 0) return fail(SPEC_ERR_INVALID_ARGUMENT, "linear %d: reserved != 0", i);
+  }
+  if (workspace_bytes < chain_bytes(n))
+    return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                chain_bytes(n));
+  if (!aligned(workspace, 256)) return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  int rc = check_device();
+  if (rc != SPEC_OK) return rc;
+  // header + zeroed counters + descriptors, assembled on the host
+  const size_t bytes = chain_bytes(n);
+  char* img = static_cast<char*>(calloc(1, bytes));
+  if (!img) return fail(SPEC_ERR_HIP, "host staging allocation failed");
+  specv::ChainSync hdr{};
+  hdr.magic = specv::kChainMagic;
+  hdr.n = n;
+  hdr.M = M;
+  // Diagnostics: SPECV_CHAIN_TRACE=<device address of n * grid * 2 uint64>
+  // records, per linear and workgroup, the wall clock at arrival and at the
+  // end of the wait (100 MHz ticks).
+  if (const char* env = getenv("SPECV_CHAIN_TRACE")) {
+    unsigned long long v = strtoull(env, nullptr, 0);
+    hdr.trace = reinterpret_cast<unsigned long long*>(v);
+  }
+  memcpy(img, &hdr, sizeof(hdr));
+  specv::StreamLinear* descs = reinterpret_cast<specv::StreamLinear*>(img + chain_desc_offset(n));
+  for (int i = 0; i < n; ++i)
+    descs[i] = specv::StreamLinear{linears[i].x, linears[i].w, linears[i].y, linears[i].d_in,
+                                   linears[i].d_out, linears[i].y_dtype == SPEC_BF16 ? 1 : 0, 0};
+  hipError_t e = hipMemcpy(workspace, img, bytes, hipMemcpyHostToDevice);
+  free(img);
+  if (e != hipSuccess) return fail(SPEC_ERR_HIP, "chain upload: %s", hipGetErrorString(e));
+  return SPEC_OK;
+}
+
+int spec_verify_gemm_chain(int n, int M, void* workspace, void* stream) {
+  clear_error();
+  if (!workspace) return fail(SPEC_ERR_INVALID_ARGUMENT, "null workspace");
+  if (n < 1 || n > kMaxChain)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "n=%d outside [1, %d]", n, kMaxChain);
+  if (M < 1 || M > specv::kMaxStreamM)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "chain M=%d outside [1, %d]", M, specv::kMaxStreamM);
+  if (!aligned(workspace, 256)) return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  int cus = 0;
+  int rc = check_device(&cus);
+  if (rc != SPEC_OK) return rc;
+  char* base = static_cast<char*>(workspace);
+  return launched(
+      specv::launch_gemm_chain(reinterpret_cast<const specv::StreamLinear*>(base + chain_desc_offset(n)),
+                               n, reinterpret_cast<specv::ChainSync*>(base), M,
+                               cus * stream_wgs_per_cu(M), static_cast<hipStream_t>(stream)),
+      "spec_verify_gemm_chain");
+}
+
+int spec_chain_error(void* workspace, int* error) {
+  clear_error();
+  if (!workspace || !error) return fail(SPEC_ERR_INVALID_ARGUMENT, "null workspace or error");
+  if (!aligned(workspace, 256)) return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  int rc = check_device();
+  if (rc != SPEC_OK) return rc;
+  specv::ChainSync hdr;
+  hipError_t e = hipMemcpy(&hdr, workspace, sizeof(hdr), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SPEC_ERR_HIP, "chain error read: %s", hipGetErrorString(e));
+  *error = (int)hdr.error;
+  if (hdr.error) {
+    const unsigned zero = 0;
+    e = hipMemcpy(static_cast<char*>(workspace) + offsetof(specv::ChainSync, error), &zero,
+                  sizeof(zero), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(SPEC_ERR_HIP, "chain error clear: %s", hipGetErrorString(e));
+  }
+  return SPEC_OK;
 }
 
 int spec_softmax(const float* logits, int rows, int V, float* probs, float* row_max,
@@ -218,9 +349,10 @@ int spec_verify(const uint16_t* hidden, const uint16_t* lm_head, int d, float* t
   if (workspace_bytes < need)
     return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   if (!aligned(workspace, 256)) return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  if ((rc = check_device()) != SPEC_OK) return rc;
+  int cus = 0;
+  if ((rc = check_device(&cus)) != SPEC_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (lm_head && (rc = run_gemm(hidden, lm_head, target_logits, false, M, d, V, s)) != SPEC_OK)
+  if (lm_head && (rc = run_gemm(hidden, lm_head, target_logits, false, M, d, V, cus, s)) != SPEC_OK)
     return rc;
   return launched(specv::launch_verify_sampling(target_logits, draft_logits, draft_tokens, u_accept,
                                                 u_sample, B, K, V, out_tokens, n_emitted,

@@ -1,0 +1,582 @@
+// Weight-streaming linears for few verify positions: y = x . w^T with M <= 16
+// rows of x, bf16 in, fp32 accumulation.
+//
+// At M = B*(K+1) of 5 a linear does 5 FLOPs per weight byte, far below the
+// chip's ridge, so the pass is bound by reading w once from HBM ("Speculative
+// Decoding: Guess Several Tokens, Check Them in One Pass", Step 1; "What
+// Actually Happens During Speculative Decoding in LLMs", the 5-candidate
+// pass). The kernel is built around that read:
+//
+//  * Persistent workgroups (a fixed number per CU) walk row blocks of w
+//    round-robin. Each lane group of 16 lanes owns RPL rows of a row block;
+//    one 16-byte non-temporal load per lane covers 256 contiguous bytes of a
+//    row per segment, and the four waves of a workgroup interleave segments
+//    along the reduction dimension.
+//  * The activation tile x[:, chunk] is staged in LDS and stays there across
+//    row blocks; lanes read it back with 16-byte LDS loads.
+//  * Products use v_dot2c_f32_bf16 (two bf16 products per lane-op).
+//  * The stage loop is software-pipelined two stages deep and the pipeline
+//    runs across row-block and linear boundaries, so the weight loads of the
+//    next row block (or the next linear) are in flight while the current
+//    one finishes.
+//  * Partial sums are reduced across the 16 lanes of a group with DPP and
+//    across the 4 waves through LDS in a fixed order: outputs are
+//    deterministic.
+//
+// Chain mode runs a list of linears in order in one launch. Linear l+1 reads
+// its activations only after every workgroup has finished linear l (an
+// arrival counter per linear), as the next layer of a forward pass would;
+// its weight loads, which depend on nothing, are issued before that wait.
+// The per-XCD L2 caches are kept out of the hand-off instead of being
+// flushed: outputs are written and activations read with device-scope (sc1)
+// accesses, and a workgroup bumps the counter only after its own output
+// stores have completed (vmcnt), so no cache write-back or invalidate is
+// issued per barrier. Counters are generation-based, so the workspace never
+// needs clearing between launches; a bounded spin turns a stalled barrier
+// into an error flag instead of a hang.
+
+#include "common.h"
+#include "internal.h"
+
+namespace specv {
+
+#ifndef SPECV_STREAM_DEPTH
+#define SPECV_STREAM_DEPTH 2
+#endif
+constexpr int kStreamThreads = 256;
+constexpr int kSeg = 128;           // reduction elements per lane group per segment
+constexpr int kCachePolicyDevice = 16;  // buffer-load aux bits: sc1 (device scope)
+constexpr int kSpinLimit = 1 << 18;  // well under a second of polling before a barrier gives up
+constexpr int kPollSleep = 4;        // s_sleep units (64 clocks each) between polls
+
+// Pointers taken from a descriptor are generic; naming the global address
+// space lets the compiler emit global (not flat) loads and stores, which
+// count only on vmcnt.
+#define SPECV_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ const SPECV_GLOBAL T* gptr(const void* p) {
+  return (const SPECV_GLOBAL T*)(p);
+}
+template <class T>
+__device__ __forceinline__ SPECV_GLOBAL T* gptr_mut(void* p) {
+  return (SPECV_GLOBAL T*)(p);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float dot8_bf16(u32x4 a, u32x4 b, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.x), as_bf16x2(b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.y), as_bf16x2(b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.z), as_bf16x2(b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.w), as_bf16x2(b.w), acc, false);
+  return acc;
+}
+
+// Per-workgroup schedule of one linear.
+struct LinSched {
+  const uint16_t* x;
+  const uint16_t* w;
+  void* y;
+  int K, N;
+  int n_it;    // pipeline stages per row block (ceil(K / elems per stage))
+  int n_rb;    // row blocks of the linear
+  int my_rb;   // row blocks this workgroup owns (bid, bid + G, ...)
+  int kc;      // activation chunk length (multiple of a stage)
+  int ipc;     // stages per chunk
+  int bf16;
+  int ragged_k;
+};
+
+template <int M, int RPL, int U, int KCMAX>
+struct Stream {
+  static constexpr int NR = 4 * RPL;              // rows per row block
+  static constexpr int EPI = 4 * U * kSeg;         // reduction elements per stage
+  static constexpr int STG = (M * (KCMAX / 8) + kStreamThreads - 1) / kStreamThreads;
+  static constexpr size_t kXBytes = (size_t)M * KCMAX * 2;
+  static constexpr size_t kRedBytes = (size_t)4 * NR * M * 4;
+  static constexpr size_t kLdsBytes = kXBytes + kRedBytes;
+  static_assert(KCMAX % EPI == 0, "chunk must hold whole stages");
+
+  __device__ static LinSched sched(const StreamLinear& d) {
+    LinSched s;
+    s.x = d.x;
+    s.w = d.w;
+    s.y = d.y;
+    s.K = d.K;
+    s.N = d.N;
+    s.bf16 = d.out_bf16;
+    s.n_it = (d.K + EPI - 1) / EPI;
+    s.n_rb = (d.N + NR - 1) / NR;
+    const int bid = blockIdx.x, G = gridDim.x;
+    s.my_rb = s.n_rb > bid ? (s.n_rb - bid + G - 1) / G : 0;
+    const int n_chunks = (s.n_it * EPI + KCMAX - 1) / KCMAX;
+    s.ipc = (s.n_it + n_chunks - 1) / n_chunks;
+    s.kc = s.ipc * EPI;
+    s.ragged_k = (d.K % EPI) != 0;
+    return s;
+  }
+};
+
+// A position in a workgroup's stage sequence: linear l, its j-th row block,
+// stage it.
+struct Cursor {
+  int l, j, it;
+  bool valid;
+};
+
+template <int M, int RPL, int U, int KCMAX>
+__global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinear single,
+                                                                     const StreamLinear* chain,
+                                                                     int n_lin, ChainSync* sync) {
+  using S = Stream<M, RPL, U, KCMAX>;
+  constexpr int NR = S::NR, EPI = S::EPI;
+  extern __shared__ u32x4 lds[];
+  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + S::kXBytes);
+  __shared__ unsigned s_gen;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, sub = lane & 15;
+  const int bid = blockIdx.x, G = gridDim.x;
+  const bool is_chain = chain != nullptr;
+  unsigned* counts = is_chain ? reinterpret_cast<unsigned*>(sync + 1) : nullptr;
+  if (is_chain && (sync->magic != kChainMagic || sync->n != n_lin || sync->M != M)) {
+    if (bid == 0 && tid == 0)
+      __hip_atomic_fetch_or(&sync->error, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;  // every workgroup reads the same header and leaves
+  }
+
+  auto desc = [&](int l) -> StreamLinear {
+    if (!is_chain) return single;
+    const SPECV_GLOBAL StreamLinear* d = gptr<StreamLinear>(chain + l);
+    return StreamLinear{d->x, d->w, d->y, d->K, d->N, d->out_bf16, d->reserved};
+  };
+
+  // ---- barrier between linears (chain mode)
+  unsigned target = 0;
+  if (is_chain) {
+    if (tid == 0) s_gen = __hip_atomic_load(&sync->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    target = (s_gen + 1u) * (unsigned)G;
+  }
+  // Arrival: every wave's device-scope output stores have completed (the
+  // caller waited on vmcnt) before the barrier, so the count only rises once
+  // the linear's outputs are visible at device scope.
+  unsigned long long* trace = is_chain ? sync->trace : nullptr;
+  // Release flags: the last workgroup to arrive at linear l publishes the
+  // count to kReleaseLanes flags on separate 64-byte lines, and waiters poll
+  // the flag of their lane, so polls do not queue on the line the arrivals
+  // update.
+  unsigned* release = is_chain ? counts + chain_release_offset(n_lin) : nullptr;
+  auto flag = [&](int l, int lane_id) { return release + ((size_t)l * kReleaseLanes + lane_id) * 16; };
+  auto arrive = [&](int l) {
+    __syncthreads();
+    if (tid == 0) {
+      if (trace) trace[((size_t)l * G + bid) * 2] = wall_clock64();
+      const unsigned prev =
+          __hip_atomic_fetch_add(&counts[l], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev + 1u == target) {
+        for (int x = 0; x < kReleaseLanes; ++x)
+          __hip_atomic_store(flag(l, x), target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  };
+  auto wait = [&](int l) {
+    if (tid == 0) {
+      int spins = 0;
+      const unsigned* f = flag(l, bid % kReleaseLanes);
+      while ((int)(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - target) < 0) {
+        if (++spins > kSpinLimit) {
+          __hip_atomic_fetch_or(&sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(kPollSleep);
+      }
+      if (trace) trace[((size_t)(l + 1) * G + bid) * 2 + 1] = wall_clock64();
+    }
+    __syncthreads();
+  };
+
+  // ---- cursors: first stage of the first linear this workgroup works on
+  LinSched cs, ps;
+  Cursor c{0, 0, 0, false}, p;
+  auto seek = [&](Cursor& cur, LinSched& s, int l) {
+    // first linear >= l with work for this workgroup
+    for (; l < n_lin; ++l) {
+      s = S::sched(desc(l));
+      if (s.my_rb > 0) {
+        cur = Cursor{l, 0, 0, true};
+        return;
+      }
+    }
+    cur.valid = false;
+    cur.l = n_lin;
+  };
+  auto advance = [&](Cursor& cur, LinSched& s) {
+    if (++cur.it < s.n_it) return;
+    cur.it = 0;
+    if (++cur.j < s.my_rb) return;
+    seek(cur, s, cur.l + 1);
+  };
+
+  // ---- activation staging: x[:, chunk] -> registers -> LDS. Loads of the
+  // next chunk of the same linear are issued one pipeline stage early.
+  u32x4 xs[S::STG];
+  auto load_x = [&](const LinSched& s, int chunk) {
+    const int k0 = chunk * s.kc;
+    const int kc = min(s.kc, s.K - k0);
+    const int units = kc / 8, total = M * units;
+    if (is_chain) {
+      // x may be the previous linear's output: read it at device scope
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(s.x), (short)0, M * s.K * 2, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < S::STG; ++i) {
+        const int u = min(tid + i * kStreamThreads, total - 1);
+        const int m = u / units, cc = u - m * units;
+        xs[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (m * s.K + k0 + cc * 8) * 2, 0,
+                                                         kCachePolicyDevice));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::STG; ++i) {
+        const int u = min(tid + i * kStreamThreads, total - 1);
+        const int m = u / units, cc = u - m * units;
+        xs[i] = *gptr<u32x4>(s.x + (size_t)m * s.K + k0 + cc * 8);
+      }
+    }
+  };
+  auto store_x = [&](const LinSched& s, int chunk) {
+    const int k0 = chunk * s.kc;
+    const int kc = min(s.kc, s.K - k0);
+    const int units = kc / 8, total = M * units, row_units = s.kc / 8;
+#pragma unroll
+    for (int i = 0; i < S::STG; ++i) {
+      const int u = tid + i * kStreamThreads;
+      if (u < total) {
+        const int m = u / units, cc = u - m * units;
+        lds[m * row_units + cc] = xs[i];
+      }
+    }
+  };
+
+  // element offset of this lane's 8 values for segment u of stage it
+  auto kofs = [&](int it, int u) { return ((it * U + u) * 4 + wave) * kSeg + sub * 8; };
+
+  auto load_fast = [&](u32x4 (&buf)[U][RPL], const LinSched& s, const Cursor& cur) {
+    const int rb = bid + cur.j * G;
+    const SPECV_GLOBAL u32x4* base = gptr<u32x4>(s.w + (size_t)(rb * NR + grp * RPL) * s.K);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k8 = kofs(cur.it, u) >> 3;
+#pragma unroll
+      for (int r = 0; r < RPL; ++r)
+        buf[u][r] = __builtin_nontemporal_load(base + (size_t)r * (s.K >> 3) + k8);
+    }
+  };
+  auto load_safe = [&](u32x4 (&buf)[U][RPL], const LinSched& s, const Cursor& cur) {
+    const int rb = bid + cur.j * G;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const int row = rb * NR + grp * RPL + r;
+      const SPECV_GLOBAL u32x4* base = gptr<u32x4>(s.w + (size_t)min(row, s.N - 1) * s.K);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = kofs(cur.it, u);
+        u32x4 v = __builtin_nontemporal_load(base + (min(k, s.K - 8) >> 3));
+        buf[u][r] = (row < s.N && k < s.K) ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto stage_is_safe = [&](const LinSched& s, const Cursor& cur) {
+    return (s.ragged_k && cur.it == s.n_it - 1) ||
+           ((bid + cur.j * G + 1) * NR > s.N);
+  };
+  auto load = [&](u32x4 (&buf)[U][RPL], const LinSched& s, const Cursor& cur) {
+    if (stage_is_safe(s, cur))
+      load_safe(buf, s, cur);
+    else
+      load_fast(buf, s, cur);
+  };
+
+  float acc[RPL][M];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+  };
+  auto compute = [&](const u32x4 (&buf)[U][RPL], const LinSched& s, const Cursor& cur) {
+    const int chunk_base = (cur.it / s.ipc) * s.kc;
+    const int row_units = s.kc / 8;
+    if (s.ragged_k && cur.it == s.n_it - 1) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = kofs(cur.it, u);
+        const bool ok = k < s.K;
+        const int lu = ok ? (k - chunk_base) >> 3 : 0;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          u32x4 xv = lds[m * row_units + lu];
+          xv = ok ? xv : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int r = 0; r < RPL; ++r) acc[r][m] = dot8_bf16(buf[u][r], xv, acc[r][m]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int lu = (kofs(cur.it, u) - chunk_base) >> 3;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const u32x4 xv = lds[m * row_units + lu];
+#pragma unroll
+          for (int r = 0; r < RPL; ++r) acc[r][m] = dot8_bf16(buf[u][r], xv, acc[r][m]);
+        }
+      }
+    }
+  };
+  auto finish = [&](const LinSched& s, const Cursor& cur) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[r][m] = row16_sum(acc[r][m]);
+    if (sub == 0) {
+#pragma unroll
+      for (int r = 0; r < RPL; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) red[(wave * NR + grp * RPL + r) * M + m] = acc[r][m];
+    }
+    __syncthreads();
+    const int rb = bid + cur.j * G;
+    for (int i = tid; i < NR * M; i += kStreamThreads) {
+      const int m = i / NR, rr = i - m * NR;
+      const int row = rb * NR + rr;
+      if (row < s.N) {
+        const float v = ((red[(0 * NR + rr) * M + m] + red[(1 * NR + rr) * M + m]) +
+                         red[(2 * NR + rr) * M + m]) +
+                        red[(3 * NR + rr) * M + m];
+        const size_t o = (size_t)m * s.N + row;
+        if (is_chain) {  // visible at device scope without a cache write-back
+          if (s.bf16)
+            __hip_atomic_store(gptr_mut<uint16_t>(s.y) + o, f32_to_bf16_bits(v),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            __hip_atomic_store(gptr_mut<float>(s.y) + o, v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        } else if (s.bf16) {
+          gptr_mut<uint16_t>(s.y)[o] = f32_to_bf16_bits(v);
+        } else {
+          gptr_mut<float>(s.y)[o] = v;
+        }
+      }
+    }
+    __syncthreads();
+    zero_acc();
+  };
+
+  // Arrive at the counters of linears [from, to) in which this workgroup
+  // has no row block (nothing to wait for, nothing to compute).
+  auto arrive_empty = [&](int from, int to) {
+    if (!is_chain) return;
+    for (int l = from; l < to; ++l) arrive(l);
+  };
+
+  // One pipeline step on buffer buf: compute stage c, refill buf with stage
+  // p, close the row block / linear if c was its last stage, advance c.
+  auto step = [&](u32x4 (&buf)[U][RPL]) {
+    if (c.it == 0 && c.j == 0) {
+      // first stage of a linear: its x may depend on the previous linear
+      if (is_chain && c.l > 0) wait(c.l - 1);
+      load_x(cs, 0);
+      store_x(cs, 0);
+      __syncthreads();
+    } else if (c.it % cs.ipc == 0 && cs.ipc < cs.n_it) {
+      // next activation chunk (chunk 0 again for a new row block); its loads
+      // were issued during the previous stage
+      __syncthreads();
+      store_x(cs, c.it / cs.ipc);
+      __syncthreads();
+    }
+    compute(buf, cs, c);
+    const bool closes_rb = c.it == cs.n_it - 1;
+    if (closes_rb) finish(cs, c);  // output stores precede the refill load
+    // The next stage of this linear opens a new activation chunk: issue its
+    // loads now, ahead of the weight refill, so that consuming them next
+    // stage (vmcnt completes in order) leaves the refill in flight.
+    if (cs.ipc < cs.n_it) {
+      const bool same_rb = !closes_rb;
+      const bool next_rb = closes_rb && c.j + 1 < cs.my_rb;
+      const int nit = closes_rb ? 0 : c.it + 1;
+      if ((same_rb || next_rb) && nit % cs.ipc == 0) load_x(cs, nit / cs.ipc);
+    }
+    const bool refilled = p.valid;
+    if (refilled) {
+      load(buf, ps, p);
+      advance(p, ps);
+    }
+    if (closes_rb && c.j == cs.my_rb - 1 && is_chain) {
+      // complete this wave's output stores (and older loads), keeping the
+      // refill just issued in flight
+      if (refilled)
+        wait_vmcnt<U * RPL>();  // only this step's refill may stay in flight
+      else
+        wait_vmcnt<0>();
+      arrive(c.l);
+    }
+    const int l_before = c.l;
+    advance(c, cs);
+    arrive_empty(l_before + 1, c.valid ? c.l : n_lin);
+  };
+
+  zero_acc();
+  seek(c, cs, 0);
+  arrive_empty(0, c.valid ? c.l : n_lin);
+  p = c;
+  ps = cs;
+  // DEPTH register stages of weights are in flight ahead of the compute.
+  u32x4 wa[U][RPL], wb[U][RPL];
+#if SPECV_STREAM_DEPTH >= 3
+  u32x4 wc[U][RPL];
+#endif
+  if (p.valid) {
+    load(wa, ps, p);
+    advance(p, ps);
+  }
+  if (p.valid) {
+    load(wb, ps, p);
+    advance(p, ps);
+  }
+#if SPECV_STREAM_DEPTH >= 3
+  if (p.valid) {
+    load(wc, ps, p);
+    advance(p, ps);
+  }
+#endif
+  while (c.valid) {
+    step(wa);
+    if (!c.valid) break;
+    step(wb);
+#if SPECV_STREAM_DEPTH >= 3
+    if (!c.valid) break;
+    step(wc);
+#endif
+  }
+
+  // exit: the last workgroup out advances the generation
+  if (is_chain) {
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned prev =
+          __hip_atomic_fetch_add(&sync->exit_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev + 1u == target)
+        __hip_atomic_fetch_add(&sync->gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launch: per-M tile choice and the persistent grid
+// ---------------------------------------------------------------------------
+
+template <int M, int RPL, int U, int KCMAX>
+static hipError_t launch_m(const StreamLinear& single, const StreamLinear* chain, int n_lin,
+                           ChainSync* sync, int grid, hipStream_t s) {
+  using S = Stream<M, RPL, U, KCMAX>;
+  hipLaunchKernelGGL((gemm_stream_kernel<M, RPL, U, KCMAX>), dim3(grid), dim3(kStreamThreads),
+                     S::kLdsBytes, s, single, chain, n_lin, sync);
+  return hipGetLastError();
+}
+
+// Tile parameters per M: (RPL, U, KCMAX). Rows per row block = 4 * RPL;
+// activation chunk KCMAX elements (M * KCMAX * 2 bytes of LDS).
+#ifndef SPECV_T5
+#define SPECV_T5(X) X(5, 2, 4, 4096)
+#endif
+#define SPECV_STREAM_TABLE(X) \
+  X(1, 4, 2, 8192)            \
+  X(2, 4, 2, 8192)            \
+  X(3, 4, 2, 4096)            \
+  X(4, 4, 2, 4096)            \
+  SPECV_T5(X)                 \
+  X(6, 4, 2, 4096)            \
+  X(7, 4, 2, 2048)            \
+  X(8, 4, 2, 2048)            \
+  X(9, 2, 2, 2048)            \
+  X(10, 2, 2, 2048)           \
+  X(11, 2, 2, 2048)           \
+  X(12, 2, 2, 2048)           \
+  X(13, 2, 2, 1024)           \
+  X(14, 2, 2, 1024)           \
+  X(15, 2, 2, 1024)           \
+  X(16, 2, 2, 1024)
+
+size_t stream_rows_per_block(int M) {
+  switch (M) {
+#define SPECV_NR(MM, RPL, U, KC) \
+  case MM:                       \
+    return 4 * RPL;
+    SPECV_STREAM_TABLE(SPECV_NR)
+#undef SPECV_NR
+    default:
+      return 0;
+  }
+}
+
+template <int M, int RPL, int U, int KCMAX>
+static int max_wgs_m() {
+  using S = Stream<M, RPL, U, KCMAX>;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_stream_kernel<M, RPL, U, KCMAX>,
+                                                   kStreamThreads, S::kLdsBytes) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
+}
+
+int stream_max_wgs_per_cu(int M) {
+  switch (M) {
+#define SPECV_OCC(MM, RPL, U, KC) \
+  case MM:                        \
+    return max_wgs_m<MM, RPL, U, KC>();
+    SPECV_STREAM_TABLE(SPECV_OCC)
+#undef SPECV_OCC
+    default:
+      return 1;
+  }
+}
+
+hipError_t launch_gemm_stream_any(const StreamLinear& single, const StreamLinear* chain, int n_lin,
+                                  ChainSync* sync, int M, int grid, hipStream_t s) {
+  switch (M) {
+#define SPECV_CASE(MM, RPL, U, KC) \
+  case MM:                         \
+    return launch_m<MM, RPL, U, KC>(single, chain, n_lin, sync, grid, s);
+    SPECV_STREAM_TABLE(SPECV_CASE)
+#undef SPECV_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm_stream(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
+                              int K, int N, int grid, hipStream_t s) {
+  StreamLinear d{x, w, y, K, N, out_bf16 ? 1 : 0, 0};
+  const int n_rb = (N + (int)stream_rows_per_block(M) - 1) / (int)stream_rows_per_block(M);
+  if (grid > n_rb) grid = n_rb;
+  return launch_gemm_stream_any(d, nullptr, 1, nullptr, M, grid, s);
+}
+
+hipError_t launch_gemm_chain(const StreamLinear* chain, int n_lin, ChainSync* sync, int M, int grid,
+                             hipStream_t s) {
+  StreamLinear none{nullptr, nullptr, nullptr, 0, 0, 0, 0};
+  return launch_gemm_stream_any(none, chain, n_lin, sync, M, grid, s);
+}
+
+}  // namespace specv

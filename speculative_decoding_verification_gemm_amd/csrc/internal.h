@@ -13,8 +13,51 @@ namespace specv {
 // kernel; larger M uses the MFMA kernel.
 constexpr int kMaxStreamM = 16;
 
+// One linear of a streaming launch; layout identical to spec_linear of the
+// public header (x, w, y, d_in, d_out, y_dtype, reserved).
+struct StreamLinear {
+  const uint16_t* x;
+  const uint16_t* w;
+  void* y;
+  int K;         // d_in
+  int N;         // d_out
+  int out_bf16;  // SPEC_BF16 (1) or SPEC_F32 (0)
+  int reserved;
+};
+static_assert(sizeof(StreamLinear) == 40, "descriptor layout");
+
+// Header of a chain workspace; followed by `n` per-linear arrival counters
+// (unsigned) and then the n descriptors (StreamLinear, 64-byte aligned).
+struct ChainSync {
+  unsigned gen;         // launches completed
+  unsigned exit_count;  // workgroups that left, cumulative
+  unsigned error;       // bit 0: a barrier wait gave up; bit 1: plan mismatch
+  unsigned magic;
+  int n;                // linears in the plan
+  int M;                // rows of every x
+  int reserved[2];
+  unsigned long long* trace;  // optional per-linear timestamps (nullptr: off)
+  int pad[6];           // header is one 64-byte line
+};
+static_assert(sizeof(ChainSync) == 64, "chain header is one cache line");
+constexpr unsigned kChainMagic = 0x53504348u;  // "SPCH"
+// Chain workspace after the header: n arrival counters, then (64-byte
+// aligned) n x kReleaseLanes release flags, one 64-byte line each, then the
+// descriptors.
+constexpr int kReleaseLanes = 8;
+__host__ __device__ inline size_t chain_release_offset(int n) {  // in unsigned words from counts
+  return (((size_t)n * 4 + 63) & ~(size_t)63) / 4;
+}
+__host__ __device__ inline size_t chain_counts_bytes(int n) {
+  return chain_release_offset(n) * 4 + (size_t)n * kReleaseLanes * 64;
+}
+
+size_t stream_rows_per_block(int M);
+int stream_max_wgs_per_cu(int M);
 hipError_t launch_gemm_stream(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
-                              int K, int N, hipStream_t s);
+                              int K, int N, int grid, hipStream_t s);
+hipError_t launch_gemm_chain(const StreamLinear* chain, int n_lin, ChainSync* sync, int M, int grid,
+                             hipStream_t s);
 hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
                             int K, int N, hipStream_t s);
 

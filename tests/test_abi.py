@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 13
     for n in names:
         assert hasattr(sv.lib, n), n
 
@@ -118,3 +118,30 @@ def test_verify_rejects(sv):
     assert _verify(sv, B=1 << 20, K=64, V=1 << 20) == -1     # grid bound
     assert _verify(sv, wsb=100) == -4
     assert _verify(sv, ws=A + 16) == -4
+
+
+def test_chain_rejects(sv):
+    L = sv.SpecLinear
+    good = (L * 2)(L(A, A, A, 4096, 4096, 1, 0), L(A, A, A, 4096, 128, 0, 0))
+    nb = sv.lib.spec_chain_workspace_bytes(2)
+    assert nb > 0 and nb % 256 == 0 and sv.lib.spec_chain_workspace_bytes(0) == 0
+    assert sv.lib.spec_chain_workspace_bytes(4097) == 0
+    f = sv.lib.spec_chain_prepare
+    assert f(None, 2, 5, A, nb) == -1
+    assert f(good, 2, 5, None, nb) == -1
+    assert f(good, 0, 5, A, nb) == -1
+    assert f(good, 2, 17, A, nb) == -1            # beyond the streaming regime
+    assert f(good, 2, 0, A, nb) == -1
+    assert f(good, 2, 5, A, nb - 1) == -4
+    assert f(good, 2, 5, A + 64, nb) == -4
+    for bad, code in [(L(A, A, A, 4100, 8, 1, 0), -1), (L(A, A, A, 8, 8, 3, 0), -1),
+                      (L(A, A, A, 8, 8, 1, 1), -1), (L(A + 8, A, A, 8, 8, 1, 0), -2),
+                      (L(A, A, None, 8, 8, 1, 0), -1)]:
+        arr = (L * 2)(good[0], bad)
+        assert f(arr, 2, 5, A, nb) == code
+        assert b"linear 1" in sv.lib.spec_last_error()
+    g = sv.lib.spec_verify_gemm_chain
+    assert g(0, 5, A, None) == -1 and g(2, 17, A, None) == -1 and g(2, 5, None, None) == -1
+    assert g(2, 5, A + 8, None) == -4
+    import ctypes
+    assert sv.lib.spec_chain_error(None, ctypes.byref(ctypes.c_int())) == -1

@@ -1,0 +1,136 @@
+"""GPU tests of spec_verify_gemm_chain: the stack of linears in one launch.
+
+Each linear of a chain must equal what spec_verify_gemm computes for it
+(bitwise: same kernel arithmetic) and the fp64 oracle within the GEMM
+tolerance. A chain whose linear i+1 reads linear i's output checks that the
+device-side barrier orders the layers.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def rel_err(y, ref):
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    return float(np.max(np.abs(y - ref) / np.maximum(np.abs(ref), rms)))
+
+
+def make_linears(dev, M, shapes, seed, chained=False):
+    import torch
+    from synth import device as sd
+    out, x = [], None
+    for i, (d_in, d_out, dt) in enumerate(shapes):
+        if x is None or not chained:
+            x = sd.normal_bf16((M, d_in), 1.0, seed + 2 * i, dev)
+        # chained layers keep activations O(1): w ~ N(0, 1/d_in)
+        std = (1.0 / d_in) ** 0.5 if chained else synth.WEIGHT_STD
+        w = sd.normal_bf16((d_out, d_in), std, seed + 2 * i + 1, dev)
+        y = torch.empty((M, d_out), dtype=dt, device=dev)
+        out.append((x, w, y))
+        x = y
+    return out
+
+
+@pytest.mark.parametrize("M", [1, 5, 8, 16])
+def test_chain_matches_single_launches(sv, dev, M):
+    import torch
+    shapes = [(1032, 777, torch.bfloat16), (4096, 6144, torch.bfloat16), (8192, 256, torch.float32),
+              (14336, 4096, torch.bfloat16), (264, 3000, torch.float32)]
+    lin = make_linears(dev, M, shapes, 100 + M)
+    ch = sv.Chain(lin, dev)
+    ch.run()
+    torch.cuda.synchronize()
+    assert ch.error() == 0
+    for x, w, y in lin:
+        ref = sv.verify_gemm(x, w, out_dtype=y.dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(ref, y)
+
+
+def test_chain_of_dependent_layers(sv, dev):
+    """y_i feeds x_{i+1}: the oracle recomputes each layer from the GPU's own
+    bf16 input of that layer (its x), and the final check recomputes layer
+    i+1 from layer i's GPU output, which only passes if the barrier made the
+    whole of y_i visible before x_{i+1} was read."""
+    import torch
+    from synth import device as sd
+    M = 5
+    dims = [4096, 6144, 4096, 14336, 4096, 4096, 1000]
+    shapes = [(dims[i], dims[i + 1], torch.bfloat16) for i in range(len(dims) - 1)]
+    lin = make_linears(dev, M, shapes, 7, chained=True)
+    ch = sv.Chain(lin, dev)
+    for _ in range(3):  # repeated launches reuse the counters (generations)
+        for _, _, y in lin:
+            y.zero_()
+        ch.run()
+        torch.cuda.synchronize()
+        assert ch.error() == 0
+        for i, (x, w, y) in enumerate(lin):
+            ref = oracle.linear(sd.to_bits(x), sd.to_bits(w))
+            e = rel_err(y.float().cpu().numpy().astype(np.float64), ref)
+            assert e <= 2e-2, (i, e)
+            if i > 0:
+                assert x.data_ptr() == lin[i - 1][2].data_ptr()
+
+
+def test_chain_oracle_llama_layer(sv, dev):
+    import torch
+    from synth import device as sd
+    M = 5
+    shapes = [(4096, 6144, torch.bfloat16), (4096, 4096, torch.bfloat16),
+              (4096, 28672, torch.bfloat16), (14336, 4096, torch.bfloat16),
+              (4096, 128256, torch.float32)]
+    lin = make_linears(dev, M, shapes, 55)
+    ch = sv.Chain(lin, dev)
+    ch.run()
+    torch.cuda.synchronize()
+    assert ch.error() == 0
+    rng = np.random.default_rng(0)
+    for x, w, y in lin:
+        cols = np.unique(np.concatenate([np.arange(4), np.arange(w.shape[0] - 4, w.shape[0]),
+                                         rng.integers(0, w.shape[0], 64)]))
+        idx = torch.from_numpy(cols).to(dev)
+        ref = oracle.linear(sd.to_bits(x), sd.to_bits(w.index_select(0, idx)))
+        got = y.index_select(1, idx).float().cpu().numpy().astype(np.float64)
+        assert rel_err(got, ref) <= 2e-2
+
+
+def test_chain_plan_mismatch_is_reported(sv, dev):
+    import torch
+    lin = make_linears(dev, 5, [(512, 256, torch.float32), (256, 128, torch.float32)], 3)
+    ch = sv.Chain(lin, dev)
+    for _, _, y in lin:
+        y.fill_(7.0)
+    sv.check(sv.lib.spec_verify_gemm_chain(2, 4, sv._ptr(ch.workspace), sv._stream()))
+    torch.cuda.synchronize()
+    assert ch.error() == 2
+    assert all(bool((y == 7.0).all()) for _, _, y in lin)  # nothing computed
+    ch.run()
+    torch.cuda.synchronize()
+    assert ch.error() == 0
+
+
+def test_chain_graph_replay(sv, dev):
+    import torch
+    shapes = [(4096, 4096, torch.bfloat16), (4096, 6144, torch.bfloat16)]
+    lin = make_linears(dev, 5, shapes, 9)
+    ch = sv.Chain(lin, dev)
+    ch.run()
+    torch.cuda.synchronize()
+    want = [y.clone() for _, _, y in lin]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ch.run()
+    for _ in range(3):
+        for _, _, y in lin:
+            y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, y) for a, (_, _, y) in zip(want, lin))
+    assert ch.error() == 0
