@@ -203,9 +203,11 @@ int spec_chain_prepare(const spec_linear* linears, int n, int M, void* workspace
   hdr.magic = specv::kChainMagic;
   hdr.n = n;
   hdr.M = M;
-  // Diagnostics: SPECV_CHAIN_TRACE=<device address of n * grid * 2 uint64>
-  // records, per linear and workgroup, the wall clock at arrival and at the
-  // end of the wait (100 MHz ticks).
+  // Diagnostics: SPECV_CHAIN_TRACE=<device address of n * grid * 4 uint64>
+  // records, per linear and workgroup, the wall clock (100 MHz ticks) at
+  // arrival, at the end of the wait for the previous linear, and when the
+  // first activation chunk is staged, and when the last output stores of
+  // the linear have been issued.
   if (const char* env = getenv("SPECV_CHAIN_TRACE")) {
     unsigned long long v = strtoull(env, nullptr, 0);
     hdr.trace = reinterpret_cast<unsigned long long*>(v);

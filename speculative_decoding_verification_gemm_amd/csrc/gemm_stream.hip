@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
   auto arrive = [&](int l) {
     __syncthreads();
     if (tid == 0) {
-      if (trace) trace[((size_t)l * G + bid) * 2] = wall_clock64();
+      if (trace) trace[((size_t)l * G + bid) * 4] = wall_clock64();
       const unsigned prev =
           __hip_atomic_fetch_add(&counts[l], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (prev + 1u == target) {
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
         }
         __builtin_amdgcn_s_sleep(kPollSleep);
       }
-      if (trace) trace[((size_t)(l + 1) * G + bid) * 2 + 1] = wall_clock64();
+      if (trace) trace[((size_t)(l + 1) * G + bid) * 4 + 1] = wall_clock64();
     }
     __syncthreads();
   };
@@ -398,6 +398,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
       load_x(cs, 0);
       store_x(cs, 0);
       __syncthreads();
+      if (trace && tid == 0) trace[((size_t)c.l * G + bid) * 4 + 2] = wall_clock64();
     } else if (c.it % cs.ipc == 0 && cs.ipc < cs.n_it) {
       // next activation chunk (chunk 0 again for a new row block); its loads
       // were issued during the previous stage
@@ -423,6 +424,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
       advance(p, ps);
     }
     if (closes_rb && c.j == cs.my_rb - 1 && is_chain) {
+      if (trace && tid == 0) trace[((size_t)c.l * G + bid) * 4 + 3] = wall_clock64();
       // complete this wave's output stores (and older loads), keeping the
       // refill just issued in flight
       if (refilled)
