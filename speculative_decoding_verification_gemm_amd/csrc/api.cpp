@@ -121,7 +121,8 @@ int run_gemm(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M
   if (M <= specv::kMaxStreamM)
     e = specv::launch_gemm_stream(x, w, y, out_bf16, M, d_in, d_out, cus * stream_wgs_per_cu(M), s);
   else
-    e = specv::launch_gemm_mfma(x, w, y, out_bf16, M, d_in, d_out, s);
+    e = M <= specv::kMaxSkinnyM ? specv::launch_gemm_skinny(x, w, y, out_bf16, M, d_in, d_out, s)
+                                : specv::launch_gemm_mfma(x, w, y, out_bf16, M, d_in, d_out, s);
   return launched(e, "spec_verify_gemm");
 }
 

@@ -7,22 +7,26 @@
 // Actually Happens During Speculative Decoding in LLMs", the 5-candidate
 // pass). The kernel is built around that read:
 //
-//  * Persistent workgroups (a fixed number per CU) walk row blocks of w
-//    round-robin. Each lane group of 16 lanes owns RPL rows of a row block;
-//    one 16-byte non-temporal load per lane covers 256 contiguous bytes of a
-//    row per segment, and the four waves of a workgroup interleave segments
-//    along the reduction dimension.
+//  * One persistent workgroup of eight waves per CU walks row blocks of w
+//    round-robin. (A second co-resident workgroup measurably received less
+//    bandwidth than the first; with one, every CU streams alike.) Each lane
+//    group of 16 lanes owns RPL rows of a row block; one 16-byte
+//    non-temporal load per lane covers 256 contiguous bytes of a row per
+//    segment, and the eight waves interleave segments along the reduction
+//    dimension.
 //  * The activation tile x[:, chunk] is staged in LDS and stays there across
-//    row blocks; lanes read it back with 16-byte LDS loads.
+//    row blocks; lanes read it back with 16-byte LDS loads. Chunks are as
+//    large as LDS allows, so most linears stage their activations once.
 //  * Products use v_dot2c_f32_bf16 (two bf16 products per lane-op).
-//  * The stage loop is software-pipelined two stages deep and the pipeline
-//    runs across row-block and linear boundaries, so the weight loads of the
-//    next row block (or the next linear) are in flight while the current
-//    one finishes.
+//  * DEPTH register stages of weights are in flight ahead of the compute,
+//    across row-block and linear boundaries, so the next linear's weights
+//    stream while the current one finishes. Weight loads are issued on every
+//    path (clamped addresses, no selects on loaded values), which keeps the
+//    compiler's vmcnt waits exact.
 //  * Partial sums are reduced across the 16 lanes of a group with DPP and
-//    across the 4 waves through LDS in a fixed order: outputs are
+//    across the waves through LDS in a fixed order: outputs are
 //    deterministic.
-//
+
 // Chain mode runs a list of linears in order in one launch. Linear l+1 reads
 // its activations only after every workgroup has finished linear l (an
 // arrival counter per linear), as the next layer of a forward pass would;
@@ -35,15 +39,18 @@
 // needs clearing between launches; a bounded spin turns a stalled barrier
 // into an error flag instead of a hang.
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
 namespace specv {
 
-#ifndef SPECV_STREAM_DEPTH
-#define SPECV_STREAM_DEPTH 2
+#ifndef SPECV_STREAM_WAVES
+#define SPECV_STREAM_WAVES 8
 #endif
-constexpr int kStreamThreads = 256;
+constexpr int kStreamWaves = SPECV_STREAM_WAVES;  // one workgroup per CU
+constexpr int kStreamThreads = kStreamWaves * kWave;
 constexpr int kSeg = 128;           // reduction elements per lane group per segment
 constexpr int kCachePolicyDevice = 16;  // buffer-load aux bits: sc1 (device scope)
 constexpr int kSpinLimit = 1 << 18;  // well under a second of polling before a barrier gives up
@@ -72,6 +79,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
+// A pointer every lane holds the same value of, made visibly uniform (a
+// buffer resource built from it then lives in scalar registers).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo);
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0..N-1, unrolled.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 __device__ __forceinline__ float dot8_bf16(u32x4 a, u32x4 b, float acc) {
   acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.x), as_bf16x2(b.x), acc, false);
   acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.y), as_bf16x2(b.y), acc, false);
@@ -98,12 +123,14 @@ struct LinSched {
 template <int M, int RPL, int U, int KCMAX>
 struct Stream {
   static constexpr int NR = 4 * RPL;              // rows per row block
-  static constexpr int EPI = 4 * U * kSeg;         // reduction elements per stage
-  static constexpr int STG = (M * (KCMAX / 8) + kStreamThreads - 1) / kStreamThreads;
-  static constexpr size_t kXBytes = (size_t)M * KCMAX * 2;
-  static constexpr size_t kRedBytes = (size_t)4 * NR * M * 4;
+  static constexpr int EPI = kStreamWaves * U * kSeg;  // reduction elements per stage
+  // Activation region rounded up to whole 1 KB blocks: staging writes one
+  // 1 KB block (64 lanes x 16 bytes) per wave instruction.
+  static constexpr size_t kXBytes = ((size_t)M * KCMAX * 2 + 1023) / 1024 * 1024;
+  static constexpr size_t kRedBytes = (size_t)kStreamWaves * NR * M * 4;
   static constexpr size_t kLdsBytes = kXBytes + kRedBytes;
   static_assert(KCMAX % EPI == 0, "chunk must hold whole stages");
+  static_assert(EPI % 512 == 0, "a chunk row must be whole 64-lane staging blocks");
 
   __device__ static LinSched sched(const StreamLinear& d) {
     LinSched s;
@@ -132,7 +159,7 @@ struct Cursor {
   bool valid;
 };
 
-template <int M, int RPL, int U, int KCMAX>
+template <int M, int RPL, int U, int KCMAX, int DEPTH>
 __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinear single,
                                                                      const StreamLinear* chain,
                                                                      int n_lin, ChainSync* sync) {
@@ -152,9 +179,13 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
     return;  // every workgroup reads the same header and leaves
   }
 
-  auto desc = [&](int l) -> StreamLinear {
+  // Descriptors are read-only while the kernel runs: read them through the
+  // constant address space (scalar loads, counted on lgkmcnt), so that
+  // moving to the next linear never waits on the weight loads in flight.
+  auto desc = [&](int l) __attribute__((always_inline)) -> StreamLinear {
     if (!is_chain) return single;
-    const SPECV_GLOBAL StreamLinear* d = gptr<StreamLinear>(chain + l);
+    const __attribute__((address_space(4))) StreamLinear* d =
+        (const __attribute__((address_space(4))) StreamLinear*)(chain + l);
     return StreamLinear{d->x, d->w, d->y, d->K, d->N, d->out_bf16, d->reserved};
   };
 
@@ -174,8 +205,8 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
   // the flag of their lane, so polls do not queue on the line the arrivals
   // update.
   unsigned* release = is_chain ? counts + chain_release_offset(n_lin) : nullptr;
-  auto flag = [&](int l, int lane_id) { return release + ((size_t)l * kReleaseLanes + lane_id) * 16; };
-  auto arrive = [&](int l) {
+  auto flag = [&](int l, int lane_id) __attribute__((always_inline)) { return release + ((size_t)l * kReleaseLanes + lane_id) * 16; };
+  auto arrive = [&](int l) __attribute__((always_inline)) {
     __syncthreads();
     if (tid == 0) {
       if (trace) trace[((size_t)l * G + bid) * 4] = wall_clock64();
@@ -187,7 +218,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
       }
     }
   };
-  auto wait = [&](int l) {
+  auto wait = [&](int l) __attribute__((always_inline)) {
     if (tid == 0) {
       int spins = 0;
       const unsigned* f = flag(l, bid % kReleaseLanes);
@@ -206,7 +237,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
   // ---- cursors: first stage of the first linear this workgroup works on
   LinSched cs, ps;
   Cursor c{0, 0, 0, false}, p;
-  auto seek = [&](Cursor& cur, LinSched& s, int l) {
+  auto seek = [&](Cursor& cur, LinSched& s, int l) __attribute__((always_inline)) {
     // first linear >= l with work for this workgroup
     for (; l < n_lin; ++l) {
       s = S::sched(desc(l));
@@ -218,102 +249,73 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
     cur.valid = false;
     cur.l = n_lin;
   };
-  auto advance = [&](Cursor& cur, LinSched& s) {
+  auto advance = [&](Cursor& cur, LinSched& s) __attribute__((always_inline)) {
     if (++cur.it < s.n_it) return;
     cur.it = 0;
     if (++cur.j < s.my_rb) return;
     seek(cur, s, cur.l + 1);
   };
 
-  // ---- activation staging: x[:, chunk] -> registers -> LDS. Loads of the
-  // next chunk of the same linear are issued one pipeline stage early.
-  u32x4 xs[S::STG];
-  auto load_x = [&](const LinSched& s, int chunk) {
+  // ---- activation staging: x[:, chunk] straight into LDS (global_load_lds,
+  // one 1 KB block per wave instruction, no registers). LDS row m of the
+  // chunk holds s.kc / 8 16-byte units, a whole number of blocks; units past
+  // the end of x load a clamped valid address and are never read. The
+  // staging is complete (vmcnt) and visible to all waves (barrier) on
+  // return.
+  auto stage_x = [&](const LinSched& s, int chunk) __attribute__((always_inline)) {
     const int k0 = chunk * s.kc;
-    const int kc = min(s.kc, s.K - k0);
-    const int units = kc / 8, total = M * units;
-    if (is_chain) {
-      // x may be the previous linear's output: read it at device scope
-      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(s.x), (short)0, M * s.K * 2, 0x00020000);
-#pragma unroll
-      for (int i = 0; i < S::STG; ++i) {
-        const int u = min(tid + i * kStreamThreads, total - 1);
-        const int m = u / units, cc = u - m * units;
-        xs[i] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (m * s.K + k0 + cc * 8) * 2, 0,
-                                                         kCachePolicyDevice));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < S::STG; ++i) {
-        const int u = min(tid + i * kStreamThreads, total - 1);
-        const int m = u / units, cc = u - m * units;
-        xs[i] = *gptr<u32x4>(s.x + (size_t)m * s.K + k0 + cc * 8);
+    const int units = min(s.kc, s.K - k0) / 8;  // valid units per row
+    const int blocks = s.kc / 512;              // 64-unit blocks per LDS row
+    const uint16_t* xs = s.x;
+    for (int m = 0; m < M; ++m) {
+      for (int b = wave; b < blocks; b += kStreamWaves) {
+        const int cc = min(b * 64 + lane, units - 1);
+        const SPECV_GLOBAL void* src = gptr<void>(xs + (size_t)m * s.K + k0 + cc * 8);
+        __attribute__((address_space(3))) void* dst =
+            (__attribute__((address_space(3))) void*)(lds + (m * blocks + b) * 64);
+        if (is_chain)  // x may be the previous linear's output: device scope
+          __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kCachePolicyDevice);
+        else
+          __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
       }
     }
-  };
-  auto store_x = [&](const LinSched& s, int chunk) {
-    const int k0 = chunk * s.kc;
-    const int kc = min(s.kc, s.K - k0);
-    const int units = kc / 8, total = M * units, row_units = s.kc / 8;
-#pragma unroll
-    for (int i = 0; i < S::STG; ++i) {
-      const int u = tid + i * kStreamThreads;
-      if (u < total) {
-        const int m = u / units, cc = u - m * units;
-        lds[m * row_units + cc] = xs[i];
-      }
-    }
+    wait_vmcnt<0>();
+    __syncthreads();
   };
 
   // element offset of this lane's 8 values for segment u of stage it
-  auto kofs = [&](int it, int u) { return ((it * U + u) * 4 + wave) * kSeg + sub * 8; };
+  auto kofs = [&](int it, int u) __attribute__((always_inline)) { return ((it * U + u) * kStreamWaves + wave) * kSeg + sub * 8; };
 
-  auto load_fast = [&](u32x4 (&buf)[U][RPL], const LinSched& s, const Cursor& cur) {
-    const int rb = bid + cur.j * G;
-    const SPECV_GLOBAL u32x4* base = gptr<u32x4>(s.w + (size_t)(rb * NR + grp * RPL) * s.K);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k8 = kofs(cur.it, u) >> 3;
-#pragma unroll
-      for (int r = 0; r < RPL; ++r)
-        buf[u][r] = __builtin_nontemporal_load(base + (size_t)r * (s.K >> 3) + k8);
-    }
-  };
-  auto load_safe = [&](u32x4 (&buf)[U][RPL], const LinSched& s, const Cursor& cur) {
+  // Weight loads are branch-free: rows past N and reduction elements past K
+  // read a clamped valid address. Rows past N feed outputs that are never
+  // stored, and the compute zeroes the activation for elements past K, so
+  // no loaded value needs a select (a select right after a load would make
+  // the wave wait for it). An exhausted cursor also loads a valid clamped
+  // address; its values are never used. Issuing the same loads on every
+  // path keeps the compiler's vmcnt waits exact, so DEPTH stages really are
+  // in flight.
+  auto load = [&](u32x4 (&buf)[U][RPL], const LinSched& s, const Cursor& cur)
+      __attribute__((always_inline)) {
     const int rb = bid + cur.j * G;
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
-      const int row = rb * NR + grp * RPL + r;
-      const SPECV_GLOBAL u32x4* base = gptr<u32x4>(s.w + (size_t)min(row, s.N - 1) * s.K);
+      const int row = min(rb * NR + grp * RPL + r, s.N - 1);
+      const SPECV_GLOBAL u32x4* base = gptr<u32x4>(s.w + (size_t)row * s.K);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = kofs(cur.it, u);
-        u32x4 v = __builtin_nontemporal_load(base + (min(k, s.K - 8) >> 3));
-        buf[u][r] = (row < s.N && k < s.K) ? v : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int u = 0; u < U; ++u)
+        buf[u][r] = __builtin_nontemporal_load(base + (min(kofs(cur.it, u), s.K - 8) >> 3));
     }
-  };
-  auto stage_is_safe = [&](const LinSched& s, const Cursor& cur) {
-    return (s.ragged_k && cur.it == s.n_it - 1) ||
-           ((bid + cur.j * G + 1) * NR > s.N);
-  };
-  auto load = [&](u32x4 (&buf)[U][RPL], const LinSched& s, const Cursor& cur) {
-    if (stage_is_safe(s, cur))
-      load_safe(buf, s, cur);
-    else
-      load_fast(buf, s, cur);
   };
 
   float acc[RPL][M];
-  auto zero_acc = [&]() {
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
   };
-  auto compute = [&](const u32x4 (&buf)[U][RPL], const LinSched& s, const Cursor& cur) {
+  auto compute = [&](const u32x4 (&buf)[U][RPL], const LinSched& s, const Cursor& cur)
+      __attribute__((always_inline)) {
     const int chunk_base = (cur.it / s.ipc) * s.kc;
     const int row_units = s.kc / 8;
     if (s.ragged_k && cur.it == s.n_it - 1) {
@@ -343,7 +345,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
       }
     }
   };
-  auto finish = [&](const LinSched& s, const Cursor& cur) {
+  auto finish = [&](const LinSched& s, const Cursor& cur) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
 #pragma unroll
@@ -360,9 +362,9 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
       const int m = i / NR, rr = i - m * NR;
       const int row = rb * NR + rr;
       if (row < s.N) {
-        const float v = ((red[(0 * NR + rr) * M + m] + red[(1 * NR + rr) * M + m]) +
-                         red[(2 * NR + rr) * M + m]) +
-                        red[(3 * NR + rr) * M + m];
+        float v = red[rr * M + m];
+#pragma unroll
+        for (int w = 1; w < kStreamWaves; ++w) v += red[(w * NR + rr) * M + m];  // wave order
         const size_t o = (size_t)m * s.N + row;
         if (is_chain) {  // visible at device scope without a cache write-back
           if (s.bf16)
@@ -384,53 +386,43 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
 
   // Arrive at the counters of linears [from, to) in which this workgroup
   // has no row block (nothing to wait for, nothing to compute).
-  auto arrive_empty = [&](int from, int to) {
+  auto arrive_empty = [&](int from, int to) __attribute__((always_inline)) {
     if (!is_chain) return;
     for (int l = from; l < to; ++l) arrive(l);
   };
 
-  // One pipeline step on buffer buf: compute stage c, refill buf with stage
-  // p, close the row block / linear if c was its last stage, advance c.
-  auto step = [&](u32x4 (&buf)[U][RPL]) {
+  // Waves that write outputs (the reduced row block is stored by the first
+  // NR * M threads) wait for their stores before the workgroup arrives at a
+  // linear's counter; the other waves never wait before the barrier, so the
+  // refills they issued for the next linear keep streaming through it.
+  const bool storer = wave * kWave < NR * M;
+  u32x4 wbuf[DEPTH][U][RPL];
+
+  // One pipeline step on buffer IB: compute stage c, refill the buffer with
+  // stage p (DEPTH stages ahead), close the row block / linear if c was its
+  // last stage, advance c.
+  auto step = [&](auto IB) __attribute__((always_inline)) {
+    constexpr int ib = decltype(IB)::value;
+    auto& buf = wbuf[ib];
     if (c.it == 0 && c.j == 0) {
       // first stage of a linear: its x may depend on the previous linear
       if (is_chain && c.l > 0) wait(c.l - 1);
-      load_x(cs, 0);
-      store_x(cs, 0);
-      __syncthreads();
+      stage_x(cs, 0);
       if (trace && tid == 0) trace[((size_t)c.l * G + bid) * 4 + 2] = wall_clock64();
     } else if (c.it % cs.ipc == 0 && cs.ipc < cs.n_it) {
-      // next activation chunk (chunk 0 again for a new row block); its loads
-      // were issued during the previous stage
+      // next activation chunk (chunk 0 again for a new row block), once
+      // every wave is done with the previous one
       __syncthreads();
-      store_x(cs, c.it / cs.ipc);
-      __syncthreads();
+      stage_x(cs, c.it / cs.ipc);
     }
     compute(buf, cs, c);
     const bool closes_rb = c.it == cs.n_it - 1;
     if (closes_rb) finish(cs, c);  // output stores precede the refill load
-    // The next stage of this linear opens a new activation chunk: issue its
-    // loads now, ahead of the weight refill, so that consuming them next
-    // stage (vmcnt completes in order) leaves the refill in flight.
-    if (cs.ipc < cs.n_it) {
-      const bool same_rb = !closes_rb;
-      const bool next_rb = closes_rb && c.j + 1 < cs.my_rb;
-      const int nit = closes_rb ? 0 : c.it + 1;
-      if ((same_rb || next_rb) && nit % cs.ipc == 0) load_x(cs, nit / cs.ipc);
-    }
-    const bool refilled = p.valid;
-    if (refilled) {
-      load(buf, ps, p);
-      advance(p, ps);
-    }
+    load(buf, ps, p);  // unconditional: an exhausted cursor loads a clamped valid address
+    if (p.valid) advance(p, ps);
     if (closes_rb && c.j == cs.my_rb - 1 && is_chain) {
       if (trace && tid == 0) trace[((size_t)c.l * G + bid) * 4 + 3] = wall_clock64();
-      // complete this wave's output stores (and older loads), keeping the
-      // refill just issued in flight
-      if (refilled)
-        wait_vmcnt<U * RPL>();  // only this step's refill may stay in flight
-      else
-        wait_vmcnt<0>();
+      if (storer) wait_vmcnt<0>();  // output stores complete (and, in order, older loads)
       arrive(c.l);
     }
     const int l_before = c.l;
@@ -444,33 +436,21 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
   p = c;
   ps = cs;
   // DEPTH register stages of weights are in flight ahead of the compute.
-  u32x4 wa[U][RPL], wb[U][RPL];
-#if SPECV_STREAM_DEPTH >= 3
-  u32x4 wc[U][RPL];
-#endif
-  if (p.valid) {
-    load(wa, ps, p);
-    advance(p, ps);
-  }
-  if (p.valid) {
-    load(wb, ps, p);
-    advance(p, ps);
-  }
-#if SPECV_STREAM_DEPTH >= 3
-  if (p.valid) {
-    load(wc, ps, p);
-    advance(p, ps);
-  }
-#endif
+  static_for<DEPTH>([&](auto D) __attribute__((always_inline)) {
+    load(wbuf[decltype(D)::value], ps, p);
+    if (p.valid) advance(p, ps);
+  });
   while (c.valid) {
-    step(wa);
-    if (!c.valid) break;
-    step(wb);
-#if SPECV_STREAM_DEPTH >= 3
-    if (!c.valid) break;
-    step(wc);
-#endif
+    bool more = true;
+    static_for<DEPTH>([&](auto D) __attribute__((always_inline)) {
+      if (more) {
+        step(D);
+        more = c.valid;
+      }
+    });
   }
+  // Refills past the end are never consumed; let them land before exit.
+  wait_vmcnt<0>();
 
   // exit: the last workgroup out advances the generation
   if (is_chain) {
@@ -488,41 +468,49 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
 // Launch: per-M tile choice and the persistent grid
 // ---------------------------------------------------------------------------
 
-template <int M, int RPL, int U, int KCMAX>
+template <int M, int RPL, int U, int KCMAX, int DEPTH>
 static hipError_t launch_m(const StreamLinear& single, const StreamLinear* chain, int n_lin,
                            ChainSync* sync, int grid, hipStream_t s) {
   using S = Stream<M, RPL, U, KCMAX>;
-  hipLaunchKernelGGL((gemm_stream_kernel<M, RPL, U, KCMAX>), dim3(grid), dim3(kStreamThreads),
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH>), dim3(grid), dim3(kStreamThreads),
                      S::kLdsBytes, s, single, chain, n_lin, sync);
   return hipGetLastError();
 }
 
-// Tile parameters per M: (RPL, U, KCMAX). Rows per row block = 4 * RPL;
-// activation chunk KCMAX elements (M * KCMAX * 2 bytes of LDS).
+// Tile parameters per M: (RPL, U, KCMAX, DEPTH). Rows per row block =
+// 4 * RPL; activation chunk KCMAX elements (M * KCMAX * 2 bytes of LDS, at
+// most about 150 KB so that whole activations of d_in up to 14336 stay
+// resident at M = 5); DEPTH register stages of U * RPL 16-byte loads per
+// lane in flight (8 KB per wave per stage; two-wave-per-SIMD register
+// budget).
 #ifndef SPECV_T5
-#define SPECV_T5(X) X(5, 2, 4, 4096)
+#define SPECV_T5(X) X(5, 4, 2, 14336, 4)
 #endif
 #define SPECV_STREAM_TABLE(X) \
-  X(1, 4, 2, 8192)            \
-  X(2, 4, 2, 8192)            \
-  X(3, 4, 2, 4096)            \
-  X(4, 4, 2, 4096)            \
-  SPECV_T5(X)                 \
-  X(6, 4, 2, 4096)            \
-  X(7, 4, 2, 2048)            \
-  X(8, 4, 2, 2048)            \
-  X(9, 2, 2, 2048)            \
-  X(10, 2, 2, 2048)           \
-  X(11, 2, 2, 2048)           \
-  X(12, 2, 2, 2048)           \
-  X(13, 2, 2, 1024)           \
-  X(14, 2, 2, 1024)           \
-  X(15, 2, 2, 1024)           \
-  X(16, 2, 2, 1024)
+  X(1, 4, 2, 32768, 4)         \
+  X(2, 4, 2, 32768, 4)         \
+  X(3, 4, 2, 24576, 4)         \
+  X(4, 4, 2, 18432, 4)         \
+  SPECV_T5(X)                  \
+  X(6, 4, 2, 12288, 4)         \
+  X(7, 4, 2, 10240, 4)         \
+  X(8, 4, 2, 8192, 4)          \
+  X(9, 4, 2, 6144, 4)          \
+  X(10, 4, 2, 6144, 4)         \
+  X(11, 4, 2, 6144, 4)         \
+  X(12, 4, 2, 6144, 4)         \
+  X(13, 4, 2, 4096, 3)         \
+  X(14, 4, 2, 4096, 3)         \
+  X(15, 4, 2, 4096, 3)         \
+  X(16, 4, 2, 4096, 3)
 
 size_t stream_rows_per_block(int M) {
   switch (M) {
-#define SPECV_NR(MM, RPL, U, KC) \
+#define SPECV_NR(MM, RPL, U, KC, D) \
   case MM:                       \
     return 4 * RPL;
     SPECV_STREAM_TABLE(SPECV_NR)
@@ -532,11 +520,13 @@ size_t stream_rows_per_block(int M) {
   }
 }
 
-template <int M, int RPL, int U, int KCMAX>
+template <int M, int RPL, int U, int KCMAX, int DEPTH>
 static int max_wgs_m() {
   using S = Stream<M, RPL, U, KCMAX>;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_stream_kernel<M, RPL, U, KCMAX>,
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLdsBytes);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH>,
                                                    kStreamThreads, S::kLdsBytes) != hipSuccess)
     return 1;
   return n > 0 ? n : 1;
@@ -544,9 +534,9 @@ static int max_wgs_m() {
 
 int stream_max_wgs_per_cu(int M) {
   switch (M) {
-#define SPECV_OCC(MM, RPL, U, KC) \
+#define SPECV_OCC(MM, RPL, U, KC, D) \
   case MM:                        \
-    return max_wgs_m<MM, RPL, U, KC>();
+    return max_wgs_m<MM, RPL, U, KC, D>();
     SPECV_STREAM_TABLE(SPECV_OCC)
 #undef SPECV_OCC
     default:
@@ -557,9 +547,9 @@ int stream_max_wgs_per_cu(int M) {
 hipError_t launch_gemm_stream_any(const StreamLinear& single, const StreamLinear* chain, int n_lin,
                                   ChainSync* sync, int M, int grid, hipStream_t s) {
   switch (M) {
-#define SPECV_CASE(MM, RPL, U, KC) \
+#define SPECV_CASE(MM, RPL, U, KC, D) \
   case MM:                         \
-    return launch_m<MM, RPL, U, KC>(single, chain, n_lin, sync, grid, s);
+    return launch_m<MM, RPL, U, KC, D>(single, chain, n_lin, sync, grid, s);
     SPECV_STREAM_TABLE(SPECV_CASE)
 #undef SPECV_CASE
     default:

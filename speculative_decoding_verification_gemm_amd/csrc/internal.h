@@ -12,6 +12,9 @@ namespace specv {
 // Largest number of verify positions handled by the vector-ALU streaming
 // kernel; larger M uses the MFMA kernel.
 constexpr int kMaxStreamM = 16;
+// Largest M for the weight-streaming MFMA kernel (gemm_skinny.hip); larger M
+// uses the tiled MFMA kernel.
+constexpr int kMaxSkinnyM = 128;
 
 // One linear of a streaming launch; layout identical to spec_linear of the
 // public header (x, w, y, d_in, d_out, y_dtype, reserved).
@@ -58,6 +61,8 @@ hipError_t launch_gemm_stream(const uint16_t* x, const uint16_t* w, void* y, boo
                               int K, int N, int grid, hipStream_t s);
 hipError_t launch_gemm_chain(const StreamLinear* chain, int n_lin, ChainSync* sync, int M, int grid,
                              hipStream_t s);
+hipError_t launch_gemm_skinny(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
+                              int K, int N, hipStream_t s);
 hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
                             int K, int N, hipStream_t s);
 

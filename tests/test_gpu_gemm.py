@@ -62,6 +62,28 @@ def test_stream_kernel_every_m(sv, dev, M, d_in, d_out):
     check(y, oracle.linear(x, w), torch.float32, f"stream M={M} {d_in}->{d_out}")
 
 
+# 17..128 positions: the weight-streaming MFMA kernel. d_in = 1032 leaves a
+# ragged 64-element segment, d_out = 777 a partial 16-row tile; every count
+# of 16-row position tiles (2..8) and partial position tiles are covered.
+@pytest.mark.parametrize("M", [17, 20, 31, 32, 33, 48, 63, 64, 65, 80, 96, 97, 112, 127, 128])
+def test_skinny_kernel(sv, dev, M):
+    import torch
+    x, w = synth.linear_inputs(300 + M, "skinny", M, 1032, 777)
+    for od in (torch.float32, torch.bfloat16):
+        y = run_host(sv, dev, x, w, od)
+        check(y, oracle.linear(x, w), od, f"skinny M={M} {od}")
+
+
+# d_out >= 16384 switches to two 16-row weight tiles per workgroup; 16400
+# ends in a partial tile, d_in = 520 in a partial segment.
+@pytest.mark.parametrize("M", [17, 40, 64])
+def test_skinny_kernel_wide(sv, dev, M):
+    import torch
+    x, w = synth.linear_inputs(400 + M, "skinny_wide", M, 520, 16400)
+    y = run_host(sv, dev, x, w, torch.float32)
+    check(y, oracle.linear(x, w), torch.float32, f"skinny wide M={M}")
+
+
 @pytest.mark.parametrize("M", [17, 20, 33, 64, 80, 130, 320])
 def test_mfma_kernel(sv, dev, M):
     import torch
