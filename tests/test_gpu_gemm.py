@@ -53,8 +53,11 @@ def test_tiny_linear(sv, dev, out):
 
 # ragged d_in (not a multiple of the 128-element segment) and d_out (not a
 # multiple of the rows per workgroup); 9000 spans several activation chunks
+# at the larger M. d_out 1024 (whole 16-row blocks) and 4104 (24 rows per
+# workgroup: a whole and a half block) take the 8-outputs-per-store path,
+# 777 and 300 (not multiples of 8) the one-output-per-store path.
 @pytest.mark.parametrize("M", list(range(1, 17)))
-@pytest.mark.parametrize("d_in,d_out", [(1032, 777), (9000, 300)])
+@pytest.mark.parametrize("d_in,d_out", [(1032, 777), (9000, 300), (1032, 1024), (520, 4104)])
 def test_stream_kernel_every_m(sv, dev, M, d_in, d_out):
     import torch
     x, w = synth.linear_inputs(100 + M, f"stream{d_in}", M, d_in, d_out)
