@@ -12,8 +12,8 @@
 //    reduction dimension; there are N / (16 * NT) workgroups, so the grid
 //    fills the chip without splitting the reduction across workgroups.
 //  * Its eight waves interleave 64-element segments of the reduction (128
-//    contiguous bytes of each row per segment), which keeps about 64 KB of
-//    weights in flight per workgroup. Each lane loads its 16-byte weight
+//    contiguous bytes of each row per segment); a pipeline stage holds U
+//    segments, which keeps 64 to 128 KB of weights in flight per workgroup. Each lane loads its 16-byte weight
 //    fragments straight into MFMA operand registers; no weight byte passes
 //    through LDS.
 //  * No two waves of a workgroup need the same activation element, so the
@@ -38,8 +38,9 @@ constexpr int kSegK = 64;  // reduction elements per wave segment
 #define SPECV_SK_GLOBAL __attribute__((address_space(1)))
 
 // MT 16-row tiles of positions, NT 16-row tiles of weight rows per
-// workgroup, KW waves splitting the reduction dimension.
-template <int MT, int NT, int KW, bool OUT_BF16>
+// workgroup, KW waves splitting the reduction dimension, U segments per
+// pipeline stage (two stages in flight).
+template <int MT, int NT, int KW, int U, bool OUT_BF16>
 __global__ __launch_bounds__(KW * kWave) void gemm_skinny_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y, int M,
     int N, int K) {
@@ -64,8 +65,10 @@ __global__ __launch_bounds__(KW * kWave) void gemm_skinny_kernel(
 
   // Segments s = wave, wave + KW, ...; segment s covers k in [64 s, 64 s + 64).
   // In segment s, MFMA j (0, 1) takes k = 64 s + 32 j + 8 * grp + (0..7).
+  // Stage i of a wave holds its segments i * U .. i * U + U - 1.
   const int n_seg = (K + kSegK - 1) / kSegK;
   const int my_seg = n_seg > wave ? (n_seg - wave + KW - 1) / KW : 0;
+  const int n_st = (my_seg + U - 1) / U;
   const int K8 = K >> 3;  // 16-byte units per row
 
   f32x4 acc[NT][MT];
@@ -76,58 +79,63 @@ __global__ __launch_bounds__(KW * kWave) void gemm_skinny_kernel(
 
   // Loaded values are used only by the matrix instructions: no instruction
   // between a load and its MFMA reads them, so the loads of both register
-  // stages stay in flight. Reduction elements past K (the ragged tail) load
-  // a clamped valid unit; the weight fragment is zeroed at use.
+  // stages stay in flight. Reduction elements past K (the ragged tail, and
+  // the unused segments of a wave's last stage) load a clamped valid unit;
+  // the weight fragment is zeroed at use.
   struct Frag {
-    u32x4 x[2][MT];
-    u32x4 w[2][NT];
-    bool kok[2];
+    u32x4 x[U][2][MT];
+    u32x4 w[U][2][NT];
+    bool kok[U][2];
   };
-  auto load = [&](Frag& f, int i) {
-    const int s = wave + KW * i;
+  auto load = [&](Frag& f, int i) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int u = s * (kSegK / 8) + j * 4 + grp;  // 16-byte unit index along k
-      f.kok[j] = u < K8;
-      const int uc = min(u, K8 - 1);
+    for (int u = 0; u < U; ++u) {
+      const int s = wave + KW * (i * U + u);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) f.w[j][t] = __builtin_nontemporal_load(wrow[t] + uc);
+      for (int j = 0; j < 2; ++j) {
+        const int unit = s * (kSegK / 8) + j * 4 + grp;  // 16-byte unit index along k
+        f.kok[u][j] = unit < K8;
+        const int uc = min(unit, K8 - 1);
 #pragma unroll
-      for (int t = 0; t < MT; ++t) f.x[j][t] = xrow[t][uc];
+        for (int t = 0; t < NT; ++t) f.w[u][j][t] = __builtin_nontemporal_load(wrow[t] + uc);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) f.x[u][j][t] = xrow[t][uc];
+      }
     }
   };
-  const bool ragged = (K % kSegK) != 0;
-  auto mma = [&](const Frag& f, bool last) {
+  auto mma = [&](const Frag& f, bool last) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        u32x4 wv = f.w[j][i];
-        if (ragged && last) wv = f.kok[j] ? wv : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-          acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, f.x[j][t]), __builtin_bit_cast(bf16x8, wv), acc[i][t], 0,
-              0, 0);
-      }
+        for (int i = 0; i < NT; ++i) {
+          u32x4 wv = f.w[u][j][i];
+          if (last) wv = f.kok[u][j] ? wv : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, f.x[u][j][t]), __builtin_bit_cast(bf16x8, wv),
+                acc[i][t], 0, 0, 0);
+        }
   };
 
   // The prologue and the steady-state loop issue their loads on every path
-  // (a segment past the wave's last one reads a clamped valid address and
-  // is never used), so the compiler's vmcnt waits keep both stages in
-  // flight; the last zero to three segments are finished after the loop.
-  // Only a wave's last segment can reach past K.
+  // (a stage past the wave's last one reads clamped valid addresses and is
+  // never used), so the compiler's vmcnt waits keep both stages in flight;
+  // the last zero to three stages are finished after the loop. Only a
+  // wave's last stage can reach past K.
   Frag fa, fb;
   load(fa, 0);
   load(fb, 1);
   int i = 0;
-  for (; i + 4 <= my_seg; i += 2) {
+  for (; i + 4 <= n_st; i += 2) {
     mma(fa, false);
     load(fa, i + 2);
     mma(fb, false);
     load(fb, i + 3);
   }
-  const int rem = my_seg - i;  // 0..3 segments left, already loaded up to 2
+  const int rem = n_st - i;  // 0..3 stages left, already loaded up to 2
   if (rem >= 1) mma(fa, rem == 1);
   if (rem >= 3) load(fa, i + 2);
   if (rem >= 2) mma(fb, rem == 2);
@@ -165,46 +173,53 @@ __global__ __launch_bounds__(KW * kWave) void gemm_skinny_kernel(
   }
 }
 
-template <int MT, int NT, int KW>
+template <int MT, int NT, int U>
 static hipError_t launch_skinny_t(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16,
                                   int M, int K, int N, hipStream_t s) {
+  constexpr int KW = 8;
   const dim3 grid((N + 16 * NT - 1) / (16 * NT));
   if (out_bf16)
-    hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KW, true>), grid, dim3(KW * kWave), 0, s, x, w,
-                       y, M, N, K);
+    hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KW, U, true>), grid, dim3(KW * kWave), 0, s, x,
+                       w, y, M, N, K);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KW, false>), grid, dim3(KW * kWave), 0, s, x,
+    hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KW, U, false>), grid, dim3(KW * kWave), 0, s, x,
                        w, y, M, N, K);
   return hipGetLastError();
 }
 
-// Weight rows per workgroup: more rows reuse each activation fragment for
-// more weight bytes (activation reads per weight byte = M / rows), fewer
-// rows give more workgroups. 16 * NT rows keep at least 128 workgroups on
-// the narrowest linears here (4096 rows) and 448 on the wide ones.
-template <int MT>
+// Tile choice per count of position tiles, measured on the Llama-shaped
+// linears. Narrow linears (N < 16384) use NT1 16-row weight tiles per
+// workgroup (one keeps 256 workgroups at N = 4096), wide ones NT2 (more
+// rows reuse each activation fragment for more weight bytes). U segments
+// per pipeline stage; the register file (256 VGPRs per lane at two waves
+// per SIMD) bounds NT, U and the position tiles together.
+#define SPECV_SKINNY_TABLE(X) \
+  X(2, 1, 1, 4, 1)            \
+  X(3, 1, 2, 2, 2)            \
+  X(4, 1, 2, 2, 1)            \
+  X(5, 1, 1, 2, 1)            \
+  X(6, 1, 1, 1, 1)            \
+  X(7, 1, 1, 1, 1)            \
+  X(8, 1, 1, 1, 1)
+// (MT, NT1, U1, NT2, U2)
+
+template <int MT, int NT1, int U1, int NT2, int U2>
 static hipError_t launch_skinny_m(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16,
                                   int M, int K, int N, hipStream_t s) {
-  // (Register budget: 256 VGPRs per lane at two waves per SIMD; 8 position
-  // tiles leave room for one weight tile only.)
-  constexpr int kNarrow = (MT <= 2 || MT >= 6) ? 1 : 2;
-  constexpr int kWide = MT <= 3 ? 4 : (MT <= 5 ? 2 : 1);
-  if (N >= 16384) return launch_skinny_t<MT, kWide, 8>(x, w, y, out_bf16, M, K, N, s);
-  return launch_skinny_t<MT, kNarrow, 8>(x, w, y, out_bf16, M, K, N, s);
+  if (N >= 16384) return launch_skinny_t<MT, NT2, U2>(x, w, y, out_bf16, M, K, N, s);
+  return launch_skinny_t<MT, NT1, U1>(x, w, y, out_bf16, M, K, N, s);
 }
 
 hipError_t launch_gemm_skinny(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
                               int K, int N, hipStream_t s) {
-  switch ((M + 15) / 16) {
-    case 1:
-    case 2: return launch_skinny_m<2>(x, w, y, out_bf16, M, K, N, s);
-    case 3: return launch_skinny_m<3>(x, w, y, out_bf16, M, K, N, s);
-    case 4: return launch_skinny_m<4>(x, w, y, out_bf16, M, K, N, s);
-    case 5: return launch_skinny_m<5>(x, w, y, out_bf16, M, K, N, s);
-    case 6: return launch_skinny_m<6>(x, w, y, out_bf16, M, K, N, s);
-    case 7: return launch_skinny_m<7>(x, w, y, out_bf16, M, K, N, s);
-    case 8: return launch_skinny_m<8>(x, w, y, out_bf16, M, K, N, s);
-    default: return hipErrorInvalidValue;
+  switch (max((M + 15) / 16, 2)) {
+#define SPECV_SKINNY_CASE(MT, NT1, U1, NT2, U2) \
+  case MT:                                      \
+    return launch_skinny_m<MT, NT1, U1, NT2, U2>(x, w, y, out_bf16, M, K, N, s);
+    SPECV_SKINNY_TABLE(SPECV_SKINNY_CASE)
+#undef SPECV_SKINNY_CASE
+    default:
+      return hipErrorInvalidValue;
   }
 }
 

@@ -54,7 +54,10 @@ constexpr int kStreamThreads = kStreamWaves * kWave;
 constexpr int kSeg = 128;           // reduction elements per lane group per segment
 constexpr int kCachePolicyDevice = 16;  // buffer-load aux bits: sc1 (device scope)
 constexpr int kSpinLimit = 1 << 18;  // well under a second of polling before a barrier gives up
-constexpr int kPollSleep = 4;        // s_sleep units (64 clocks each) between polls
+#ifndef SPECV_POLL_SLEEP
+#define SPECV_POLL_SLEEP 4
+#endif
+constexpr int kPollSleep = SPECV_POLL_SLEEP;  // s_sleep units (64 clocks each) between polls
 
 // Pointers taken from a descriptor are generic; naming the global address
 // space lets the compiler emit global (not flat) loads and stores, which
