@@ -213,14 +213,20 @@ def verify_batch_probs(P, Q, tokens, u_accept, u_sample):
     return {k: np.array([r[k] for r in rounds]) for k in _BATCH_KEYS}
 
 
-def verify_batch(target_logits, draft_logits, tokens, u_accept, u_sample):
+def verify_batch(target_logits, draft_logits, tokens, u_accept, u_sample, t_target=1.0,
+                 t_draft=1.0):
     """The whole sampling stage from float32 logits.
 
-    target_logits [B][K+1][V], draft_logits [B][K][V] -> softmax in fp64 ->
-    verify_round per sequence. Also returns the probabilities.
+    target_logits [B][K+1][V], draft_logits [B][K][V] -> softmax in fp64 at
+    temperatures t_target (the requested law) and t_draft (the law the
+    drafts were drawn from) -> verify_round per sequence. Also returns the
+    probabilities. t_target = 0 is greedy verification: the warped target is
+    one-hot at its argmax, so a draft is kept iff it is that argmax and the
+    round ends with the argmax ("Two Models, One Voice", Three remarks worth
+    internalizing).
     """
-    P, _, _ = softmax_rows(target_logits)
-    Q, _, _ = softmax_rows(draft_logits)
+    P, _, _ = softmax_rows(target_logits, t_target)
+    Q, _, _ = softmax_rows(draft_logits, t_draft)
     res = verify_batch_probs(P, Q, tokens, u_accept, u_sample)
     res["P"] = P
     res["Q"] = Q

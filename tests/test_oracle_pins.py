@@ -427,3 +427,101 @@ def test_invalid_inputs_have_defined_results():
     assert oracle.inverse_cdf(np.zeros(4), 0.3)[0] == -1
     tok, _, _ = spec.sample_batch(np.array([P]), np.array([Q]), [2], [[0.5, 0.5]])
     assert tok[0] == -1
+
+
+# ---------------------------------------------------------------------------
+# Temperature and greedy verification
+# ---------------------------------------------------------------------------
+
+def _greedy_logits(picks, vocab, rng):
+    """Logits whose argmax at row i is picks[i] (clear margin)."""
+    l = rng.standard_normal((len(picks), len(vocab))).astype(np.float32)
+    for i, t in enumerate(picks):
+        l[i, vocab.index(t)] = np.float32(6.0)
+    return l
+
+
+@pytest.mark.parametrize("case", ["printed", "all_match"])
+def test_greedy_worked_example(golden, case):
+    """Greedy verification (target temperature 0) reproduces the printed
+    verify_greedy call, for every choice of uniforms: three accepted guesses
+    plus the target's correction, or four plus the bonus token."""
+    g = golden("guess_several_greedy.json")
+    draft = g["draft"] if case == "printed" else g["all_match_draft"]
+    want = g["printed_result"] if case == "printed" else g["all_match_result"]
+    vocab = sorted(set(g["draft"]) | set(g["target_picks"]) | {" the", " city"})
+    rng = np.random.default_rng(5)
+    tl = _greedy_logits(g["target_picks"], vocab, rng)[None]
+    dl = rng.standard_normal((1, len(draft), len(vocab))).astype(np.float32)
+    toks = np.array([[vocab.index(t) for t in draft]])
+    for trial in range(20):
+        ua = rng.random((1, len(draft)), dtype=np.float32)
+        us = rng.random((1, len(draft) + 1), dtype=np.float32)
+        r = oracle.verify_batch(tl, dl, toks, ua, us, t_target=0.0)
+        n = int(r["n_emitted"][0])
+        got = [vocab[t] for t in r["out_tokens"][0][:n]]
+        assert got == want, (trial, got)
+        assert (r["out_tokens"][0][n:] == -1).all()
+
+
+def test_temperature_two_token_closed_form():
+    # p1 = sigmoid(d / T) for logits (0, d); T = 1 is the plain softmax
+    for d in (0.5, 2.0, -3.0):
+        for T in (0.25, 0.7, 1.0, 3.0):
+            p, _, _ = oracle.softmax_rows(np.array([[0.0, d]], np.float32), T)
+            assert abs(p[0, 1] - 1.0 / (1.0 + math.exp(-d / T))) < 1e-15
+    l = np.random.default_rng(1).standard_normal((3, 50)).astype(np.float32)
+    assert np.array_equal(oracle.softmax_rows(l, 1.0)[0], oracle.softmax_rows(l)[0])
+    # scipy reference at T: softmax of l / T
+    for T in (0.3, 2.5):
+        ref = scipy.special.softmax(l.astype(np.float64) / T, axis=-1)
+        assert np.abs(oracle.softmax_rows(l, T)[0] - ref).max() < 1e-15
+
+
+def test_temperature_zero_is_first_argmax_and_the_cold_limit():
+    l = np.array([[0.5, 2.0, 2.0, -1.0], [3.0, 1.0, 0.0, 2.9]], np.float32)
+    p0, _, s0 = oracle.softmax_rows(l, 0.0)
+    assert np.array_equal(p0, [[0, 1, 0, 0], [1, 0, 0, 0]]) and np.array_equal(s0, [1, 1])
+    # a clear maximum: T -> 0 approaches the one-hot law
+    pc, _, _ = oracle.softmax_rows(l[1:], 1e-3)
+    assert abs(pc[0, 0] - 1.0) < 1e-12
+    with pytest.raises(ValueError):
+        oracle.softmax_rows(l, -1.0)
+
+
+def test_warped_law_is_the_warped_target():
+    """The rule applied to warped p and q emits exactly the warped target
+    (its law does not depend on how p and q were produced)."""
+    rng = np.random.default_rng(2)
+    for T_t, T_d in ((0.6, 0.6), (0.6, 1.4), (2.0, 1.0)):
+        lt = rng.standard_normal((1, 40)).astype(np.float32) * 2
+        ld = lt + rng.standard_normal((1, 40)).astype(np.float32)
+        p = oracle.softmax_rows(lt, T_t)[0][0]
+        q = oracle.softmax_rows(ld, T_d)[0][0]
+        law, alpha = oracle.emitted_law(p, q)
+        assert np.abs(law - p).max() < 1e-15
+        assert abs(alpha - (1 - oracle.total_variation(p, q))) < 1e-14
+
+
+def test_greedy_expected_tokens_monte_carlo():
+    """Greedy target, drafts sampled from q: position j is accepted with
+    probability alpha_j = q_j(argmax p_j), so tokens per round have mean
+    1 + sum_i prod_{j<=i} alpha_j. 40000 rounds, within 4 standard errors."""
+    rng = np.random.default_rng(3)
+    K, V, R = 4, 12, 40000
+    lt = (rng.standard_normal((1, K + 1, V)) * 1.5).astype(np.float32)
+    ld = (lt[:, :K] + rng.standard_normal((1, K, V)).astype(np.float32) * 0.8).astype(np.float32)
+    P, _, _ = oracle.softmax_rows(lt, 0.0)
+    Q, _, _ = oracle.softmax_rows(ld, 1.0)
+    a = [Q[0, j, int(np.argmax(lt[0, j]))] for j in range(K)]
+    want = oracle.expected_tokens_general(a)
+    cq = np.cumsum(Q[0], axis=-1)
+    n_tot = np.zeros(R)
+    for r in range(R):
+        u = rng.random(K)
+        toks = np.array([[min(int(np.searchsorted(cq[j], u[j] * cq[j, -1], side="right")), V - 1)
+                          for j in range(K)]])
+        res = spec.verify_batch_probs(P, Q, toks, rng.random((1, K)), rng.random((1, K + 1)))
+        n_tot[r] = res["n_emitted"][0]
+    se = n_tot.std() / math.sqrt(R)
+    assert abs(n_tot.mean() - want) < 4 * se, (n_tot.mean(), want, se)
