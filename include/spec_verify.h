@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 1
+#define SPEC_ABI_VERSION 2
 
 /* Status codes. */
 #define SPEC_OK 0
@@ -259,6 +259,34 @@ int spec_verify(const uint16_t* hidden, const uint16_t* lm_head, int d,
                 const float* u_sample, int B, int K, int V,
                 int32_t* out_tokens, int32_t* n_emitted, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_warped -- spec_verify on temperature-warped distributions:
+ * p = softmax(target_logits / t_target), q = softmax(draft_logits /
+ * t_draft). The accept test, the first rejection and the residual or bonus
+ * draw are unchanged; they are exact for whatever distributions they are
+ * given ("Speculative Decoding: Two Models, One Voice", Three remarks worth
+ * internalizing; "Speculative Decoding: Guess Several Tokens, Check Them in
+ * One Pass", What happens to the rejected tokens). t_draft must be the
+ * temperature the drafts were drawn at ("Speculative Decoding: The Algebra
+ * and the Proof", Where it breaks).
+ *
+ *   t_target, t_draft  finite, >= 0. A temperature of 0 is the one-hot law
+ *                 of the row's first maximum: with t_target = 0 the step is
+ *                 greedy verification -- a draft is kept iff it is the
+ *                 target's argmax, and the round ends with the argmax of the
+ *                 first mismatching (or the bonus) row; u_accept and
+ *                 u_sample do not change the result ("Two Models, One
+ *                 Voice", the same remarks). spec_verify is this call with
+ *                 both temperatures 1.
+ * Other arguments, limits and workspace as for spec_verify. A negative or
+ * non-finite temperature returns SPEC_ERR_INVALID_ARGUMENT.
+ */
+int spec_verify_warped(const uint16_t* hidden, const uint16_t* lm_head, int d,
+                       float* target_logits, const float* draft_logits,
+                       const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                       int B, int K, int V, float t_target, float t_draft, int32_t* out_tokens,
+                       int32_t* n_emitted, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -40,6 +40,7 @@ SPEC_BF16 = 1
 _p = ctypes.c_void_p
 _i = ctypes.c_int
 _z = ctypes.c_size_t
+_f = ctypes.c_float
 
 # name -> (restype, argtypes), exactly as declared in include/spec_verify.h
 SIGNATURES = {
@@ -56,6 +57,8 @@ SIGNATURES = {
     "spec_verify_gemm_chain": (_i, [_i, _i, _p, _p]),
     "spec_chain_error": (_i, [_p, ctypes.POINTER(ctypes.c_int)]),
     "spec_verify": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _z, _p]),
+    "spec_verify_warped": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _f, _f, _p, _p, _p,
+                                _z, _p]),
 }
 for _name, (_res, _args) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -207,10 +210,13 @@ def new_workspace(B, K, V, device="cuda"):
 
 
 def verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
-           hidden=None, lm_head=None, workspace=None, out_tokens=None, n_emitted=None):
+           hidden=None, lm_head=None, workspace=None, out_tokens=None, n_emitted=None,
+           t_target=1.0, t_draft=1.0):
     """The verify step after the stack. With hidden [B*(K+1)][d] and lm_head
     [V][d] (bf16), target_logits [B][K+1][V] is written first; otherwise it
-    is an input. Returns (out_tokens int32 [B][K+1], n_emitted int32 [B])."""
+    is an input. t_target / t_draft are the temperatures of the target's and
+    the draft's distributions (0: greedy, one-hot at the first maximum).
+    Returns (out_tokens int32 [B][K+1], n_emitted int32 [B])."""
     torch = _torch()
     _need(target_logits, torch.float32, "target_logits", 3)
     _need(draft_logits, torch.float32, "draft_logits", 3)
@@ -232,10 +238,17 @@ def verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
         out_tokens = torch.empty((B, K1), dtype=torch.int32, device=target_logits.device)
     if n_emitted is None:
         n_emitted = torch.empty(B, dtype=torch.int32, device=target_logits.device)
-    check(lib.spec_verify(_ptr(hidden), _ptr(lm_head), d, _ptr(target_logits),
-                          _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
-                          _ptr(u_sample), B, K, V, _ptr(out_tokens), _ptr(n_emitted),
-                          _ptr(workspace), workspace.numel(), _stream()))
+    if t_target == 1.0 and t_draft == 1.0:
+        check(lib.spec_verify(_ptr(hidden), _ptr(lm_head), d, _ptr(target_logits),
+                              _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
+                              _ptr(u_sample), B, K, V, _ptr(out_tokens), _ptr(n_emitted),
+                              _ptr(workspace), workspace.numel(), _stream()))
+    else:
+        check(lib.spec_verify_warped(_ptr(hidden), _ptr(lm_head), d, _ptr(target_logits),
+                                     _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
+                                     _ptr(u_sample), B, K, V, float(t_target), float(t_draft),
+                                     _ptr(out_tokens), _ptr(n_emitted), _ptr(workspace),
+                                     workspace.numel(), _stream()))
     return out_tokens, n_emitted
 
 

@@ -3,6 +3,7 @@
 // launches nothing and the checks run on hosts without a GPU.
 
 #include <hip/hip_runtime.h>
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -327,7 +328,21 @@ int spec_verify(const uint16_t* hidden, const uint16_t* lm_head, int d, float* t
                 const float* draft_logits, const int32_t* draft_tokens, const float* u_accept,
                 const float* u_sample, int B, int K, int V, int32_t* out_tokens,
                 int32_t* n_emitted, void* workspace, size_t workspace_bytes, void* stream) {
+  return spec_verify_warped(hidden, lm_head, d, target_logits, draft_logits, draft_tokens, u_accept,
+                            u_sample, B, K, V, 1.0f, 1.0f, out_tokens, n_emitted, workspace,
+                            workspace_bytes, stream);
+}
+
+int spec_verify_warped(const uint16_t* hidden, const uint16_t* lm_head, int d,
+                       float* target_logits, const float* draft_logits,
+                       const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                       int B, int K, int V, float t_target, float t_draft, int32_t* out_tokens,
+                       int32_t* n_emitted, void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
+  if (!(t_target >= 0.0f) || !(t_draft >= 0.0f) || !std::isfinite(t_target) ||
+      !std::isfinite(t_draft))
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "temperatures must be finite and >= 0 (got %g, %g)",
+                (double)t_target, (double)t_draft);
   if (!target_logits || !draft_logits || !draft_tokens || !u_accept || !u_sample || !out_tokens ||
       !n_emitted || !workspace)
     return fail(SPEC_ERR_INVALID_ARGUMENT, "null required pointer");
@@ -359,7 +374,7 @@ int spec_verify(const uint16_t* hidden, const uint16_t* lm_head, int d, float* t
     return rc;
   return launched(specv::launch_verify_sampling(target_logits, draft_logits, draft_tokens, u_accept,
                                                 u_sample, B, K, V, out_tokens, n_emitted,
-                                                workspace, s),
+                                                workspace, t_target, t_draft, s),
                   "spec_verify sampling");
 }
 

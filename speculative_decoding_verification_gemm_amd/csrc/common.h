@@ -81,4 +81,18 @@ __device__ __forceinline__ float block_max_f32(float v, float* lds) {
   return t;
 }
 
+template <int NT>
+__device__ __forceinline__ int block_min_i32(int v, int* lds) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+  if (lane == 0) lds[wave] = v;
+  __syncthreads();
+  int t = lds[0];
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) t = min(t, lds[w]);
+  __syncthreads();
+  return t;
+}
+
 }  // namespace specv

@@ -77,9 +77,12 @@ hipError_t launch_sample_probs(const float* p, const float* q, const int32_t* n_
 
 // Fused sampling stage of spec_verify (logits in, tokens out).
 size_t verify_workspace_bytes(int B, int K, int V);
+// t_target, t_draft: temperatures (> 0), or 0 for greedy (one-hot at the
+// row's first maximum).
 hipError_t launch_verify_sampling(const float* target_logits, const float* draft_logits,
                                   const int32_t* tokens, const float* u_accept,
                                   const float* u_sample, int B, int K, int V, int32_t* out_tokens,
-                                  int32_t* n_emitted, void* workspace, hipStream_t s);
+                                  int32_t* n_emitted, void* workspace, float t_target,
+                                  float t_draft, hipStream_t s);
 
 }  // namespace specv

@@ -15,6 +15,7 @@
 // stored: per-row max and fp64 sum of exponentials are kept and each needed
 // probability is exp(l - max) / sum evaluated in fp64 from the fp32 logit.
 
+#include <limits.h>
 #include <math.h>
 
 #include "common.h"
@@ -170,14 +171,20 @@ struct ProbWeights {
   }
 };
 
+// Weights of a draw from logits: p(v) = exp((l_p[v] - m_p) / T_p) / s_p,
+// minus q(v) for a residual. ip, iq are the inverse temperatures (1 at
+// T = 1); a greedy draft (T_q = 0) is one-hot at qarg.
 struct LogitWeights {
   const float* lp;
   const float* lq;  // null for a plain draw from p
   double mp, sp, mq, sq;
+  double ip = 1.0, iq = 1.0;
+  int qarg = -1;    // >= 0: the draft is one-hot at this token
   __device__ __forceinline__ double operator()(int v) const {
-    const double pv = exp((double)lp[v] - mp) / sp;
+    const double pv = exp(((double)lp[v] - mp) * ip) / sp;
     if (!lq) return pv;
-    const double r = pv - exp((double)lq[v] - mq) / sq;
+    const double qv = qarg >= 0 ? (v == qarg ? 1.0 : 0.0) : exp(((double)lq[v] - mq) * iq) / sq;
+    const double r = pv - qv;
     return r > 0.0 ? r : 0.0;
   }
 };
@@ -350,7 +357,9 @@ hipError_t launch_sample_probs(const float* p, const float* q, const int32_t* n_
 // ---------------------------------------------------------------------------
 //
 // 1. stats_partial  grid R*C: per chunk of a row, max and fp64 sum of
-//                   exp(l - max); R = B*(K+1) target rows then B*K draft rows.
+//                   exp((l - max) / T); R = B*(K+1) target rows then B*K
+//                   draft rows. A greedy row (T = 0) keeps the first index of
+//                   the maximum instead.
 // 2. verify_accept  grid B, one wave: combine the chunk partials of the
 //                   sequence's 2K+1 rows into (max, sum) in a fixed order,
 //                   then the accept test and the first rejection.
@@ -359,11 +368,20 @@ hipError_t launch_sample_probs(const float* p, const float* q, const int32_t* n_
 //                   fallback).
 // 4. verify_draw    grid B: pick the chunk, draw inside it, emit.
 
+// Warping of the two distributions: inverse temperatures, and greedy
+// (temperature 0: one-hot at the row's first maximum).
+struct Warp {
+  double it, id;  // 1 / T_target, 1 / T_draft (0 when greedy)
+  int gt, gd;     // greedy target, greedy draft
+};
+
 struct VerifyWs {
   float* pmax;    // [R][C]
   double* psum;   // [R][C]
+  int32_t* parg;  // [R][C] first index of the chunk maximum (greedy rows)
   float* fmax;    // [R]
   double* fsum;   // [R]
+  int32_t* farg;  // [R] first index of the row maximum (greedy rows)
   int32_t* nacc;  // [B]
   double* rsum;   // [B][C] residual (or bonus p) chunk sums
   double* qsum;   // [B][C] p chunk sums for the empty-residual fallback
@@ -381,10 +399,14 @@ static VerifyWs carve(void* base, int B, int K, int V, size_t* total) {
   off = align256(off + R * C * sizeof(float));
   ws.psum = reinterpret_cast<double*>(p + off);
   off = align256(off + R * C * sizeof(double));
+  ws.parg = reinterpret_cast<int32_t*>(p + off);
+  off = align256(off + R * C * sizeof(int32_t));
   ws.fmax = reinterpret_cast<float*>(p + off);
   off = align256(off + R * sizeof(float));
   ws.fsum = reinterpret_cast<double*>(p + off);
   off = align256(off + R * sizeof(double));
+  ws.farg = reinterpret_cast<int32_t*>(p + off);
+  off = align256(off + R * sizeof(int32_t));
   ws.nacc = reinterpret_cast<int32_t*>(p + off);
   off = align256(off + (size_t)B * sizeof(int32_t));
   ws.rsum = reinterpret_cast<double*>(p + off);
@@ -411,11 +433,15 @@ __device__ __forceinline__ const float* verify_row(const float* tl, const float*
 __global__ __launch_bounds__(kScanThreads) void stats_partial_kernel(const float* __restrict__ tl,
                                                                      const float* __restrict__ dl,
                                                                      int B, int K, int V,
-                                                                     VerifyWs ws) {
+                                                                     VerifyWs ws, Warp wp) {
   __shared__ double red_d[kScanThreads / kWave];
   __shared__ float red_f[kScanThreads / kWave];
+  __shared__ int red_i[kScanThreads / kWave];
   const int C = (V + kChunk - 1) / kChunk;
   const int row = blockIdx.x / C, c = blockIdx.x - row * C;
+  const bool target = row < B * (K + 1);
+  const bool greedy = target ? wp.gt : wp.gd;
+  const double inv = target ? wp.it : wp.id;
   const float* l = verify_row(tl, dl, row, B, K, V);
   const int v0 = c * kChunk + threadIdx.x * kPerThread;
   float x[kPerThread];
@@ -426,10 +452,23 @@ __global__ __launch_bounds__(kScanThreads) void stats_partial_kernel(const float
     m = fmaxf(m, x[i]);
   }
   const float cm = block_max_f32<kScanThreads>(m, red_f);
+  if (greedy) {  // first index of the chunk maximum
+    int first = INT_MAX;
+#pragma unroll
+    for (int i = kPerThread - 1; i >= 0; --i)
+      if (v0 + i < V && x[i] == cm) first = v0 + i;
+    const int cf = block_min_i32<kScanThreads>(first, red_i);
+    if (threadIdx.x == 0) {
+      ws.pmax[(size_t)row * C + c] = cm;
+      ws.psum[(size_t)row * C + c] = 1.0;
+      ws.parg[(size_t)row * C + c] = cf;
+    }
+    return;
+  }
   double s = 0.0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i)
-    if (v0 + i < V) s += exp((double)x[i] - (double)cm);
+    if (v0 + i < V) s += exp(((double)x[i] - (double)cm) * inv);
   const double cs = block_sum_f64<kScanThreads>(s, red_d);
   if (threadIdx.x == 0) {
     ws.pmax[(size_t)row * C + c] = cm;
@@ -439,23 +478,36 @@ __global__ __launch_bounds__(kScanThreads) void stats_partial_kernel(const float
 
 __global__ __launch_bounds__(kWave) void verify_accept_kernel(
     const float* __restrict__ tl, const float* __restrict__ dl, const int32_t* __restrict__ tokens,
-    const float* __restrict__ u_accept, int B, int K, int V, VerifyWs ws) {
+    const float* __restrict__ u_accept, int B, int K, int V, VerifyWs ws, Warp wp) {
   __shared__ float smax[2 * 64 + 1];
   __shared__ double ssum[2 * 64 + 1];
+  __shared__ int sarg[2 * 64 + 1];
   const int b = blockIdx.x, lane = threadIdx.x;
   const int C = (V + kChunk - 1) / kChunk;
   // local index i: 0..K target rows, K+1..2K draft rows
   for (int i = lane; i < 2 * K + 1; i += kWave) {
     const int row = i <= K ? b * (K + 1) + i : B * (K + 1) + b * K + (i - K - 1);
+    const bool greedy = i <= K ? wp.gt : wp.gd;
+    const double inv = i <= K ? wp.it : wp.id;
     float M = -INFINITY;
     for (int c = 0; c < C; ++c) M = fmaxf(M, ws.pmax[(size_t)row * C + c]);
     double S = 0.0;
-    for (int c = 0; c < C; ++c)
-      S += ws.psum[(size_t)row * C + c] * exp((double)ws.pmax[(size_t)row * C + c] - (double)M);
+    int arg = -1;
+    if (greedy) {  // the first chunk holding the maximum has the first index
+      S = 1.0;
+      for (int c = C - 1; c >= 0; --c)
+        if (ws.pmax[(size_t)row * C + c] == M) arg = ws.parg[(size_t)row * C + c];
+    } else {
+      for (int c = 0; c < C; ++c)
+        S += ws.psum[(size_t)row * C + c] *
+             exp(((double)ws.pmax[(size_t)row * C + c] - (double)M) * inv);
+    }
     ws.fmax[row] = M;
     ws.fsum[row] = S;
+    ws.farg[row] = arg;
     smax[i] = M;
     ssum[i] = S;
+    sarg[i] = arg;
   }
   __syncthreads();
   bool acc = false;
@@ -463,9 +515,13 @@ __global__ __launch_bounds__(kWave) void verify_accept_kernel(
     const int x = tokens[(size_t)b * K + lane];
     if (x >= 0 && x < V) {
       const int trow = b * (K + 1) + lane, drow = b * K + lane;
-      const double pp = exp((double)tl[(size_t)trow * V + x] - (double)smax[lane]) / ssum[lane];
+      const double pp = wp.gt ? (x == sarg[lane] ? 1.0 : 0.0)
+                              : exp(((double)tl[(size_t)trow * V + x] - (double)smax[lane]) * wp.it) /
+                                    ssum[lane];
       const double qq =
-          exp((double)dl[(size_t)drow * V + x] - (double)smax[K + 1 + lane]) / ssum[K + 1 + lane];
+          wp.gd ? (x == sarg[K + 1 + lane] ? 1.0 : 0.0)
+                : exp(((double)dl[(size_t)drow * V + x] - (double)smax[K + 1 + lane]) * wp.id) /
+                      ssum[K + 1 + lane];
       acc = accept_decision(pp, qq, u_accept[(size_t)b * K + lane]);
     }
   }
@@ -475,17 +531,21 @@ __global__ __launch_bounds__(kWave) void verify_accept_kernel(
 
 __device__ __forceinline__ LogitWeights verify_weights(const float* tl, const float* dl, int b,
                                                        int n, int B, int K, int V,
-                                                       const VerifyWs& ws, bool with_q) {
+                                                       const VerifyWs& ws, bool with_q,
+                                                       const Warp& wp) {
   const int trow = b * (K + 1) + n;
   LogitWeights w;
   w.lp = tl + (size_t)trow * V;
   w.mp = ws.fmax[trow];
   w.sp = ws.fsum[trow];
+  w.ip = wp.it;
+  w.iq = wp.id;
   if (with_q && n < K) {
     const int drow = B * (K + 1) + b * K + n;
     w.lq = dl + (size_t)(b * K + n) * V;
     w.mq = ws.fmax[drow];
     w.sq = ws.fsum[drow];
+    w.qarg = wp.gd ? ws.farg[drow] : -1;
   } else {
     w.lq = nullptr;
     w.mq = 0.0;
@@ -495,22 +555,26 @@ __device__ __forceinline__ LogitWeights verify_weights(const float* tl, const fl
 }
 
 __global__ __launch_bounds__(kScanThreads) void resid_partial_kernel(
-    const float* __restrict__ tl, const float* __restrict__ dl, int B, int K, int V, VerifyWs ws) {
+    const float* __restrict__ tl, const float* __restrict__ dl, int B, int K, int V, VerifyWs ws,
+    Warp wp) {
   __shared__ double red_d[kScanThreads / kWave];
+  if (wp.gt) return;  // greedy target: the round ends with the row's argmax, no draw
   const int C = (V + kChunk - 1) / kChunk;
   const int b = blockIdx.x / C, c = blockIdx.x - b * C;
   const int n = ws.nacc[b];
-  const LogitWeights w = verify_weights(tl, dl, b, n, B, K, V, ws, true);
+  const LogitWeights w = verify_weights(tl, dl, b, n, B, K, V, ws, true, wp);
   const int v0 = c * kChunk + threadIdx.x * kPerThread;
   double tr = 0.0, tp = 0.0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int v = v0 + i;
     if (v < V) {
-      const double pv = exp((double)w.lp[v] - w.mp) / w.sp;
+      const double pv = exp(((double)w.lp[v] - w.mp) * w.ip) / w.sp;
       tp += pv;
       if (w.lq) {
-        const double r = pv - exp((double)w.lq[v] - w.mq) / w.sq;
+        const double qv = w.qarg >= 0 ? (v == w.qarg ? 1.0 : 0.0)
+                                      : exp(((double)w.lq[v] - w.mq) * w.iq) / w.sq;
+        const double r = pv - qv;
         tr += r > 0.0 ? r : 0.0;
       }
     }
@@ -527,7 +591,7 @@ __global__ __launch_bounds__(kScanThreads) void resid_partial_kernel(
 __global__ __launch_bounds__(kScanThreads) void verify_draw_kernel(
     const float* __restrict__ tl, const float* __restrict__ dl, const int32_t* __restrict__ tokens,
     const float* __restrict__ u_sample, int B, int K, int V, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ n_emitted, VerifyWs ws) {
+    int32_t* __restrict__ n_emitted, VerifyWs ws, Warp wp) {
   __shared__ double red_d[kScanThreads / kWave];
   __shared__ int red_i[2 * kScanThreads / kWave];
   __shared__ double s_base, s_T;
@@ -535,7 +599,14 @@ __global__ __launch_bounds__(kScanThreads) void verify_draw_kernel(
   const int b = blockIdx.x;
   const int C = (V + kChunk - 1) / kChunk;
   const int n = ws.nacc[b];
-  if (threadIdx.x == 0) {
+  if (wp.gt) {
+    // greedy target: the rejected slot (or the bonus slot) gets the row's
+    // argmax; the residual of a one-hot p is one-hot at the same token
+    if (threadIdx.x == 0) {
+      s_chunk = -2;
+      s_use_p = 0;
+    }
+  } else if (threadIdx.x == 0) {
     const double* rs = ws.rsum + (size_t)b * C;
     const double* ps = ws.qsum + (size_t)b * C;
     double Z = 0.0;
@@ -563,8 +634,10 @@ __global__ __launch_bounds__(kScanThreads) void verify_draw_kernel(
   __syncthreads();
   const int chunk = s_chunk;
   int y = -1;
-  if (chunk >= 0) {
-    const LogitWeights w = verify_weights(tl, dl, b, n, B, K, V, ws, !s_use_p);
+  if (chunk == -2) {
+    y = ws.farg[b * (K + 1) + n];
+  } else if (chunk >= 0) {
+    const LogitWeights w = verify_weights(tl, dl, b, n, B, K, V, ws, !s_use_p, wp);
     y = chunk_draw(w, chunk, V, s_base, s_T, red_d, red_i);
   }
   for (int j = threadIdx.x; j < K + 1; j += kScanThreads) {
@@ -581,18 +654,23 @@ __global__ __launch_bounds__(kScanThreads) void verify_draw_kernel(
 hipError_t launch_verify_sampling(const float* tl, const float* dl, const int32_t* tokens,
                                   const float* u_accept, const float* u_sample, int B, int K, int V,
                                   int32_t* out_tokens, int32_t* n_emitted, void* workspace,
-                                  hipStream_t s) {
+                                  float t_target, float t_draft, hipStream_t s) {
   const VerifyWs ws = carve(workspace, B, K, V, nullptr);
   const int C = (V + kChunk - 1) / kChunk;
   const int R = B * (2 * K + 1);
+  Warp wp;
+  wp.gt = t_target == 0.0f;
+  wp.gd = t_draft == 0.0f;
+  wp.it = wp.gt ? 0.0 : 1.0 / (double)t_target;
+  wp.id = wp.gd ? 0.0 : 1.0 / (double)t_draft;
   hipLaunchKernelGGL(stats_partial_kernel, dim3(R * C), dim3(kScanThreads), 0, s, tl, dl, B, K, V,
-                     ws);
+                     ws, wp);
   hipLaunchKernelGGL(verify_accept_kernel, dim3(B), dim3(kWave), 0, s, tl, dl, tokens, u_accept,
-                     B, K, V, ws);
+                     B, K, V, ws, wp);
   hipLaunchKernelGGL(resid_partial_kernel, dim3(B * C), dim3(kScanThreads), 0, s, tl, dl, B, K, V,
-                     ws);
+                     ws, wp);
   hipLaunchKernelGGL(verify_draw_kernel, dim3(B), dim3(kScanThreads), 0, s, tl, dl, tokens,
-                     u_sample, B, K, V, out_tokens, n_emitted, ws);
+                     u_sample, B, K, V, out_tokens, n_emitted, ws, wp);
   return hipGetLastError();
 }
 

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(sv.lib, n), n
 
@@ -33,7 +33,7 @@ def test_binding_covers_exactly_the_header(sv):
 
 
 def test_version_and_status_strings(sv):
-    assert sv.abi_version() == 1
+    assert sv.abi_version() == 2
     for code, name in [(0, b"SPEC_OK"), (-1, b"SPEC_ERR_INVALID_ARGUMENT"),
                        (-2, b"SPEC_ERR_ALIGNMENT"), (-3, b"SPEC_ERR_UNSUPPORTED"),
                        (-4, b"SPEC_ERR_WORKSPACE"), (-5, b"SPEC_ERR_HIP")]:
@@ -118,6 +118,21 @@ def test_verify_rejects(sv):
     assert _verify(sv, B=1 << 20, K=64, V=1 << 20) == -1     # grid bound
     assert _verify(sv, wsb=100) == -4
     assert _verify(sv, ws=A + 16) == -4
+
+
+def test_verify_warped_rejects(sv):
+    wsb = sv.lib.spec_verify_workspace_bytes(1, 4, 1000)
+
+    def call(t_t, t_d, **kw):
+        args = dict(hidden=None, lm=None, tl=A, ws=A, wsb=wsb)
+        args.update(kw)
+        return sv.lib.spec_verify_warped(args["hidden"], args["lm"], 0, args["tl"], A, A, A, A,
+                                         1, 4, 1000, t_t, t_d, A, A, args["ws"], args["wsb"], None)
+    for t_t, t_d in ((-1.0, 1.0), (1.0, -0.5), (float("inf"), 1.0), (1.0, float("nan"))):
+        assert call(t_t, t_d) == -1
+        assert b"temperature" in sv.lib.spec_last_error()
+    assert call(0.0, 1.0, tl=None) == -1       # other checks still apply
+    assert call(0.7, 0.0, wsb=100) == -4
 
 
 def test_chain_rejects(sv):
