@@ -13,6 +13,9 @@ What it computes, and where the pages define it:
   weight-streaming pass of the target ("Speculative Decoding: Guess Several
   Tokens, Check Them in One Pass", Step 1; "What Actually Happens During
   Speculative Decoding in LLMs", the 5-candidate pass).
+* ``linear_w8`` -- the same pass with FP8 E4M3 weights and a per-row scale
+  (weight-only 8-bit storage, "Speculative Decoding: The Algebra and the
+  Proof", Where it breaks).
 * ``softmax_rows`` -- p and q from logits ("Speculative Decoding: Two Models,
   One Voice", Implementing it against a real model).
 * ``speculative`` -- the accept test min(1, p/q), the first rejection, the
@@ -29,7 +32,7 @@ inverse-CDF sampling -- is "parity unpinned": only the law of the sampled
 token is pinned, the id map is a convention shared with the GPU path.
 """
 
-from .linear import bf16_to_f64, linear
+from .linear import bf16_to_f64, e4m3_to_f64, linear, linear_w8
 from .softmax import softmax_rows
 from .speculative import (
     TIE_BAND,
@@ -52,7 +55,7 @@ from .speculative import (
 
 __all__ = [
     "TIE_BAND", "accept_batch", "sample_batch", "sample_row", "verify_batch_probs",
-    "bf16_to_f64", "linear", "softmax_rows", "acceptance_rate", "accept_test",
+    "bf16_to_f64", "e4m3_to_f64", "linear", "linear_w8", "softmax_rows", "acceptance_rate", "accept_test",
     "emitted_law", "expected_tokens", "expected_tokens_general",
     "first_rejection", "inverse_cdf", "residual_weights", "total_variation",
     "verify_batch", "verify_round",

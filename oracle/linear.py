@@ -10,6 +10,12 @@ a [5 x d] matrix multiplied against the weights instead of a [1 x d] vector;
 Inputs are bfloat16 bit patterns (uint16). Widening bf16 -> fp64 is exact and
 every bf16*bf16 product is exact in fp64, so the only error is the fp64
 summation (relative error below d_in * 2^-53).
+
+``linear_w8`` is the same product with weight-only 8-bit storage: the
+weights are FP8 E4M3 codes with one float32 scale per output row, the
+activations stay bf16 ("Speculative Decoding: The Algebra and the Proof",
+Where it breaks: weight-only 8-bit storage with BF16 compute halves the bytes
+per weight and so doubles the verify pass's FLOPs per byte).
 """
 
 import numpy as np
@@ -48,4 +54,47 @@ def linear(x_bits, w_bits, block_bytes=64 << 20):
     for n0 in range(0, d_out, rows):
         w = bf16_to_f64(w_bits[n0:n0 + rows])
         y[:, n0:n0 + rows] = x @ w.T
+    return y
+
+
+def e4m3_to_f64(codes):
+    """Exact value of FP8 E4M3 codes (uint8), as float64.
+
+    The OCP 8-bit floating-point format E4M3: one sign bit, a 4-bit exponent
+    with bias 7, a 3-bit mantissa. Exponent field 0 holds the subnormals
+    (m / 8) * 2^-6; otherwise the value is (1 + m / 8) * 2^(e - 7). The
+    format has no infinities: S.1111.111 is NaN, so the largest finite
+    magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def linear_w8(x_bits, w_codes, w_scale, block_bytes=64 << 20):
+    """y[m][n] = w_scale[n] * sum_k x[m][k] * e4m3(w[n][k]) in float64.
+
+    x_bits: uint16 [M][d_in] bf16 activations.
+    w_codes: uint8 [d_out][d_in] FP8 E4M3 weight codes (nn.Linear layout).
+    w_scale: float32 [d_out], the dequantisation scale of each output row.
+    Returns float64 [M][d_out]. Blocked over rows of w like ``linear``.
+    """
+    x_bits = np.asarray(x_bits)
+    w_codes = np.asarray(w_codes)
+    w_scale = np.asarray(w_scale, dtype=np.float32)
+    if x_bits.ndim != 2 or w_codes.ndim != 2 or x_bits.shape[1] != w_codes.shape[1]:
+        raise ValueError(f"shape mismatch: x {x_bits.shape}, w {w_codes.shape}")
+    if w_scale.shape != (w_codes.shape[0],):
+        raise ValueError(f"w_scale shape {w_scale.shape}, expected ({w_codes.shape[0]},)")
+    x = bf16_to_f64(x_bits)
+    m, d_in = x.shape
+    d_out = w_codes.shape[0]
+    y = np.empty((m, d_out), dtype=np.float64)
+    rows = max(1, block_bytes // (8 * max(d_in, 1)))
+    for n0 in range(0, d_out, rows):
+        w = e4m3_to_f64(w_codes[n0:n0 + rows])
+        y[:, n0:n0 + rows] = (x @ w.T) * w_scale[n0:n0 + rows].astype(np.float64)
     return y

@@ -116,6 +116,29 @@ WEIGHT_STD = 0.02
 # Draft model stand-in
 # --------------------------------------------------------------------------
 
+# Weight-only 8-bit storage: FP8 E4M3 codes with one float32 scale per output
+# row. Codes are N(0, W8_CODE_STD^2) draws rounded to the format, and the
+# scales bring the dequantised weights to about N(0, WEIGHT_STD^2), with a
+# seeded spread across rows.
+W8_CODE_STD = 64.0
+
+
+def e4m3_normal_codes(seed, name, shape, std=W8_CODE_STD):
+    """uint8 FP8 E4M3 codes of N(0, std^2) draws, clamped to the finite range
+    [-448, 448] and rounded to the format by torch's float8_e4m3fn cast."""
+    import torch
+    z = normals(seed, name, shape, std)
+    np.clip(z, -448.0, 448.0, out=z)
+    return torch.from_numpy(z).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def w8_row_scales(seed, name, d_out):
+    """float32 [d_out]: WEIGHT_STD / W8_CODE_STD * (0.75 + 0.5 u), u uniform."""
+    u = uniforms(seed, name, (d_out,))
+    base = np.float32(WEIGHT_STD / W8_CODE_STD)
+    return (base * (np.float32(0.75) + np.float32(0.5) * u)).astype(np.float32)
+
+
 def gumbel_max_tokens(draft_logits, seed, name="draft_tokens"):
     """One draw per draft row from softmax(draft logits) by the Gumbel-max
     trick: argmax_v (l_v + g_v) with g_v = -log(-log U_v) i.i.d. Gumbel.

@@ -26,6 +26,23 @@ def normal_bf16(shape, std, seed, device="cuda"):
     return out
 
 
+def e4m3_normal_codes(shape, std, seed, device="cuda"):
+    """uint8 FP8 E4M3 codes of N(0, std^2) draws clamped to [-448, 448]."""
+    z = torch.randn(shape, generator=generator(seed, device), device=device, dtype=torch.float32)
+    if std != 1.0:
+        z.mul_(std)
+    z.clamp_(-448.0, 448.0)
+    out = z.to(torch.float8_e4m3fn).view(torch.uint8)
+    del z
+    return out
+
+
+def w8_row_scales(d_out, base, seed, device="cuda"):
+    """float32 [d_out]: base * (0.75 + 0.5 u), u uniform."""
+    u = torch.rand((d_out,), generator=generator(seed, device), device=device, dtype=torch.float32)
+    return (u.mul_(0.5).add_(0.75)).mul_(base)
+
+
 def normal_f32(shape, std, seed, device="cuda"):
     z = torch.randn(shape, generator=generator(seed, device), device=device, dtype=torch.float32)
     if std != 1.0:

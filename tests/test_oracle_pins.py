@@ -88,6 +88,82 @@ def test_linear_rejects_mismatched_shapes():
 
 
 # ---------------------------------------------------------------------------
+# FP8 E4M3 weights (weight-only 8-bit storage)
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_format_values():
+    # OCP FP8 E4M3: bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN.
+    codes = [0x38, 0xB8, 0x00, 0x80, 0x7E, 0xFE, 0x08, 0x07, 0x01, 0x3C, 0x40, 0x77, 0x30]
+    want = [1.0, -1.0, 0.0, -0.0, 448.0, -448.0, 2.0 ** -6, 7 * 2.0 ** -9, 2.0 ** -9, 1.5, 2.0,
+            240.0, 0.5]
+    got = oracle.e4m3_to_f64(np.array(codes, dtype=np.uint8))
+    for g, w in zip(got, want):
+        assert g == w and math.copysign(1, g) == math.copysign(1, w)
+    v = oracle.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    assert np.flatnonzero(np.isnan(v)).tolist() == [0x7F, 0xFF]
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)                       # codes 0x00..0x7E ascend
+    assert np.array_equal(v[0x80:0xFF], -pos)             # the sign bit only negates
+
+
+def test_e4m3_decode_matches_torch_float8():
+    import torch
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    v = oracle.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    nan = np.isnan(v)
+    assert np.array_equal(nan, np.isnan(t)) and np.array_equal(v[~nan], t[~nan])
+
+
+def test_linear_w8_one_hot_activation_selects_scaled_weight_column():
+    rng = np.random.default_rng(12)
+    M, d_in, d_out = 6, 64, 37
+    w = synth.e4m3_normal_codes(12, "pin.w8", (d_out, d_in))
+    s = synth.w8_row_scales(12, "pin.s8", d_out)
+    x = _one_bits((M, d_in))
+    cols = rng.integers(0, d_in, M)
+    x[np.arange(M), cols] = 0x3F80
+    y = oracle.linear_w8(x, w, s)
+    want = oracle.e4m3_to_f64(w)[:, cols].T * s.astype(np.float64)[None, :]
+    assert np.array_equal(y, want)
+
+
+def test_linear_w8_matches_exact_rational_sum():
+    # E4M3 and bf16 values are dyadic rationals: the exact result is a
+    # Fraction; fp64 lies within (d_in + 1) * 2^-53 * scale * sum|x||w|.
+    M, d_in, d_out = 3, 56, 9
+    x = synth.bf16_normal_bits(13, "pin.x8", (M, d_in))
+    w = synth.e4m3_normal_codes(13, "pin.w8b", (d_out, d_in))
+    s = synth.w8_row_scales(13, "pin.s8b", d_out)
+    y = oracle.linear_w8(x, w, s, block_bytes=8 * d_in * 4)  # ragged row blocks
+    xf = oracle.bf16_to_f64(x)
+    wf = oracle.e4m3_to_f64(w)
+    for m in range(M):
+        for n in range(d_out):
+            exact = Fraction(float(s[n])) * sum(
+                Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xf[m], wf[n]))
+            bound = (d_in + 1) * 2.0 ** -53 * float(s[n]) * float(np.abs(xf[m]) @ np.abs(wf[n]))
+            assert abs(Fraction(float(y[m, n])) - exact) <= Fraction(bound)
+
+
+def test_linear_w8_unit_scale_is_the_bf16_linear_of_the_decoded_weights():
+    # every E4M3 value is exact in bf16 (3 mantissa bits, exponents within
+    # range), so with unit scales the product is the bf16 linear of them
+    x = synth.bf16_normal_bits(14, "pin.x8c", (4, 40))
+    w = synth.e4m3_normal_codes(14, "pin.w8c", (21, 40))
+    wb = synth.bf16_bits(oracle.e4m3_to_f64(w).astype(np.float32))
+    assert np.array_equal(oracle.bf16_to_f64(wb), oracle.e4m3_to_f64(w))
+    y = oracle.linear_w8(x, w, np.ones(21, np.float32))
+    assert np.array_equal(y, oracle.linear(x, wb))
+
+
+def test_linear_w8_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        oracle.linear_w8(np.zeros((2, 8), np.uint16), np.zeros((3, 16), np.uint8), np.ones(3))
+    with pytest.raises(ValueError):
+        oracle.linear_w8(np.zeros((2, 8), np.uint16), np.zeros((3, 8), np.uint8), np.ones(4))
+
+
+# ---------------------------------------------------------------------------
 # Softmax
 # ---------------------------------------------------------------------------
 
