@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 2
+#define SPEC_ABI_VERSION 3
 
 /* Status codes. */
 #define SPEC_OK 0
@@ -146,6 +146,58 @@ int spec_chain_prepare(const spec_linear* linears, int n, int M, void* workspace
  * be ordered (same stream).
  */
 int spec_verify_gemm_chain(int n, int M, void* workspace, void* stream);
+
+/*
+ * Weight-only 8-bit storage (FP8 weights, bf16 activations and compute):
+ * half the bytes per weight, so the weight-streaming verify pass moves half
+ * as much and its FLOPs per byte double ("Speculative Decoding: The Algebra
+ * and the Proof", Where it breaks). Each weight is an FP8 E4M3 code (OCP
+ * 8-bit floating point: 1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; no infinities; 0x7F and 0xFF are NaN; largest finite 448), and each
+ * output row n has one float32 scale:
+ *
+ *   y[m][n] = w_scale[n] * sum_k x[m][k] * e4m3(w[n][k])
+ *
+ * E4M3 values are exact in bf16, products are exact in fp32, and the sum is
+ * accumulated in fp32 like spec_verify_gemm's; the scale multiplies the sum.
+ *
+ * spec_verify_gemm_w8 -- one linear.
+ *   x        device, bf16 [M][d_in], 16-byte aligned.
+ *   w        device, uint8 E4M3 codes [d_out][d_in], 16-byte aligned.
+ *   w_scale  device, float32 [d_out], 4-byte aligned.
+ *   y        device, [M][d_out] of y_dtype.
+ *   d_in     multiple of 16, in [16, 2^20]; d_out in [1, 2^24].
+ *   M        1..16: the weight-streaming regime, where halving the bytes
+ *            halves the time. M > 16 returns SPEC_ERR_UNSUPPORTED.
+ * Errors as spec_verify_gemm. Nothing is allocated; the call is
+ * asynchronous on `stream`.
+ */
+int spec_verify_gemm_w8(const uint16_t* x, const uint8_t* w, const float* w_scale, void* y,
+                        int y_dtype, int M, int d_in, int d_out, void* stream);
+
+/* One linear of an FP8-weight chain: spec_linear with w_scale. */
+typedef struct spec_linear_w8 {
+  const uint16_t* x;
+  const uint8_t* w;
+  const float* w_scale;
+  void* y;
+  int32_t d_in;
+  int32_t d_out;
+  int32_t y_dtype;
+  int32_t reserved;
+} spec_linear_w8;
+
+/*
+ * spec_chain_prepare_w8 / spec_verify_gemm_chain_w8 -- spec_chain_prepare
+ * and spec_verify_gemm_chain for a chain whose every linear has FP8 E4M3
+ * weights (each checked as spec_verify_gemm_w8 checks its arguments). The
+ * workspace is sized by spec_chain_workspace_bytes(n) as for a bf16 chain; a
+ * workspace prepared by one kind of prepare call run by the other kind of
+ * chain call computes nothing and sets bit 1 of spec_chain_error.
+ */
+int spec_chain_prepare_w8(const spec_linear_w8* linears, int n, int M, void* workspace,
+                          size_t workspace_bytes);
+int spec_verify_gemm_chain_w8(int n, int M, void* workspace, void* stream);
 
 /*
  * spec_chain_error -- read and clear the device-side error word of a chain

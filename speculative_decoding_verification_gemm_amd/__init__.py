@@ -55,6 +55,9 @@ SIGNATURES = {
     "spec_chain_workspace_bytes": (_z, [_i]),
     "spec_chain_prepare": (_i, [_p, _i, _i, _p, _z]),
     "spec_verify_gemm_chain": (_i, [_i, _i, _p, _p]),
+    "spec_verify_gemm_w8": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _p]),
+    "spec_chain_prepare_w8": (_i, [_p, _i, _i, _p, _z]),
+    "spec_verify_gemm_chain_w8": (_i, [_i, _i, _p, _p]),
     "spec_chain_error": (_i, [_p, ctypes.POINTER(ctypes.c_int)]),
     "spec_verify": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _z, _p]),
     "spec_verify_warped": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _f, _f, _p, _p, _p,
@@ -70,6 +73,13 @@ class SpecLinear(ctypes.Structure):
     """spec_linear of include/spec_verify.h."""
     _fields_ = [("x", ctypes.c_void_p), ("w", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("y_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class SpecLinearW8(ctypes.Structure):
+    """spec_linear_w8 of include/spec_verify.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("w", ctypes.c_void_p), ("w_scale", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
                 ("y_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
@@ -140,6 +150,33 @@ def verify_gemm(x, w, out=None, out_dtype=None):
     if code is None:
         raise TypeError("out must be float32 or bfloat16")
     check(lib.spec_verify_gemm(_ptr(x), _ptr(w), _ptr(out), code, M, d_in, d_out, _stream()))
+    return out
+
+
+def verify_gemm_w8(x, w, w_scale, out=None, out_dtype=None):
+    """y[m][n] = w_scale[n] * sum_k x[m][k] * e4m3(w[n][k]) (weight-only FP8).
+
+    x bf16 [M][d_in]; w uint8 FP8 E4M3 codes [d_out][d_in]; w_scale float32
+    [d_out]; out_dtype torch.float32 (default) or torch.bfloat16."""
+    torch = _torch()
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w, torch.uint8, "w", 2)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, d_in = x.shape
+    d_out = w.shape[0]
+    if w.shape[1] != d_in or w_scale.shape[0] != d_out:
+        raise ValueError(f"x {tuple(x.shape)}, w {tuple(w.shape)}, w_scale "
+                         f"{tuple(w_scale.shape)} disagree")
+    if out is None:
+        out = torch.empty((M, d_out), dtype=out_dtype or torch.float32, device=x.device)
+    _need(out, out.dtype, "out", 2)
+    if tuple(out.shape) != (M, d_out):
+        raise ValueError(f"out must be {(M, d_out)}, got {tuple(out.shape)}")
+    code = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16}.get(out.dtype)
+    if code is None:
+        raise TypeError("out must be float32 or bfloat16")
+    check(lib.spec_verify_gemm_w8(_ptr(x), _ptr(w), _ptr(w_scale), _ptr(out), code, M, d_in,
+                                  d_out, _stream()))
     return out
 
 
@@ -256,18 +293,23 @@ class Chain:
     """A prepared chain of linears (spec_chain_prepare) and its workspace.
 
     linears: list of (x, w, y) device tensors, x bf16 [M][d_in], w bf16
-    [d_out][d_in], y fp32 or bf16 [M][d_out]. The tensors must stay alive
-    while the chain is used."""
+    [d_out][d_in], y fp32 or bf16 [M][d_out]; or, for a chain of FP8-weight
+    linears, (x, w, w_scale, y) with w uint8 E4M3 codes and w_scale float32
+    [d_out]. The tensors must stay alive while the chain is used."""
 
     def __init__(self, linears, device="cuda"):
         torch = _torch()
         if not linears:
             raise ValueError("empty chain")
         M = linears[0][0].shape[0]
-        descs = (SpecLinear * len(linears))()
-        for i, (x, w, y) in enumerate(linears):
+        self.w8 = len(linears[0]) == 4
+        descs = ((SpecLinearW8 if self.w8 else SpecLinear) * len(linears))()
+        for i, lin in enumerate(linears):
+            if len(lin) != (4 if self.w8 else 3):
+                raise ValueError("a chain is all bf16 (x, w, y) or all FP8 (x, w, w_scale, y)")
+            x, w, y = lin[0], lin[1], lin[-1]
             _need(x, torch.bfloat16, f"x[{i}]", 2)
-            _need(w, torch.bfloat16, f"w[{i}]", 2)
+            _need(w, torch.uint8 if self.w8 else torch.bfloat16, f"w[{i}]", 2)
             _need(y, y.dtype, f"y[{i}]", 2)
             code = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16}.get(y.dtype)
             if code is None:
@@ -275,8 +317,15 @@ class Chain:
             if x.shape[0] != M or tuple(y.shape) != (M, w.shape[0]) or x.shape[1] != w.shape[1]:
                 raise ValueError(f"linear {i}: shapes x {tuple(x.shape)}, w {tuple(w.shape)}, "
                                  f"y {tuple(y.shape)} disagree")
-            descs[i] = SpecLinear(x.data_ptr(), w.data_ptr(), y.data_ptr(), x.shape[1],
-                                  w.shape[0], code, 0)
+            if self.w8:
+                _need(lin[2], torch.float32, f"w_scale[{i}]", 1)
+                if lin[2].shape[0] != w.shape[0]:
+                    raise ValueError(f"linear {i}: w_scale has {lin[2].shape[0]} entries")
+                descs[i] = SpecLinearW8(x.data_ptr(), w.data_ptr(), lin[2].data_ptr(),
+                                        y.data_ptr(), x.shape[1], w.shape[0], code, 0)
+            else:
+                descs[i] = SpecLinear(x.data_ptr(), w.data_ptr(), y.data_ptr(), x.shape[1],
+                                      w.shape[0], code, 0)
         self.n, self.M = len(linears), M
         self.keep = list(linears)
         nbytes = lib.spec_chain_workspace_bytes(self.n)
@@ -284,10 +333,12 @@ class Chain:
             raise ValueError(f"chain of {self.n} linears is out of range")
         self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         torch.cuda.synchronize()
-        check(lib.spec_chain_prepare(descs, self.n, self.M, _ptr(self.workspace), nbytes))
+        prepare = lib.spec_chain_prepare_w8 if self.w8 else lib.spec_chain_prepare
+        check(prepare(descs, self.n, self.M, _ptr(self.workspace), nbytes))
 
     def run(self):
-        check(lib.spec_verify_gemm_chain(self.n, self.M, _ptr(self.workspace), _stream()))
+        run = lib.spec_verify_gemm_chain_w8 if self.w8 else lib.spec_verify_gemm_chain
+        check(run(self.n, self.M, _ptr(self.workspace), _stream()))
 
     def error(self):
         """Read and clear the device-side error word (synchronous)."""

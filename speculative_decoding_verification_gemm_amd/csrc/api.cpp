@@ -61,12 +61,12 @@ int check_device(int* cus = nullptr) {
 // Resident workgroups per CU for the streaming kernel: the occupancy limit,
 // capped at 2 (measured best for the Llama-shaped linears); the
 // SPECV_STREAM_WGS_PER_CU environment variable overrides the cap.
-std::atomic<int> g_stream_occ[17];
-int stream_wgs_per_cu(int M) {
-  int occ = g_stream_occ[M].load(std::memory_order_relaxed);
+std::atomic<int> g_stream_occ[2][17];
+int stream_wgs_per_cu(int M, bool w8 = false) {
+  int occ = g_stream_occ[w8][M].load(std::memory_order_relaxed);
   if (occ == 0) {
-    occ = specv::stream_max_wgs_per_cu(M);
-    g_stream_occ[M].store(occ, std::memory_order_relaxed);
+    occ = specv::stream_max_wgs_per_cu(M, w8);
+    g_stream_occ[w8][M].store(occ, std::memory_order_relaxed);
   }
   int cap = 2;
   if (const char* env = getenv("SPECV_STREAM_WGS_PER_CU")) {
@@ -109,6 +109,23 @@ int check_gemm_args(const uint16_t* x, const uint16_t* w, const void* y, int y_d
   return SPEC_OK;
 }
 
+// FP8 weights: as check_gemm_args, plus the scale vector, d_in a multiple of
+// 16 (one 16-byte load holds 16 weights) and M within the streaming kernel.
+int check_gemm_w8_args(const uint16_t* x, const uint8_t* w, const float* w_scale, const void* y,
+                       int y_dtype, int M, int d_in, int d_out) {
+  if (!w_scale) return fail(SPEC_ERR_INVALID_ARGUMENT, "null w_scale");
+  int rc = check_gemm_args(x, reinterpret_cast<const uint16_t*>(w), y, y_dtype, M, d_in, d_out);
+  if (rc != SPEC_OK) return rc;
+  if (d_in % 16 != 0)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "d_in=%d must be a multiple of 16 for FP8 weights",
+                d_in);
+  if (!aligned(w_scale, 4)) return fail(SPEC_ERR_ALIGNMENT, "w_scale is not 4-byte aligned");
+  if (M > specv::kMaxStreamM)
+    return fail(SPEC_ERR_UNSUPPORTED, "FP8 weights are implemented for M <= %d (got %d)",
+                specv::kMaxStreamM, M);
+  return SPEC_OK;
+}
+
 int check_bkv(int B, int K, int V) {
   if (B < 1 || B > kMaxB) return fail(SPEC_ERR_INVALID_ARGUMENT, "B=%d outside [1, %d]", B, kMaxB);
   if (K < 1 || K > kMaxK) return fail(SPEC_ERR_INVALID_ARGUMENT, "K=%d outside [1, %d]", K, kMaxK);
@@ -120,7 +137,8 @@ int run_gemm(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M
              int d_out, int cus, hipStream_t s) {
   hipError_t e;
   if (M <= specv::kMaxStreamM)
-    e = specv::launch_gemm_stream(x, w, y, out_bf16, M, d_in, d_out, cus * stream_wgs_per_cu(M), s);
+    e = specv::launch_gemm_stream(x, w, nullptr, y, out_bf16, false, M, d_in, d_out,
+                                  cus * stream_wgs_per_cu(M), s);
   else
     e = M <= specv::kMaxSkinnyM ? specv::launch_gemm_skinny(x, w, y, out_bf16, M, d_in, d_out, s)
                                 : specv::launch_gemm_mfma(x, w, y, out_bf16, M, d_in, d_out, s);
@@ -135,6 +153,80 @@ size_t chain_desc_offset(int n) {
 }
 size_t chain_bytes(int n) {
   return (chain_desc_offset(n) + (size_t)n * sizeof(specv::StreamLinear) + 255) & ~(size_t)255;
+}
+
+// Validates the n descriptors (fill(i, &desc) checks linear i and writes its
+// internal descriptor), then uploads header, zeroed counters and
+// descriptors. The header's magic records the weight format.
+template <class Fill>
+int chain_prepare(int n, int M, void* workspace, size_t workspace_bytes, bool w8, Fill&& fill) {
+  if (!workspace) return fail(SPEC_ERR_INVALID_ARGUMENT, "null workspace");
+  if (n < 1 || n > kMaxChain)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "n=%d outside [1, %d]", n, kMaxChain);
+  if (M < 1 || M > specv::kMaxStreamM)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "chain M=%d outside [1, %d]", M, specv::kMaxStreamM);
+  const size_t bytes = chain_bytes(n);
+  char* img = static_cast<char*>(calloc(1, bytes));
+  if (!img) return fail(SPEC_ERR_HIP, "host staging allocation failed");
+  specv::StreamLinear* descs = reinterpret_cast<specv::StreamLinear*>(img + chain_desc_offset(n));
+  for (int i = 0; i < n; ++i) {
+    int rc = fill(i, &descs[i]);
+    if (rc != SPEC_OK) {
+      free(img);
+      char msg[512];
+      snprintf(msg, sizeof(msg), "linear %d: %s", i, g_err);
+      return fail(rc, "%s", msg);
+    }
+  }
+  if (workspace_bytes < bytes) {
+    free(img);
+    return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, bytes);
+  }
+  if (!aligned(workspace, 256)) {
+    free(img);
+    return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  }
+  int rc = check_device();
+  if (rc != SPEC_OK) {
+    free(img);
+    return rc;
+  }
+  specv::ChainSync hdr{};
+  hdr.magic = w8 ? specv::kChainMagicW8 : specv::kChainMagic;
+  hdr.n = n;
+  hdr.M = M;
+  // Diagnostics: SPECV_CHAIN_TRACE=<device address of n * grid * 4 uint64>
+  // records, per linear and workgroup, the wall clock (100 MHz ticks) at
+  // arrival, at the end of the wait for the previous linear, and when the
+  // first activation chunk is staged, and when the last output stores of
+  // the linear have been issued.
+  if (const char* env = getenv("SPECV_CHAIN_TRACE")) {
+    unsigned long long v = strtoull(env, nullptr, 0);
+    hdr.trace = reinterpret_cast<unsigned long long*>(v);
+  }
+  memcpy(img, &hdr, sizeof(hdr));
+  hipError_t e = hipMemcpy(workspace, img, bytes, hipMemcpyHostToDevice);
+  free(img);
+  if (e != hipSuccess) return fail(SPEC_ERR_HIP, "chain upload: %s", hipGetErrorString(e));
+  return SPEC_OK;
+}
+
+int chain_run(int n, int M, void* workspace, bool w8, void* stream) {
+  if (!workspace) return fail(SPEC_ERR_INVALID_ARGUMENT, "null workspace");
+  if (n < 1 || n > kMaxChain)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "n=%d outside [1, %d]", n, kMaxChain);
+  if (M < 1 || M > specv::kMaxStreamM)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "chain M=%d outside [1, %d]", M, specv::kMaxStreamM);
+  if (!aligned(workspace, 256)) return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  int cus = 0;
+  int rc = check_device(&cus);
+  if (rc != SPEC_OK) return rc;
+  char* base = static_cast<char*>(workspace);
+  return launched(specv::launch_gemm_chain(
+                      reinterpret_cast<const specv::StreamLinear*>(base + chain_desc_offset(n)), n,
+                      reinterpret_cast<specv::ChainSync*>(base), M, w8,
+                      cus * stream_wgs_per_cu(M, w8), static_cast<hipStream_t>(stream)),
+                  w8 ? "spec_verify_gemm_chain_w8" : "spec_verify_gemm_chain");
 }
 
 }  // namespace
@@ -176,72 +268,57 @@ size_t spec_chain_workspace_bytes(int n) {
 int spec_chain_prepare(const spec_linear* linears, int n, int M, void* workspace,
                        size_t workspace_bytes) {
   clear_error();
-  if (!linears || !workspace) return fail(SPEC_ERR_INVALID_ARGUMENT, "null linears or workspace");
-  if (n < 1 || n > kMaxChain)
-    return fail(SPEC_ERR_INVALID_ARGUMENT, "n=%d outside [1, %d]", n, kMaxChain);
-  if (M < 1 || M > specv::kMaxStreamM)
-    return fail(SPEC_ERR_INVALID_ARGUMENT, "chain M=%d outside [1, %d]", M, specv::kMaxStreamM);
-  for (int i = 0; i < n; ++i) {
-    const spec_linear& d = linears[i];
-    int rc = check_gemm_args(d.x, d.w, d.y, d.y_dtype, M, d.d_in, d.d_out);
-    if (rc != SPEC_OK) {
-      char msg[512];
-      snprintf(msg, sizeof(msg), "linear %d: %s", i, g_err);
-      return fail(rc, "%s", msg);
-    }
-    if (d.reserved != 0) return fail(SPEC_ERR_INVALID_ARGUMENT, "linear %d: reserved != 0", i);
-  }
-  if (workspace_bytes < chain_bytes(n))
-    return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
-                chain_bytes(n));
-  if (!aligned(workspace, 256)) return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  int rc = check_device();
-  if (rc != SPEC_OK) return rc;
-  // header + zeroed counters + descriptors, assembled on the host
-  const size_t bytes = chain_bytes(n);
-  char* img = static_cast<char*>(calloc(1, bytes));
-  if (!img) return fail(SPEC_ERR_HIP, "host staging allocation failed");
-  specv::ChainSync hdr{};
-  hdr.magic = specv::kChainMagic;
-  hdr.n = n;
-  hdr.M = M;
-  // Diagnostics: SPECV_CHAIN_TRACE=<device address of n * grid * 4 uint64>
-  // records, per linear and workgroup, the wall clock (100 MHz ticks) at
-  // arrival, at the end of the wait for the previous linear, and when the
-  // first activation chunk is staged, and when the last output stores of
-  // the linear have been issued.
-  if (const char* env = getenv("SPECV_CHAIN_TRACE")) {
-    unsigned long long v = strtoull(env, nullptr, 0);
-    hdr.trace = reinterpret_cast<unsigned long long*>(v);
-  }
-  memcpy(img, &hdr, sizeof(hdr));
-  specv::StreamLinear* descs = reinterpret_cast<specv::StreamLinear*>(img + chain_desc_offset(n));
-  for (int i = 0; i < n; ++i)
-    descs[i] = specv::StreamLinear{linears[i].x, linears[i].w, linears[i].y, linears[i].d_in,
-                                   linears[i].d_out, linears[i].y_dtype == SPEC_BF16 ? 1 : 0, 0};
-  hipError_t e = hipMemcpy(workspace, img, bytes, hipMemcpyHostToDevice);
-  free(img);
-  if (e != hipSuccess) return fail(SPEC_ERR_HIP, "chain upload: %s", hipGetErrorString(e));
-  return SPEC_OK;
+  if (!linears) return fail(SPEC_ERR_INVALID_ARGUMENT, "null linears");
+  return chain_prepare(n, M, workspace, workspace_bytes, false,
+                       [&](int i, specv::StreamLinear* d) {
+                         const spec_linear& l = linears[i];
+                         int rc = check_gemm_args(l.x, l.w, l.y, l.y_dtype, M, l.d_in, l.d_out);
+                         if (rc == SPEC_OK && l.reserved != 0)
+                           rc = fail(SPEC_ERR_INVALID_ARGUMENT, "reserved != 0");
+                         *d = specv::StreamLinear{l.x, l.w, nullptr, l.y, l.d_in, l.d_out,
+                                                  l.y_dtype == SPEC_BF16 ? 1 : 0, 0};
+                         return rc;
+                       });
+}
+
+int spec_chain_prepare_w8(const spec_linear_w8* linears, int n, int M, void* workspace,
+                          size_t workspace_bytes) {
+  clear_error();
+  if (!linears) return fail(SPEC_ERR_INVALID_ARGUMENT, "null linears");
+  return chain_prepare(n, M, workspace, workspace_bytes, true,
+                       [&](int i, specv::StreamLinear* d) {
+                         const spec_linear_w8& l = linears[i];
+                         int rc = check_gemm_w8_args(l.x, l.w, l.w_scale, l.y, l.y_dtype, M,
+                                                     l.d_in, l.d_out);
+                         if (rc == SPEC_OK && l.reserved != 0)
+                           rc = fail(SPEC_ERR_INVALID_ARGUMENT, "reserved != 0");
+                         *d = specv::StreamLinear{l.x, l.w, l.w_scale, l.y, l.d_in, l.d_out,
+                                                  l.y_dtype == SPEC_BF16 ? 1 : 0, 0};
+                         return rc;
+                       });
 }
 
 int spec_verify_gemm_chain(int n, int M, void* workspace, void* stream) {
   clear_error();
-  if (!workspace) return fail(SPEC_ERR_INVALID_ARGUMENT, "null workspace");
-  if (n < 1 || n > kMaxChain)
-    return fail(SPEC_ERR_INVALID_ARGUMENT, "n=%d outside [1, %d]", n, kMaxChain);
-  if (M < 1 || M > specv::kMaxStreamM)
-    return fail(SPEC_ERR_INVALID_ARGUMENT, "chain M=%d outside [1, %d]", M, specv::kMaxStreamM);
-  if (!aligned(workspace, 256)) return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  int cus = 0;
-  int rc = check_device(&cus);
+  return chain_run(n, M, workspace, false, stream);
+}
+
+int spec_verify_gemm_chain_w8(int n, int M, void* workspace, void* stream) {
+  clear_error();
+  return chain_run(n, M, workspace, true, stream);
+}
+
+int spec_verify_gemm_w8(const uint16_t* x, const uint8_t* w, const float* w_scale, void* y,
+                        int y_dtype, int M, int d_in, int d_out, void* stream) {
+  clear_error();
+  int rc = check_gemm_w8_args(x, w, w_scale, y, y_dtype, M, d_in, d_out);
   if (rc != SPEC_OK) return rc;
-  char* base = static_cast<char*>(workspace);
-  return launched(
-      specv::launch_gemm_chain(reinterpret_cast<const specv::StreamLinear*>(base + chain_desc_offset(n)),
-                               n, reinterpret_cast<specv::ChainSync*>(base), M,
-                               cus * stream_wgs_per_cu(M), static_cast<hipStream_t>(stream)),
-      "spec_verify_gemm_chain");
+  int cus = 0;
+  if ((rc = check_device(&cus)) != SPEC_OK) return rc;
+  return launched(specv::launch_gemm_stream(x, w, w_scale, y, y_dtype == SPEC_BF16, true, M, d_in,
+                                            d_out, cus * stream_wgs_per_cu(M, true),
+                                            static_cast<hipStream_t>(stream)),
+                  "spec_verify_gemm_w8");
 }
 
 int spec_chain_error(void* workspace, int* error) {

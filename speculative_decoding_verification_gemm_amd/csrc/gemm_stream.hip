@@ -18,6 +18,11 @@
 //    row blocks; lanes read it back with 16-byte LDS loads. Chunks are as
 //    large as LDS allows, so most linears stage their activations once.
 //  * Products use v_dot2c_f32_bf16 (two bf16 products per lane-op).
+//  * Weight-only 8-bit storage ("Speculative Decoding: The Algebra and the
+//    Proof", Where it breaks): with FP8 E4M3 weights a 16-byte load holds
+//    16 weights, which v_cvt_scalef32_pk_bf16_fp8 widens exactly to bf16
+//    before the same dot products; the row's scale multiplies the reduced
+//    sum. Half the bytes stream per weight.
 //  * DEPTH register stages of weights are in flight ahead of the compute,
 //    across row-block and linear boundaries, so the next linear's weights
 //    stream while the current one finishes. Weight loads are issued on every
@@ -51,7 +56,16 @@ namespace specv {
 #endif
 constexpr int kStreamWaves = SPECV_STREAM_WAVES;  // one workgroup per CU
 constexpr int kStreamThreads = kStreamWaves * kWave;
-constexpr int kSeg = 128;           // reduction elements per lane group per segment
+// Weight element format: elements per 16-byte load (kEpl), reduction
+// elements per lane group per segment (16 lanes x 16 bytes), bytes per
+// element.
+template <bool W8>
+struct WFmt {
+  static constexpr int kEpl = W8 ? 16 : 8;
+  static constexpr int kEplShift = W8 ? 4 : 3;
+  static constexpr int kSeg = 16 * kEpl;
+  static constexpr int kEsz = W8 ? 1 : 2;
+};
 constexpr int kCachePolicyDevice = 16;  // buffer-load aux bits: sc1 (device scope)
 constexpr int kSpinLimit = 1 << 18;  // well under a second of polling before a barrier gives up
 #ifndef SPECV_POLL_SLEEP
@@ -108,10 +122,19 @@ __device__ __forceinline__ float dot8_bf16(u32x4 a, u32x4 b, float acc) {
   return acc;
 }
 
+// Two FP8 E4M3 weights (the low or high 16 bits of v) as a bf16 pair; every
+// E4M3 value is exact in bf16 (3 mantissa bits, exponents 2^-9 .. 2^8).
+template <bool HI>
+__device__ __forceinline__ uint32_t widen_fp8x2_t(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, HI));
+}
+#define widen_fp8x2(v, hi) widen_fp8x2_t<hi>(v)
+
 // Per-workgroup schedule of one linear.
 struct LinSched {
   const uint16_t* x;
-  const uint16_t* w;
+  const void* w;
+  const float* scale;  // FP8 weights: per-row scales
   void* y;
   int K, N;
   int n_it;    // pipeline stages per row block (ceil(K / elems per stage))
@@ -119,26 +142,30 @@ struct LinSched {
   int my_rb;   // row blocks this workgroup owns (bid, bid + G, ...)
   int kc;      // activation chunk length (multiple of a stage)
   int ipc;     // stages per chunk
+  int xs;      // LDS row stride of the activation chunk, elements (multiple of 512)
   int bf16;
   int ragged_k;
 };
 
-template <int M, int RPL, int U, int KCMAX>
+template <int M, int RPL, int U, int KCMAX, bool W8>
 struct Stream {
   static constexpr int NR = 4 * RPL;              // rows per row block
-  static constexpr int EPI = kStreamWaves * U * kSeg;  // reduction elements per stage
+  static constexpr int EPI = kStreamWaves * U * WFmt<W8>::kSeg;  // reduction elements per stage
   // Activation region rounded up to whole 1 KB blocks: staging writes one
   // 1 KB block (64 lanes x 16 bytes) per wave instruction.
   static constexpr size_t kXBytes = ((size_t)M * KCMAX * 2 + 1023) / 1024 * 1024;
-  static constexpr size_t kRedBytes = (size_t)kStreamWaves * NR * M * 4;
+  // two partial-sum buffers, used by alternate row blocks
+  static constexpr size_t kRedFloats = (size_t)kStreamWaves * NR * M;
+  static constexpr size_t kRedBytes = 2 * kRedFloats * 4;
   static constexpr size_t kLdsBytes = kXBytes + kRedBytes;
-  static_assert(KCMAX % EPI == 0, "chunk must hold whole stages");
+  static_assert(KCMAX % 512 == 0 && KCMAX >= EPI, "LDS rows are whole 64-lane blocks");
   static_assert(EPI % 512 == 0, "a chunk row must be whole 64-lane staging blocks");
 
   __device__ static LinSched sched(const StreamLinear& d) {
     LinSched s;
     s.x = d.x;
     s.w = d.w;
+    s.scale = d.w_scale;
     s.y = d.y;
     s.K = d.K;
     s.N = d.N;
@@ -147,9 +174,20 @@ struct Stream {
     s.n_rb = (d.N + NR - 1) / NR;
     const int bid = blockIdx.x, G = gridDim.x;
     s.my_rb = s.n_rb > bid ? (s.n_rb - bid + G - 1) / G : 0;
-    const int n_chunks = (s.n_it * EPI + KCMAX - 1) / KCMAX;
-    s.ipc = (s.n_it + n_chunks - 1) / n_chunks;
-    s.kc = s.ipc * EPI;
+    if (d.K <= KCMAX) {
+      // the whole reduction dimension is staged once; LDS rows hold K
+      // rounded up to a 512-element block, which may be less than the
+      // stages span (the last stage's elements past K are never read)
+      s.ipc = s.n_it;
+      s.kc = s.n_it * EPI;
+      s.xs = (d.K + 511) / 512 * 512;
+    } else {
+      const int ipc_max = KCMAX / EPI;
+      const int n_chunks = (s.n_it + ipc_max - 1) / ipc_max;
+      s.ipc = (s.n_it + n_chunks - 1) / n_chunks;
+      s.kc = s.ipc * EPI;
+      s.xs = s.kc;
+    }
     s.ragged_k = (d.K % EPI) != 0;
     return s;
   }
@@ -162,21 +200,24 @@ struct Cursor {
   bool valid;
 };
 
-template <int M, int RPL, int U, int KCMAX, int DEPTH>
+template <int M, int RPL, int U, int KCMAX, int DEPTH, bool W8>
 __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinear single,
                                                                      const StreamLinear* chain,
                                                                      int n_lin, ChainSync* sync) {
-  using S = Stream<M, RPL, U, KCMAX>;
+  using S = Stream<M, RPL, U, KCMAX, W8>;
+  using F = WFmt<W8>;
   constexpr int NR = S::NR, EPI = S::EPI;
   extern __shared__ u32x4 lds[];
-  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + S::kXBytes);
+  float* const red_base = reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + S::kXBytes);
+  int red_par = 0;  // partial-sum buffer of the next row block
   __shared__ unsigned s_gen;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, sub = lane & 15;
   const int bid = blockIdx.x, G = gridDim.x;
   const bool is_chain = chain != nullptr;
   unsigned* counts = is_chain ? reinterpret_cast<unsigned*>(sync + 1) : nullptr;
-  if (is_chain && (sync->magic != kChainMagic || sync->n != n_lin || sync->M != M)) {
+  if (is_chain &&
+      (sync->magic != (W8 ? kChainMagicW8 : kChainMagic) || sync->n != n_lin || sync->M != M)) {
     if (bid == 0 && tid == 0)
       __hip_atomic_fetch_or(&sync->error, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;  // every workgroup reads the same header and leaves
@@ -189,7 +230,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
     if (!is_chain) return single;
     const __attribute__((address_space(4))) StreamLinear* d =
         (const __attribute__((address_space(4))) StreamLinear*)(chain + l);
-    return StreamLinear{d->x, d->w, d->y, d->K, d->N, d->out_bf16, d->reserved};
+    return StreamLinear{d->x, d->w, d->w_scale, d->y, d->K, d->N, d->out_bf16, d->reserved};
   };
 
   // ---- barrier between linears (chain mode)
@@ -261,14 +302,14 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
 
   // ---- activation staging: x[:, chunk] straight into LDS (global_load_lds,
   // one 1 KB block per wave instruction, no registers). LDS row m of the
-  // chunk holds s.kc / 8 16-byte units, a whole number of blocks; units past
+  // chunk holds s.xs / 8 16-byte units, a whole number of blocks; units past
   // the end of x load a clamped valid address and are never read. The
   // staging is complete (vmcnt) and visible to all waves (barrier) on
   // return.
   auto stage_x = [&](const LinSched& s, int chunk) __attribute__((always_inline)) {
     const int k0 = chunk * s.kc;
     const int units = min(s.kc, s.K - k0) / 8;  // valid units per row
-    const int blocks = s.kc / 512;              // 64-unit blocks per LDS row
+    const int blocks = s.xs / 512;              // 64-unit blocks per LDS row
     const uint16_t* xs = s.x;
     for (int m = 0; m < M; ++m) {
       for (int b = wave; b < blocks; b += kStreamWaves) {
@@ -286,8 +327,10 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
     __syncthreads();
   };
 
-  // element offset of this lane's 8 values for segment u of stage it
-  auto kofs = [&](int it, int u) __attribute__((always_inline)) { return ((it * U + u) * kStreamWaves + wave) * kSeg + sub * 8; };
+  // element offset of this lane's F::kEpl weights for segment u of stage it
+  auto kofs = [&](int it, int u) __attribute__((always_inline)) {
+    return ((it * U + u) * kStreamWaves + wave) * F::kSeg + sub * F::kEpl;
+  };
 
   // Weight loads are branch-free: rows past N and reduction elements past K
   // read a clamped valid address. Rows past N feed outputs that are never
@@ -303,10 +346,12 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
       const int row = min(rb * NR + grp * RPL + r, s.N - 1);
-      const SPECV_GLOBAL u32x4* base = gptr<u32x4>(s.w + (size_t)row * s.K);
+      const SPECV_GLOBAL u32x4* base =
+          gptr<u32x4>(static_cast<const char*>(s.w) + (size_t)row * s.K * F::kEsz);
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        buf[u][r] = __builtin_nontemporal_load(base + (min(kofs(cur.it, u), s.K - 8) >> 3));
+        buf[u][r] = __builtin_nontemporal_load(
+            base + (min(kofs(cur.it, u), s.K - F::kEpl) >> F::kEplShift));
     }
   };
 
@@ -320,7 +365,47 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
   auto compute = [&](const u32x4 (&buf)[U][RPL], const LinSched& s, const Cursor& cur)
       __attribute__((always_inline)) {
     const int chunk_base = (cur.it / s.ipc) * s.kc;
-    const int row_units = s.kc / 8;
+    const int row_units = s.xs / 8;
+    if constexpr (W8) {
+      // 16 weights per register quad: widen to two bf16 octets (exact), then
+      // two dot products against the matching activation units. On the
+      // ragged last stage, activations past K are zeroed (d_in is a multiple
+      // of 16, so a lane's 16 weights are all inside K or all outside).
+      auto body = [&](auto RAG) __attribute__((always_inline)) {
+        constexpr bool rag = decltype(RAG)::value;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          u32x4 lo[RPL], hi[RPL];
+#pragma unroll
+          for (int r = 0; r < RPL; ++r) {
+            lo[r] = u32x4{widen_fp8x2(buf[u][r].x, false), widen_fp8x2(buf[u][r].x, true),
+                          widen_fp8x2(buf[u][r].y, false), widen_fp8x2(buf[u][r].y, true)};
+            hi[r] = u32x4{widen_fp8x2(buf[u][r].z, false), widen_fp8x2(buf[u][r].z, true),
+                          widen_fp8x2(buf[u][r].w, false), widen_fp8x2(buf[u][r].w, true)};
+          }
+          const int k = kofs(cur.it, u);
+          const bool ok = !rag || k < s.K;
+          const int lu = ok ? (k - chunk_base) >> 3 : 0;
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            u32x4 xa = lds[m * row_units + lu];
+            u32x4 xb = lds[m * row_units + lu + 1];
+            if constexpr (rag) {
+              xa = ok ? xa : u32x4{0u, 0u, 0u, 0u};
+              xb = ok ? xb : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int r = 0; r < RPL; ++r)
+              acc[r][m] = dot8_bf16(hi[r], xb, dot8_bf16(lo[r], xa, acc[r][m]));
+          }
+        }
+      };
+      if (s.ragged_k && cur.it == s.n_it - 1)
+        body(std::true_type{});
+      else
+        body(std::false_type{});
+      return;
+    }
     if (s.ragged_k && cur.it == s.n_it - 1) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -348,7 +433,15 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
       }
     }
   };
+  // Row block done: partial sums reduced within each lane group (DPP), then
+  // across the waves through LDS in wave order, and stored. Alternate row
+  // blocks use alternate LDS buffers, so one barrier per row block suffices:
+  // a buffer is written again only two row blocks later, after every thread
+  // has passed the barrier of the row block in between, which follows its
+  // reads.
   auto finish = [&](const LinSched& s, const Cursor& cur) __attribute__((always_inline)) {
+    float* const red = red_base + red_par * S::kRedFloats;
+    red_par ^= 1;
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
 #pragma unroll
@@ -361,6 +454,20 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
     }
     __syncthreads();
     const int rb = bid + cur.j * G;
+    // FP8 weights: the row block's scales through the scalar cache (uniform
+    // addresses, counted on lgkmcnt), so no wait on the weight loads in
+    // flight; each thread then picks its row's scale.
+    float scl[W8 ? NR : 1];
+    if constexpr (W8) {
+      // pointer and row made visibly uniform, or the compiler emits vector
+      // loads whose waits would drain the weight loads in flight
+      const __attribute__((address_space(4))) float* sp =
+          (const __attribute__((address_space(4))) float*)uniform_ptr(s.scale);
+      const int row0 = __builtin_amdgcn_readfirstlane(rb * NR);
+      const int last = __builtin_amdgcn_readfirstlane(s.N - 1);
+#pragma unroll
+      for (int j = 0; j < NR; ++j) scl[j] = sp[min(row0 + j, last)];
+    }
     for (int i = tid; i < NR * M; i += kStreamThreads) {
       const int m = i / NR, rr = i - m * NR;
       const int row = rb * NR + rr;
@@ -368,6 +475,12 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
         float v = red[rr * M + m];
 #pragma unroll
         for (int w = 1; w < kStreamWaves; ++w) v += red[(w * NR + rr) * M + m];  // wave order
+        if constexpr (W8) {
+          float sc = scl[0];
+#pragma unroll
+          for (int j = 1; j < NR; ++j) sc = rr == j ? scl[j] : sc;
+          v *= sc;
+        }
         const size_t o = (size_t)m * s.N + row;
         if (is_chain) {  // visible at device scope without a cache write-back
           if (s.bf16)
@@ -383,7 +496,6 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
         }
       }
     }
-    __syncthreads();
     zero_acc();
   };
 
@@ -471,16 +583,16 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
 // Launch: per-M tile choice and the persistent grid
 // ---------------------------------------------------------------------------
 
-template <int M, int RPL, int U, int KCMAX, int DEPTH>
+template <int M, int RPL, int U, int KCMAX, int DEPTH, bool W8>
 static hipError_t launch_m(const StreamLinear& single, const StreamLinear* chain, int n_lin,
                            ChainSync* sync, int grid, hipStream_t s) {
-  using S = Stream<M, RPL, U, KCMAX>;
+  using S = Stream<M, RPL, U, KCMAX, W8>;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH>),
+      reinterpret_cast<const void*>(&gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH, W8>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH>), dim3(grid), dim3(kStreamThreads),
-                     S::kLdsBytes, s, single, chain, n_lin, sync);
+  hipLaunchKernelGGL((gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH, W8>), dim3(grid),
+                     dim3(kStreamThreads), S::kLdsBytes, s, single, chain, n_lin, sync);
   return hipGetLastError();
 }
 
@@ -511,35 +623,64 @@ static hipError_t launch_m(const StreamLinear& single, const StreamLinear* chain
   X(15, 4, 2, 4096, 3)         \
   X(16, 4, 2, 4096, 3)
 
-size_t stream_rows_per_block(int M) {
-  switch (M) {
-#define SPECV_NR(MM, RPL, U, KC, D) \
-  case MM:                       \
-    return 4 * RPL;
-    SPECV_STREAM_TABLE(SPECV_NR)
-#undef SPECV_NR
-    default:
-      return 0;
-  }
-}
+// FP8 weights: a segment holds 256 weights (16 bytes per lane), so a stage
+// of U = 2 segments covers 4096 reduction elements in the same 8 loads per
+// lane as a bf16 stage (half the bytes each). KCMAX as for bf16 (the LDS
+// holds bf16 activations either way).
+#ifndef SPECV_STREAM_W8_TABLE
+#define SPECV_STREAM_W8_TABLE(X) \
+  X(1, 4, 2, 32768, 4)            \
+  X(2, 4, 2, 32768, 4)            \
+  X(3, 4, 2, 24576, 4)            \
+  X(4, 4, 2, 18432, 4)            \
+  X(5, 4, 2, 14336, 4)            \
+  X(6, 4, 2, 12288, 3)            \
+  X(7, 4, 2, 10240, 3)            \
+  X(8, 4, 2, 8192, 3)             \
+  X(9, 4, 2, 6144, 2)             \
+  X(10, 4, 2, 6144, 2)            \
+  X(11, 4, 2, 6144, 2)            \
+  X(12, 4, 2, 6144, 2)            \
+  X(13, 4, 2, 4096, 2)            \
+  X(14, 4, 2, 4096, 2)            \
+  X(15, 4, 1, 4096, 3)            \
+  X(16, 4, 1, 4096, 2)
+#endif
 
-template <int M, int RPL, int U, int KCMAX, int DEPTH>
+// Both tables use 16-row blocks (RPL = 4).
+size_t stream_rows_per_block(int M) { return M >= 1 && M <= kMaxStreamM ? 16 : 0; }
+
+template <int M, int RPL, int U, int KCMAX, int DEPTH, bool W8>
 static int max_wgs_m() {
-  using S = Stream<M, RPL, U, KCMAX>;
+  using S = Stream<M, RPL, U, KCMAX, W8>;
+  static_assert(S::NR == 16, "row block size shared by both weight formats");
   int n = 0;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLdsBytes);
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH>,
-                                                   kStreamThreads, S::kLdsBytes) != hipSuccess)
+  (void)hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH, W8>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLdsBytes);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH, W8>, kStreamThreads, S::kLdsBytes) !=
+      hipSuccess)
     return 1;
   return n > 0 ? n : 1;
 }
 
-int stream_max_wgs_per_cu(int M) {
+int stream_max_wgs_per_cu(int M, bool w8) {
+  if (w8) {
+    switch (M) {
+#define SPECV_OCC8(MM, RPL, U, KC, D) \
+  case MM:                            \
+    return max_wgs_m<MM, RPL, U, KC, D, true>();
+      SPECV_STREAM_W8_TABLE(SPECV_OCC8)
+#undef SPECV_OCC8
+      default:
+        return 1;
+    }
+  }
   switch (M) {
 #define SPECV_OCC(MM, RPL, U, KC, D) \
-  case MM:                        \
-    return max_wgs_m<MM, RPL, U, KC, D>();
+  case MM:                           \
+    return max_wgs_m<MM, RPL, U, KC, D, false>();
     SPECV_STREAM_TABLE(SPECV_OCC)
 #undef SPECV_OCC
     default:
@@ -547,12 +688,24 @@ int stream_max_wgs_per_cu(int M) {
   }
 }
 
-hipError_t launch_gemm_stream_any(const StreamLinear& single, const StreamLinear* chain, int n_lin,
-                                  ChainSync* sync, int M, int grid, hipStream_t s) {
+static hipError_t launch_gemm_stream_any(const StreamLinear& single, const StreamLinear* chain,
+                                         int n_lin, ChainSync* sync, int M, bool w8, int grid,
+                                         hipStream_t s) {
+  if (w8) {
+    switch (M) {
+#define SPECV_CASE8(MM, RPL, U, KC, D) \
+  case MM:                             \
+    return launch_m<MM, RPL, U, KC, D, true>(single, chain, n_lin, sync, grid, s);
+      SPECV_STREAM_W8_TABLE(SPECV_CASE8)
+#undef SPECV_CASE8
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
   switch (M) {
 #define SPECV_CASE(MM, RPL, U, KC, D) \
-  case MM:                         \
-    return launch_m<MM, RPL, U, KC, D>(single, chain, n_lin, sync, grid, s);
+  case MM:                            \
+    return launch_m<MM, RPL, U, KC, D, false>(single, chain, n_lin, sync, grid, s);
     SPECV_STREAM_TABLE(SPECV_CASE)
 #undef SPECV_CASE
     default:
@@ -560,18 +713,19 @@ hipError_t launch_gemm_stream_any(const StreamLinear& single, const StreamLinear
   }
 }
 
-hipError_t launch_gemm_stream(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
-                              int K, int N, int grid, hipStream_t s) {
-  StreamLinear d{x, w, y, K, N, out_bf16 ? 1 : 0, 0};
+hipError_t launch_gemm_stream(const uint16_t* x, const void* w, const float* w_scale, void* y,
+                              bool out_bf16, bool w8, int M, int K, int N, int grid,
+                              hipStream_t s) {
+  StreamLinear d{x, w, w_scale, y, K, N, out_bf16 ? 1 : 0, 0};
   const int n_rb = (N + (int)stream_rows_per_block(M) - 1) / (int)stream_rows_per_block(M);
   if (grid > n_rb) grid = n_rb;
-  return launch_gemm_stream_any(d, nullptr, 1, nullptr, M, grid, s);
+  return launch_gemm_stream_any(d, nullptr, 1, nullptr, M, w8, grid, s);
 }
 
-hipError_t launch_gemm_chain(const StreamLinear* chain, int n_lin, ChainSync* sync, int M, int grid,
-                             hipStream_t s) {
-  StreamLinear none{nullptr, nullptr, nullptr, 0, 0, 0, 0};
-  return launch_gemm_stream_any(none, chain, n_lin, sync, M, grid, s);
+hipError_t launch_gemm_chain(const StreamLinear* chain, int n_lin, ChainSync* sync, int M, bool w8,
+                             int grid, hipStream_t s) {
+  StreamLinear none{nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0};
+  return launch_gemm_stream_any(none, chain, n_lin, sync, M, w8, grid, s);
 }
 
 }  // namespace specv

@@ -16,18 +16,19 @@ constexpr int kMaxStreamM = 16;
 // uses the tiled MFMA kernel.
 constexpr int kMaxSkinnyM = 128;
 
-// One linear of a streaming launch; layout identical to spec_linear of the
-// public header (x, w, y, d_in, d_out, y_dtype, reserved).
+// One linear of a streaming launch (single call, or one descriptor of a
+// chain workspace, filled from spec_linear / spec_linear_w8).
 struct StreamLinear {
   const uint16_t* x;
-  const uint16_t* w;
+  const void* w;         // bf16 [N][K], or FP8 E4M3 codes [N][K]
+  const float* w_scale;  // FP8 weights: scale of each output row; bf16: unused
   void* y;
   int K;         // d_in
   int N;         // d_out
   int out_bf16;  // SPEC_BF16 (1) or SPEC_F32 (0)
   int reserved;
 };
-static_assert(sizeof(StreamLinear) == 40, "descriptor layout");
+static_assert(sizeof(StreamLinear) == 48, "descriptor layout");
 
 // Header of a chain workspace; followed by `n` per-linear arrival counters
 // (unsigned) and then the n descriptors (StreamLinear, 64-byte aligned).
@@ -43,7 +44,8 @@ struct ChainSync {
   int pad[6];           // header is one 64-byte line
 };
 static_assert(sizeof(ChainSync) == 64, "chain header is one cache line");
-constexpr unsigned kChainMagic = 0x53504348u;  // "SPCH"
+constexpr unsigned kChainMagic = 0x53504348u;    // "SPCH": bf16 weights
+constexpr unsigned kChainMagicW8 = 0x53503848u;  // "SP8H": FP8 E4M3 weights
 // Chain workspace after the header: n arrival counters, then (64-byte
 // aligned) n x kReleaseLanes release flags, one 64-byte line each, then the
 // descriptors.
@@ -56,11 +58,14 @@ __host__ __device__ inline size_t chain_counts_bytes(int n) {
 }
 
 size_t stream_rows_per_block(int M);
-int stream_max_wgs_per_cu(int M);
-hipError_t launch_gemm_stream(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
-                              int K, int N, int grid, hipStream_t s);
-hipError_t launch_gemm_chain(const StreamLinear* chain, int n_lin, ChainSync* sync, int M, int grid,
-                             hipStream_t s);
+int stream_max_wgs_per_cu(int M, bool w8);
+// Streaming kernel, one linear: bf16 weights (w_scale null) or FP8 E4M3
+// weights with per-row scales (w8).
+hipError_t launch_gemm_stream(const uint16_t* x, const void* w, const float* w_scale, void* y,
+                              bool out_bf16, bool w8, int M, int K, int N, int grid,
+                              hipStream_t s);
+hipError_t launch_gemm_chain(const StreamLinear* chain, int n_lin, ChainSync* sync, int M, bool w8,
+                             int grid, hipStream_t s);
 hipError_t launch_gemm_skinny(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
                               int K, int N, hipStream_t s);
 hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 17
     for n in names:
         assert hasattr(sv.lib, n), n
 
@@ -33,7 +33,7 @@ def test_binding_covers_exactly_the_header(sv):
 
 
 def test_version_and_status_strings(sv):
-    assert sv.abi_version() == 2
+    assert sv.abi_version() == 3
     for code, name in [(0, b"SPEC_OK"), (-1, b"SPEC_ERR_INVALID_ARGUMENT"),
                        (-2, b"SPEC_ERR_ALIGNMENT"), (-3, b"SPEC_ERR_UNSUPPORTED"),
                        (-4, b"SPEC_ERR_WORKSPACE"), (-5, b"SPEC_ERR_HIP")]:
@@ -133,6 +133,44 @@ def test_verify_warped_rejects(sv):
         assert b"temperature" in sv.lib.spec_last_error()
     assert call(0.0, 1.0, tl=None) == -1       # other checks still apply
     assert call(0.7, 0.0, wsb=100) == -4
+
+
+def test_gemm_w8_rejects(sv):
+    f = sv.lib.spec_verify_gemm_w8
+    cases = [
+        ((A, A, None, A, 0, 5, 4096, 4096), -1),     # null w_scale
+        ((None, A, A, A, 0, 5, 4096, 4096), -1),     # null x
+        ((A, A, A, A, 2, 5, 4096, 4096), -1),        # bad y_dtype
+        ((A, A, A, A, 0, 5, 4104, 4096), -1),        # d_in a multiple of 8 but not of 16
+        ((A, A, A, A, 0, 5, 0, 4096), -1),
+        ((A, A, A, A, 0, 0, 4096, 4096), -1),
+        ((A, A, A, A, 0, 5, 4096, 0), -1),
+        ((A, A, A + 2, A, 0, 5, 4096, 4096), -2),    # misaligned scales
+        ((A, A + 8, A, A, 0, 5, 4096, 4096), -2),    # misaligned weights
+        ((A, A, A, A, 0, 17, 4096, 4096), -3),       # beyond the streaming kernel
+    ]
+    for args, code in cases:
+        assert f(*args, None) == code, args
+        assert sv.lib.spec_last_error()
+
+
+def test_chain_w8_rejects(sv):
+    L = sv.SpecLinearW8
+    good = (L * 2)(L(A, A, A, A, 4096, 4096, 1, 0), L(A, A, A, A, 4096, 128, 0, 0))
+    nb = sv.lib.spec_chain_workspace_bytes(2)
+    f = sv.lib.spec_chain_prepare_w8
+    assert f(None, 2, 5, A, nb) == -1
+    assert f(good, 2, 5, None, nb) == -1
+    assert f(good, 2, 17, A, nb) == -1
+    assert f(good, 2, 5, A, nb - 1) == -4
+    for bad, code in [(L(A, A, None, A, 4096, 8, 1, 0), -1), (L(A, A, A, A, 4104, 8, 1, 0), -1),
+                      (L(A, A, A, A, 4096, 8, 1, 1), -1), (L(A, A, A + 2, A, 4096, 8, 1, 0), -2)]:
+        arr = (L * 2)(good[0], bad)
+        assert f(arr, 2, 5, A, nb) == code
+        assert b"linear 1" in sv.lib.spec_last_error()
+    g = sv.lib.spec_verify_gemm_chain_w8
+    assert g(0, 5, A, None) == -1 and g(2, 17, A, None) == -1 and g(2, 5, None, None) == -1
+    assert g(2, 5, A + 8, None) == -4
 
 
 def test_chain_rejects(sv):
