@@ -12,13 +12,15 @@ synthetic Llama-shaped inputs already resident in HBM:
 
 Each phase is captured once in a HIP graph; a timed step replays the two
 graphs back to back with HIP events between them on the same stream.
-Prints one JSON line: the throughput in verified positions per second, the
+With --w8 every linear (stack and lm-head) holds FP8 E4M3 weights with a
+per-row scale (weight-only 8-bit storage, bf16 activations and products);
+M <= 16 only. Prints one JSON line: the throughput in verified positions per second, the
 per-phase times, the roofline of the GEMM phase (algorithmic bytes over its
 measured time, against the 8 TB/s HBM peak; MFMA peak where the FLOPs
 dominate) and the fp64 oracle's rate on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--workload llama8b|llama70b]
-                    [--batch B] [--no-graph] [--no-chain] [--no-cpu-baseline]
+                    [--batch B] [--no-graph] [--no-chain] [--no-cpu-baseline] [--w8]
     python bench.py --copy-calibration   # plain device copy of known size,
                                          # the scale for HBM traffic counters
 """
@@ -51,6 +53,8 @@ def parse():
                     help="one spec_verify_gemm launch per linear instead of one chain launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=2026)
+    ap.add_argument("--w8", action="store_true",
+                    help="FP8 E4M3 weights with per-row scales for every linear (M <= 16)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (the known-size "
                          "reference that scales FETCH_SIZE / WRITE_SIZE counters)")
@@ -89,22 +93,32 @@ def load_traffic(name):
 class Workload:
     """Device-resident inputs of one verify step."""
 
-    def __init__(self, stack, B, K, seed, dev):
+    def __init__(self, stack, B, K, seed, dev, w8=False):
         import torch
         import synth
         from synth import device as sd
 
-        self.stack, self.B, self.K, self.dev = stack, B, K, dev
+        self.stack, self.B, self.K, self.dev, self.w8 = stack, B, K, dev, w8
         self.M = B * (K + 1)
         self.linears = []  # (name, x, w, y)
+        self.scales = []   # FP8 weights: per-row scales of each linear
+        base = synth.WEIGHT_STD / synth.W8_CODE_STD
+
+        def weights(d_out, d_in, wseed):
+            if not w8:
+                return sd.normal_bf16((d_out, d_in), synth.WEIGHT_STD, wseed, dev), None
+            return (sd.e4m3_normal_codes((d_out, d_in), synth.W8_CODE_STD, wseed, dev),
+                    sd.w8_row_scales(d_out, base, wseed + 977, dev))
+
         for i, (name, d_in, d_out) in enumerate(stack.all_linears()[:-1]):
-            w = sd.normal_bf16((d_out, d_in), synth.WEIGHT_STD, seed * 1000 + 2 * i, dev)
+            w, sc = weights(d_out, d_in, seed * 1000 + 2 * i)
             x = sd.normal_bf16((self.M, d_in), 1.0, seed * 1000 + 2 * i + 1, dev)
             y = torch.empty((self.M, d_out), dtype=torch.bfloat16, device=dev)
             self.linears.append((name, x, w, y))
+            self.scales.append(sc)
         V, d = stack.vocab, stack.hidden
         self.V = V
-        self.lm_head = sd.normal_bf16((V, d), synth.WEIGHT_STD, seed * 7 + 1, dev)
+        self.lm_head, self.lm_scale = weights(V, d, seed * 7 + 1)
         self.hidden = sd.normal_bf16((self.M, d), 1.0, seed * 7 + 2, dev)
         self.target_logits = torch.empty((B, K + 1, V), dtype=torch.float32, device=dev)
         self.out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
@@ -118,26 +132,41 @@ class Workload:
         from the draft distributions (Gumbel-max)."""
         import torch
         from synth import device as sd
-        sv.verify_gemm(self.hidden, self.lm_head, out=self.target_logits.view(self.M, self.V))
+        self.lm_head_gemm(sv)
         tl = self.target_logits[:, :self.K, :]
         self.draft_logits = (tl + sd.normal_f32(tl.shape, sigma, seed * 7 + 5, self.dev)).contiguous()
         self.draft_tokens = sd.gumbel_max_tokens(self.draft_logits, seed * 7 + 6)
         self.workspace = sv.new_workspace(self.B, self.K, self.V, self.dev)
         torch.cuda.synchronize()
 
+    def lm_head_gemm(self, sv):
+        out = self.target_logits.view(self.M, self.V)
+        if self.w8:
+            sv.verify_gemm_w8(self.hidden, self.lm_head, self.lm_scale, out=out)
+        else:
+            sv.verify_gemm(self.hidden, self.lm_head, out=out)
+
     def make_chain(self, sv):
         """All stack linears and the lm-head as one chain (one launch)."""
-        lin = [(x, w, y) for _, x, w, y in self.linears]
-        lin.append((self.hidden, self.lm_head, self.target_logits.view(self.M, self.V)))
+        if self.w8:
+            lin = [(x, w, sc, y) for (_, x, w, y), sc in zip(self.linears, self.scales)]
+            lin.append((self.hidden, self.lm_head, self.lm_scale,
+                        self.target_logits.view(self.M, self.V)))
+        else:
+            lin = [(x, w, y) for _, x, w, y in self.linears]
+            lin.append((self.hidden, self.lm_head, self.target_logits.view(self.M, self.V)))
         self.chain = sv.Chain(lin, self.dev)
 
     def gemm_phase(self, sv):
         if getattr(self, "chain", None) is not None:
             self.chain.run()
             return
-        for _, x, w, y in self.linears:
-            sv.verify_gemm(x, w, out=y)
-        sv.verify_gemm(self.hidden, self.lm_head, out=self.target_logits.view(self.M, self.V))
+        for (_, x, w, y), sc in zip(self.linears, self.scales):
+            if self.w8:
+                sv.verify_gemm_w8(x, w, sc, out=y)
+            else:
+                sv.verify_gemm(x, w, out=y)
+        self.lm_head_gemm(sv)
 
     def sampling_phase(self, sv):
         sv.verify(self.target_logits, self.draft_logits, self.draft_tokens, self.u_accept,
@@ -148,9 +177,11 @@ class Workload:
         """Algorithmic HBM bytes of the GEMM phase: every weight once, every
         activation once, every output once (bf16 stack outputs, fp32 logits)."""
         total = 0
-        for _, x, w, y in self.linears:
-            total += 2 * w.numel() + 2 * x.numel() + 2 * y.numel()
-        total += 2 * self.lm_head.numel() + 2 * self.hidden.numel() + 4 * self.target_logits.numel()
+        for (_, x, w, y), sc in zip(self.linears, self.scales):
+            total += w.numel() * w.element_size() + 2 * x.numel() + 2 * y.numel()
+            total += 0 if sc is None else 4 * sc.numel()
+        total += self.lm_head.numel() * self.lm_head.element_size() + 2 * self.hidden.numel()
+        total += 4 * self.target_logits.numel() + (0 if self.lm_scale is None else 4 * self.V)
         return total
 
     def gemm_flops(self):
@@ -165,8 +196,9 @@ class Workload:
 
 def cpu_baseline(wl, sample_layers=None):
     """The fp64 oracle on the host cores, on a bounded sample of the same
-    step: the first layer's linears, the lm-head and the sampling stage on
-    the GPU step's inputs; the remaining layers are scaled from the first."""
+    step: the first layers' linears (whole layers until about 10 s of oracle
+    time), the lm-head and the sampling stage on the GPU step's inputs; the
+    remaining layers are scaled from the sampled ones."""
     import numpy as np
     import oracle
     from synth import device as sd
@@ -177,19 +209,31 @@ def cpu_baseline(wl, sample_layers=None):
     except Exception:
         threads = 1
     per_layer = len(wl.stack.linears)
-    if sample_layers is None:
-        sample_layers = wl.stack.layers
     t_layer = 0.0
-    for name, x, w, _ in wl.linears[:per_layer * sample_layers]:
-        xb, wb = sd.to_bits(x), sd.to_bits(w)
-        t0 = time.perf_counter()
-        oracle.linear(xb, wb)
-        t_layer += time.perf_counter() - t0
+    def lin(x, w, sc):
+        xb = sd.to_bits(x)
+        if sc is None:
+            wb = sd.to_bits(w)
+            t0 = time.perf_counter()
+            y = oracle.linear(xb, wb)
+        else:
+            wb, sb = w.cpu().numpy(), sc.cpu().numpy()
+            t0 = time.perf_counter()
+            y = oracle.linear_w8(xb, wb, sb)
+        return y, time.perf_counter() - t0
+
+    # whole layers until about 10 s of oracle time (or all of them)
+    pairs = list(zip(wl.linears, wl.scales))
+    done = 0
+    while done < wl.stack.layers and (sample_layers is None and t_layer < 10.0
+                                      or sample_layers is not None and done < sample_layers):
+        for (name, x, w, _), sc in pairs[per_layer * done:per_layer * (done + 1)]:
+            t_layer += lin(x, w, sc)[1]
+        done += 1
+    sample_layers = done
     t_layer /= sample_layers
-    xb, wb = sd.to_bits(wl.hidden), sd.to_bits(wl.lm_head)
-    t0 = time.perf_counter()
-    logits = oracle.linear(xb, wb).astype(np.float32).reshape(wl.B, wl.K + 1, wl.V)
-    t_lm = time.perf_counter() - t0
+    logits, t_lm = lin(wl.hidden, wl.lm_head, wl.lm_scale)
+    logits = logits.astype(np.float32).reshape(wl.B, wl.K + 1, wl.V)
     dl = wl.draft_logits.cpu().numpy()
     toks = wl.draft_tokens.cpu().numpy()
     ua, us = wl.u_accept.cpu().numpy(), wl.u_sample.cpu().numpy()
@@ -248,7 +292,11 @@ def main():
     stack = {"llama8b": synth.LLAMA_8B, "llama70b": synth.LLAMA_70B_16L}[args.workload]
     key = {"llama8b": "llama8b_lm_head", "llama70b": "llama70b_lm_head"}[args.workload]
     B, K = args.batch, K_DRAFT
-    wl = Workload(stack, B, K, args.seed, dev)
+    if args.w8 and B * (K + 1) > 16:
+        print(f"--w8 covers M <= 16 (the weight-streaming kernel); B={B} gives M={B * (K + 1)}",
+              file=sys.stderr)
+        sys.exit(2)
+    wl = Workload(stack, B, K, args.seed, dev, w8=args.w8)
     wl.make_drafts(sv, synth.draft_noise_sigma(key, 0.8), args.seed)
     use_chain = not args.no_chain and wl.M <= 16
     if use_chain:
@@ -302,7 +350,7 @@ def main():
     gemm_flops = wl.gemm_flops()
     launches = wl.n_gemm_launches()
     achieved = gemm_bytes / (ms_gemm * 1e-3) / 1e9
-    traffic = load_traffic(f"traffic_gemm_stream_{args.workload}_b{B}")
+    traffic = load_traffic(f"traffic_gemm_stream_{'w8_' if args.w8 else ''}{args.workload}_b{B}")
     # The GEMM phase is bound by whichever floor is higher: reading the
     # weights at the HBM peak, or the FLOPs at the dense bf16 MFMA peak.
     mfma_bound = gemm_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > gemm_bytes / (HBM_PEAK_GBS * 1e9)
@@ -330,9 +378,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) bf16 weights, "
-                "draft logits = target logits + calibrated noise, alpha~0.8)",
+        "dtype": "bf16 (fp8 e4m3 weights)" if args.w8 else "bf16",
+        "data": ("synthetic (seeded N(0,1) activations, "
+                 + ("FP8 E4M3 weight codes N(0,64^2) with per-row scales ~0.02/64, "
+                    if args.w8 else "N(0,0.02^2) bf16 weights, ")
+                 + "draft logits = target logits + calibrated noise, alpha~0.8)"),
         "config": {
             "workload": (f"{stack.name} verify step: {stack.layers} layers x (QKV, O, gate/up, "
                          f"down) + lm-head {stack.hidden}->{stack.vocab} + sampling"),
@@ -342,6 +392,7 @@ def main():
             "vocab": wl.V,
             "graph": not args.no_graph,
             "gemm_launch": "chain" if use_chain else "per-linear",
+            "weights": "fp8_e4m3 + fp32 row scale" if args.w8 else "bf16",
         },
         "pct_hbm_peak_in_verify": 100.0 * achieved / HBM_PEAK_GBS,
         "ms_gemm_phase": ms_gemm,
@@ -355,7 +406,8 @@ def main():
         "emitted_tokens_per_s": B * e_n / (ms_step * 1e-3),
         "roofline": {
             **roof,
-            "kernel": ("gemm_stream chain (all stack linears + lm-head in one launch)" if use_chain
+            "kernel": (("gemm_stream FP8-weight chain" if args.w8 else "gemm_stream chain")
+                       + " (all stack linears + lm-head in one launch)" if use_chain
                        else "per-linear spec_verify_gemm launches (stack linears + lm-head)"),
             "traffic": traffic,
             "hbm_gbs": achieved,
