@@ -32,7 +32,7 @@ inverse-CDF sampling -- is "parity unpinned": only the law of the sampled
 token is pinned, the id map is a convention shared with the GPU path.
 """
 
-from .linear import bf16_to_f64, e4m3_to_f64, linear, linear_w8
+from .linear import bf16_to_f64, e4m3_to_f64, linear, linear_w8, round_to_bf16, to_bf16_bits
 from .softmax import softmax_rows
 from .speculative import (
     TIE_BAND,
@@ -55,7 +55,8 @@ from .speculative import (
 
 __all__ = [
     "TIE_BAND", "accept_batch", "sample_batch", "sample_row", "verify_batch_probs",
-    "bf16_to_f64", "e4m3_to_f64", "linear", "linear_w8", "softmax_rows", "acceptance_rate", "accept_test",
+    "bf16_to_f64", "e4m3_to_f64", "linear", "linear_w8", "round_to_bf16", "to_bf16_bits",
+    "softmax_rows", "acceptance_rate", "accept_test",
     "emitted_law", "expected_tokens", "expected_tokens_general",
     "first_rejection", "inverse_cdf", "residual_weights", "total_variation",
     "verify_batch", "verify_round",

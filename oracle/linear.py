@@ -31,6 +31,26 @@ def bf16_to_f64(bits):
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def round_to_bf16(values):
+    """Nearest bfloat16 value of finite float64 values, ties to even, as
+    float64 (round-to-nearest-even is the IEEE default the format uses).
+
+    bfloat16 keeps 8 significant bits: for |v| in [2^(e-1), 2^e) the spacing
+    is 2^(e-8); below 2^-126 the subnormal spacing 2^-133 applies. Values
+    beyond the largest bfloat16 are not expected here.
+    """
+    v = np.asarray(values, dtype=np.float64)
+    _, e = np.frexp(v)
+    step = np.maximum(e - 8, -133)
+    return np.ldexp(np.rint(np.ldexp(v, -step)), step)
+
+
+def to_bf16_bits(values):
+    """bfloat16 bit patterns (uint16) of round_to_bf16(values)."""
+    r = round_to_bf16(values).astype(np.float32)  # exact: r is a bfloat16 value
+    return (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
 def linear(x_bits, w_bits, block_bytes=64 << 20):
     """y[m][n] = sum_k x[m][k] * w[n][k] in float64.
 

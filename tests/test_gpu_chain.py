@@ -53,16 +53,25 @@ def test_chain_matches_single_launches(sv, dev, M):
 
 
 def test_chain_of_dependent_layers(sv, dev):
-    """y_i feeds x_{i+1}: the oracle recomputes each layer from the GPU's own
-    bf16 input of that layer (its x), and the final check recomputes layer
-    i+1 from layer i's GPU output, which only passes if the barrier made the
-    whole of y_i visible before x_{i+1} was read."""
+    """y_i feeds x_{i+1}. The oracle runs the same dependent chain on its
+    own, from the seeded first input only: each layer in fp64, rounded to
+    bf16 (nearest, ties to even) as the next layer's input. Every GPU layer
+    must match it within the GEMM tolerance; a layer that read its input
+    before the previous layer's output was complete and visible (the outputs
+    are zeroed before every launch) would miss by far."""
     import torch
     from synth import device as sd
     M = 5
     dims = [4096, 6144, 4096, 14336, 4096, 4096, 1000]
     shapes = [(dims[i], dims[i + 1], torch.bfloat16) for i in range(len(dims) - 1)]
     lin = make_linears(dev, M, shapes, 7, chained=True)
+    for i in range(1, len(lin)):
+        assert lin[i][0].data_ptr() == lin[i - 1][2].data_ptr()
+    refs, cur = [], sd.to_bits(lin[0][0])
+    for _, w, _ in lin:
+        r = oracle.linear(cur, sd.to_bits(w))
+        refs.append(r)
+        cur = oracle.to_bf16_bits(r)
     ch = sv.Chain(lin, dev)
     for _ in range(3):  # repeated launches reuse the counters (generations)
         for _, _, y in lin:
@@ -70,12 +79,9 @@ def test_chain_of_dependent_layers(sv, dev):
         ch.run()
         torch.cuda.synchronize()
         assert ch.error() == 0
-        for i, (x, w, y) in enumerate(lin):
-            ref = oracle.linear(sd.to_bits(x), sd.to_bits(w))
+        for i, ((_, _, y), ref) in enumerate(zip(lin, refs)):
             e = rel_err(y.float().cpu().numpy().astype(np.float64), ref)
             assert e <= 2e-2, (i, e)
-            if i > 0:
-                assert x.data_ptr() == lin[i - 1][2].data_ptr()
 
 
 def test_chain_oracle_llama_layer(sv, dev):

@@ -33,6 +33,25 @@ def test_bf16_decode_ieee_values():
         assert g == w and math.copysign(1, g) == math.copysign(1, w)
 
 
+def test_round_to_bf16_ties_to_even_and_spacing():
+    # 8 significant bits: between 1 and 2 the spacing is 2^-7
+    vals = [1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -30, -(1 + 2 ** -8),
+            3.0 + 2 ** -7, 2 ** -130 + 2 ** -134, 0.0, 448.0, 1e-3]
+    want = [1.0, 1.0, 1 + 2 ** -6, 1 + 2 ** -7, -1.0, 3.0, 2 ** -130, 0.0, 448.0,
+            0.0009994506835937500]
+    got = oracle.round_to_bf16(np.array(vals))
+    assert got.tolist() == want
+    bits = oracle.to_bf16_bits(np.array([1.0, -2.0, 3.140625, 1 + 2 ** -8]))
+    assert bits.tolist() == [0x3F80, 0xC000, 0x4049, 0x3F80]
+
+
+def test_round_to_bf16_matches_torch_on_float32_values():
+    import torch
+    v = np.random.default_rng(8).standard_normal(20000).astype(np.float32) * np.float32(37)
+    t = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_to_bf16(v.astype(np.float64)), t)
+
+
 def _one_bits(shape):
     return np.zeros(shape, dtype=np.uint16)
 
