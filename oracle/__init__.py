@@ -16,6 +16,10 @@ What it computes, and where the pages define it:
 * ``linear_w8`` -- the same pass with FP8 E4M3 weights and a per-row scale
   (weight-only 8-bit storage, "Speculative Decoding: The Algebra and the
   Proof", Where it breaks).
+* ``verify_attention`` -- the K+1 verify positions attending causally over
+  the KV cache, grouped-query heads ("Speculative Decoding: Guess Several
+  Tokens, Check Them in One Pass", Step 1: the pass works like a tiny
+  prefill and reads the cache once).
 * ``softmax_rows`` -- p and q from logits ("Speculative Decoding: Two Models,
   One Voice", Implementing it against a real model).
 * ``speculative`` -- the accept test min(1, p/q), the first rejection, the
@@ -32,6 +36,7 @@ inverse-CDF sampling -- is "parity unpinned": only the law of the sampled
 token is pinned, the id map is a convention shared with the GPU path.
 """
 
+from .attention import verify_attention
 from .linear import bf16_to_f64, e4m3_to_f64, linear, linear_w8, round_to_bf16, to_bf16_bits
 from .softmax import softmax_rows
 from .speculative import (
@@ -56,7 +61,7 @@ from .speculative import (
 __all__ = [
     "TIE_BAND", "accept_batch", "sample_batch", "sample_row", "verify_batch_probs",
     "bf16_to_f64", "e4m3_to_f64", "linear", "linear_w8", "round_to_bf16", "to_bf16_bits",
-    "softmax_rows", "acceptance_rate", "accept_test",
+    "softmax_rows", "verify_attention", "acceptance_rate", "accept_test",
     "emitted_law", "expected_tokens", "expected_tokens_general",
     "first_rejection", "inverse_cdf", "residual_weights", "total_variation",
     "verify_batch", "verify_round",

@@ -183,6 +183,95 @@ def test_linear_w8_rejects_bad_shapes():
 
 
 # ---------------------------------------------------------------------------
+# Verify attention (causal K+1 queries over the KV cache)
+# ---------------------------------------------------------------------------
+
+def _attn_inputs(seed, B, K1, H, Hkv, T, D):
+    q = synth.bf16_normal_bits(seed, "pin.aq", (B, K1, H, D))
+    k = synth.bf16_normal_bits(seed, "pin.ak", (B, T, Hkv, D))
+    v = synth.bf16_normal_bits(seed, "pin.av", (B, T, Hkv, D))
+    return q, k, v
+
+
+def test_attention_equal_keys_average_the_visible_values():
+    # equal scores: the softmax is uniform over the positions a query sees,
+    # so position i averages values 0 .. T-K1+i exactly
+    B, K1, H, Hkv, T, D = 2, 5, 4, 2, 37, 8
+    q, _, v = _attn_inputs(1, B, K1, H, Hkv, T, D)
+    k = np.zeros((B, T, Hkv, D), np.uint16)
+    o = oracle.verify_attention(q, k, v, 0.3)
+    vf = oracle.bf16_to_f64(v)
+    for i in range(K1):
+        want = vf[:, :T - K1 + i + 1].mean(axis=1)          # [B][Hkv][D]
+        for h in range(H):
+            assert np.allclose(o[:, i, h], want[:, h // (H // Hkv)], rtol=0, atol=1e-15)
+
+
+def test_attention_dominant_key_selects_its_value_when_visible():
+    B, K1, H, Hkv, T, D = 1, 4, 2, 1, 20, 8
+    q = np.full((B, K1, H, D), 0x3F80, np.uint16)            # all ones
+    k = np.zeros((B, T, Hkv, D), np.uint16)
+    j = T - 2                                                 # seen by the last two queries
+    k[0, j, 0, :] = 0x4200                                    # 32.0: score 256 * scale
+    v = synth.bf16_normal_bits(2, "pin.av2", (B, T, Hkv, D))
+    o = oracle.verify_attention(q, k, v, 4.0)                 # score gap 1024: exp underflows
+    vf = oracle.bf16_to_f64(v)
+    for i in range(K1):
+        last = T - K1 + i
+        want = vf[0, j, 0] if j <= last else vf[0, :last + 1, 0].mean(axis=0)
+        for h in range(H):
+            assert np.array_equal(o[0, i, h], want) or np.allclose(o[0, i, h], want, atol=1e-15)
+
+
+def test_attention_matches_masked_scipy_softmax():
+    B, K1, H, Hkv, T, D = 2, 5, 8, 2, 29, 16
+    q, k, v = _attn_inputs(3, B, K1, H, Hkv, T, D)
+    scale = 1 / math.sqrt(D)
+    o = oracle.verify_attention(q, k, v, scale)
+    qf, kf, vf = (oracle.bf16_to_f64(a) for a in (q, k, v))
+    mask = np.arange(T)[None, :] > (T - K1 + np.arange(K1))[:, None]   # [K1][T] future keys
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // Hkv)
+            s = scale * np.einsum("id,td->it", qf[b, :, h], kf[b, :, g])
+            s[mask] = -np.inf
+            p = scipy.special.softmax(s, axis=-1)
+            assert np.abs(o[b, :, h] - p @ vf[b, :, g]).max() < 1e-13
+
+
+def test_attention_is_causal_and_grouped():
+    B, K1, H, Hkv, T, D = 1, 5, 6, 2, 16, 8
+    q, k, v = _attn_inputs(4, B, K1, H, Hkv, T, D)
+    o = oracle.verify_attention(q, k, v, 0.5)
+    # changing the last key/value changes only the last query's output
+    k2, v2 = k.copy(), v.copy()
+    k2[0, T - 1] ^= 0x0100
+    v2[0, T - 1] ^= 0x0100
+    o2 = oracle.verify_attention(q, k2, v2, 0.5)
+    assert np.array_equal(o[:, :K1 - 1], o2[:, :K1 - 1])
+    assert not np.array_equal(o[:, K1 - 1], o2[:, K1 - 1])
+    # heads of one group with the same query give the same output; swapping
+    # the two key/value heads swaps the outputs of the two groups
+    q3 = q.copy()
+    q3[:, :, 1] = q3[:, :, 0]
+    o3 = oracle.verify_attention(q3, k, v, 0.5)
+    assert np.array_equal(o3[:, :, 0], o3[:, :, 1])
+    q4 = np.concatenate([q[:, :, 3:], q[:, :, :3]], axis=2)
+    o4 = oracle.verify_attention(q4, k[:, :, ::-1], v[:, :, ::-1], 0.5)
+    assert np.array_equal(o4, np.concatenate([o[:, :, 3:], o[:, :, :3]], axis=2))
+
+
+def test_attention_single_query_is_decode_attention_over_everything():
+    B, K1, H, Hkv, T, D = 1, 1, 2, 2, 9, 4
+    q, k, v = _attn_inputs(5, B, K1, H, Hkv, T, D)
+    o = oracle.verify_attention(q, k, v, 1.0)
+    qf, kf, vf = (oracle.bf16_to_f64(a) for a in (q, k, v))
+    for h in range(H):
+        p = scipy.special.softmax(kf[0, :, h] @ qf[0, 0, h])
+        assert np.abs(o[0, 0, h] - p @ vf[0, :, h]).max() < 1e-14
+
+
+# ---------------------------------------------------------------------------
 # Softmax
 # ---------------------------------------------------------------------------
 
