@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 3
+#define SPEC_ABI_VERSION 4
 
 /* Status codes. */
 #define SPEC_OK 0
@@ -198,6 +198,40 @@ typedef struct spec_linear_w8 {
 int spec_chain_prepare_w8(const spec_linear_w8* linears, int n, int M, void* workspace,
                           size_t workspace_bytes);
 int spec_verify_gemm_chain_w8(int n, int M, void* workspace, void* stream);
+
+/*
+ * spec_verify_attention -- the attention of the verify pass: the K+1 verify
+ * positions of each sequence attend, through the causal mask, over that
+ * sequence's KV cache, which is read once for all of them ("Speculative
+ * Decoding: Guess Several Tokens, Check Them in One Pass", Step 1: the pass
+ * works like a tiny prefill).
+ *
+ *   q        device, bf16 [B][K+1][n_heads][head_dim], 16-byte aligned.
+ *   k_cache  device, bf16 [B][T][n_kv_heads][head_dim]: the keys of all T
+ *            positions, the K+1 verify positions last; 16-byte aligned.
+ *   v_cache  device, bf16, same layout as k_cache.
+ *   out      device, [B][K+1][n_heads][head_dim] of out_dtype (SPEC_F32 or
+ *            SPEC_BF16).
+ *   Query position i (0..K) sits at position T-K-1+i and sees positions
+ *   0..T-K-1+i; query head h reads key/value head h / (n_heads /
+ *   n_kv_heads). out = softmax(scale * q . k) v, fp32 softmax and
+ *   accumulation (the probabilities enter the value product as bf16).
+ *   Limits: head_dim = 128; n_kv_heads divides n_heads;
+ *   (K+1) * n_heads / n_kv_heads <= 32 query rows per key/value head
+ *   (else SPEC_ERR_UNSUPPORTED); 0 <= K <= 64; K+1 <= T <= 2^24;
+ *   1 <= B, n_kv_heads <= 65535; scale finite.
+ *   workspace  device, at least spec_verify_attention_workspace_bytes(...)
+ *            bytes (may be 0, then workspace may be null), 256-byte aligned,
+ *            caller-owned; it holds the partial results of the context
+ *            splits and is not read before being written.
+ * Asynchronous on `stream`; allocates nothing.
+ */
+size_t spec_verify_attention_workspace_bytes(int B, int K, int T, int n_heads, int n_kv_heads,
+                                             int head_dim);
+int spec_verify_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                          void* out, int out_dtype, int B, int K, int T, int n_heads,
+                          int n_kv_heads, int head_dim, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * spec_chain_error -- read and clear the device-side error word of a chain

@@ -58,6 +58,8 @@ SIGNATURES = {
     "spec_verify_gemm_w8": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _p]),
     "spec_chain_prepare_w8": (_i, [_p, _i, _i, _p, _z]),
     "spec_verify_gemm_chain_w8": (_i, [_i, _i, _p, _p]),
+    "spec_verify_attention_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i]),
+    "spec_verify_attention": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _z, _p]),
     "spec_chain_error": (_i, [_p, ctypes.POINTER(ctypes.c_int)]),
     "spec_verify": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _z, _p]),
     "spec_verify_warped": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _f, _f, _p, _p, _p,
@@ -177,6 +179,40 @@ def verify_gemm_w8(x, w, w_scale, out=None, out_dtype=None):
         raise TypeError("out must be float32 or bfloat16")
     check(lib.spec_verify_gemm_w8(_ptr(x), _ptr(w), _ptr(w_scale), _ptr(out), code, M, d_in,
                                   d_out, _stream()))
+    return out
+
+
+def verify_attention(q, k_cache, v_cache, scale=None, out=None, out_dtype=None, workspace=None):
+    """The verify positions' attention over the KV cache.
+
+    q bf16 [B][K+1][H][D]; k_cache, v_cache bf16 [B][T][Hkv][D] with the K+1
+    verify positions last; scale defaults to 1/sqrt(D). Returns out
+    [B][K+1][H][D] (bf16 unless out_dtype / out say otherwise)."""
+    torch = _torch()
+    _need(q, torch.bfloat16, "q", 4)
+    _need(k_cache, torch.bfloat16, "k_cache", 4)
+    _need(v_cache, torch.bfloat16, "v_cache", 4)
+    B, K1, H, D = q.shape
+    T, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, T, Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError(f"q {tuple(q.shape)}, k {tuple(k_cache.shape)}, v "
+                         f"{tuple(v_cache.shape)} disagree")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty((B, K1, H, D), dtype=out_dtype or torch.bfloat16, device=q.device)
+    _need(out, out.dtype, "out", 4)
+    if tuple(out.shape) != (B, K1, H, D):
+        raise ValueError(f"out must be {(B, K1, H, D)}, got {tuple(out.shape)}")
+    code = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16}.get(out.dtype)
+    if code is None:
+        raise TypeError("out must be float32 or bfloat16")
+    nbytes = lib.spec_verify_attention_workspace_bytes(B, K1 - 1, T, H, Hkv, D)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    check(lib.spec_verify_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), code, B,
+                                    K1 - 1, T, H, Hkv, D, float(scale), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(), _stream()))
     return out
 
 

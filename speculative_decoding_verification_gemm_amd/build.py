@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["api.cpp", "gemm_stream.hip", "gemm_skinny.hip", "gemm_mfma.hip", "sampler.hip"]
+SOURCES = ["api.cpp", "gemm_stream.hip", "gemm_skinny.hip", "gemm_mfma.hip", "sampler.hip", "attention.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

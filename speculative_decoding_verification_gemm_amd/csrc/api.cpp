@@ -308,6 +308,66 @@ int spec_verify_gemm_chain_w8(int n, int M, void* workspace, void* stream) {
   return chain_run(n, M, workspace, true, stream);
 }
 
+}  // extern "C"
+
+namespace {
+// Shape checks shared by the attention entry points (SPEC_OK or an error).
+int check_attention_shape(int B, int K, int T, int H, int Hkv, int D) {
+  if (B < 1 || B > 65535) return fail(SPEC_ERR_INVALID_ARGUMENT, "B=%d outside [1, 65535]", B);
+  if (K < 0 || K > kMaxK) return fail(SPEC_ERR_INVALID_ARGUMENT, "K=%d outside [0, %d]", K, kMaxK);
+  if (T < K + 1 || T > (1 << 24))
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "T=%d outside [K+1, 2^24]", T);
+  if (H < 1 || Hkv < 1 || Hkv > 65535 || H % Hkv != 0)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "n_heads=%d, n_kv_heads=%d: kv heads must divide heads",
+                H, Hkv);
+  if (D != 128) return fail(SPEC_ERR_UNSUPPORTED, "head_dim=%d (implemented: 128)", D);
+  if ((long long)(K + 1) * (H / Hkv) > 32)
+    return fail(SPEC_ERR_UNSUPPORTED, "(K+1) * n_heads / n_kv_heads = %lld query rows > 32",
+                (long long)(K + 1) * (H / Hkv));
+  return SPEC_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_attention_workspace_bytes(int B, int K, int T, int n_heads, int n_kv_heads,
+                                             int head_dim) {
+  if (check_attention_shape(B, K, T, n_heads, n_kv_heads, head_dim) != SPEC_OK) return 0;
+  const size_t n = specv::attention_workspace_bytes(
+      B, K + 1, n_heads, n_kv_heads, specv::attention_splits(B, n_kv_heads, T));
+  return (n + 255) & ~(size_t)255;
+}
+
+int spec_verify_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                          void* out, int out_dtype, int B, int K, int T, int n_heads,
+                          int n_kv_heads, int head_dim, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (!q || !k_cache || !v_cache || !out)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "null pointer (q, k_cache, v_cache or out)");
+  if (out_dtype != SPEC_F32 && out_dtype != SPEC_BF16)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "out_dtype %d is neither SPEC_F32 nor SPEC_BF16",
+                out_dtype);
+  int rc = check_attention_shape(B, K, T, n_heads, n_kv_heads, head_dim);
+  if (rc != SPEC_OK) return rc;
+  if (!std::isfinite(scale)) return fail(SPEC_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(SPEC_ERR_ALIGNMENT, "q, k_cache and v_cache must be 16-byte aligned");
+  if (!aligned(out, out_dtype == SPEC_F32 ? 4 : 2))
+    return fail(SPEC_ERR_ALIGNMENT, "out is not aligned to its element size");
+  const size_t need = spec_verify_attention_workspace_bytes(B, K, T, n_heads, n_kv_heads, head_dim);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  }
+  if ((rc = check_device()) != SPEC_OK) return rc;
+  return launched(specv::launch_verify_attention(q, k_cache, v_cache, out, out_dtype == SPEC_BF16,
+                                                 B, K + 1, T, n_heads, n_kv_heads, scale,
+                                                 workspace, static_cast<hipStream_t>(stream)),
+                  "spec_verify_attention");
+}
+
 int spec_verify_gemm_w8(const uint16_t* x, const uint8_t* w, const float* w_scale, void* y,
                         int y_dtype, int M, int d_in, int d_out, void* stream) {
   clear_error();

@@ -71,6 +71,15 @@ hipError_t launch_gemm_skinny(const uint16_t* x, const uint16_t* w, void* y, boo
 hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
                             int K, int N, hipStream_t s);
 
+// Verify attention (attention.hip): head dimension 128, (K+1) * H / Hkv <= 32
+// query rows per key/value head. The split count depends only on the shape;
+// the workspace holds the split partials (0 bytes when there is one split).
+int attention_splits(int B, int Hkv, int T);
+size_t attention_workspace_bytes(int B, int K1, int H, int Hkv, int n_split);
+hipError_t launch_verify_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   void* out, bool out_bf16, int B, int K1, int T, int H, int Hkv,
+                                   float scale, void* workspace, hipStream_t s);
+
 hipError_t launch_softmax_rows(const float* logits, int rows, int V, float* probs, float* row_max,
                                float* row_sumexp, hipStream_t s);
 hipError_t launch_accept_probs(const float* p, const float* q, const int32_t* tokens,

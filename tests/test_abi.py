@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(sv.lib, n), n
 
@@ -33,7 +33,7 @@ def test_binding_covers_exactly_the_header(sv):
 
 
 def test_version_and_status_strings(sv):
-    assert sv.abi_version() == 3
+    assert sv.abi_version() == 4
     for code, name in [(0, b"SPEC_OK"), (-1, b"SPEC_ERR_INVALID_ARGUMENT"),
                        (-2, b"SPEC_ERR_ALIGNMENT"), (-3, b"SPEC_ERR_UNSUPPORTED"),
                        (-4, b"SPEC_ERR_WORKSPACE"), (-5, b"SPEC_ERR_HIP")]:
@@ -151,6 +151,33 @@ def test_gemm_w8_rejects(sv):
     ]
     for args, code in cases:
         assert f(*args, None) == code, args
+        assert sv.lib.spec_last_error()
+
+
+def test_attention_rejects(sv):
+    wsb = sv.lib.spec_verify_attention_workspace_bytes
+    f = sv.lib.spec_verify_attention
+    # B=1, K=4, T=4096, 32/8 heads, D=128: splits, so a workspace is needed
+    nb = wsb(1, 4, 4096, 32, 8, 128)
+    assert nb > 0 and nb % 256 == 0
+    assert wsb(64, 4, 4096, 32, 8, 128) == 0          # enough workgroups without splits
+    assert wsb(1, 4, 4096, 32, 8, 64) == 0             # unsupported head_dim
+    assert wsb(1, 8, 4096, 32, 8, 128) == 0            # 36 query rows per kv head
+    assert wsb(1, 4, 4, 32, 8, 128) == 0               # T < K+1
+
+    def call(**kw):
+        args = dict(q=A, k=A, v=A, out=A, dt=1, B=1, K=4, T=4096, H=32, Hkv=8, D=128,
+                    scale=0.088, ws=A, wsb=nb)
+        args.update(kw)
+        return f(args["q"], args["k"], args["v"], args["out"], args["dt"], args["B"], args["K"],
+                 args["T"], args["H"], args["Hkv"], args["D"], args["scale"], args["ws"],
+                 args["wsb"], None)
+    for kw, code in [(dict(q=None), -1), (dict(out=None), -1), (dict(dt=2), -1),
+                     (dict(B=0), -1), (dict(K=-1), -1), (dict(K=65), -1), (dict(T=4), -1),
+                     (dict(Hkv=5), -1), (dict(D=64), -3), (dict(K=8), -3),
+                     (dict(scale=float("nan")), -1), (dict(k=A + 8), -2), (dict(out=A + 1), -2),
+                     (dict(wsb=nb - 1), -4), (dict(ws=None), -4), (dict(ws=A + 16), -4)]:
+        assert call(**kw) == code, kw
         assert sv.lib.spec_last_error()
 
 
