@@ -21,6 +21,8 @@ dominate) and the fp64 oracle's rate on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--workload llama8b|llama70b]
                     [--batch B] [--no-graph] [--no-chain] [--no-cpu-baseline] [--w8]
+    python bench.py --attention [--batch B] [--context C]
+                                         # the verify attention alone
     python bench.py --copy-calibration   # plain device copy of known size,
                                          # the scale for HBM traffic counters
 """
@@ -53,6 +55,11 @@ def parse():
                     help="one spec_verify_gemm launch per linear instead of one chain launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=2026)
+    ap.add_argument("--attention", action="store_true",
+                    help="time spec_verify_attention alone: Llama-3.1-8B layer (32 query / 8 "
+                         "key-value heads, head_dim 128), K+1 = 5 queries per sequence")
+    ap.add_argument("--context", type=int, default=4096,
+                    help="cached tokens before the verify positions (--attention)")
     ap.add_argument("--w8", action="store_true",
                     help="FP8 E4M3 weights with per-row scales for every linear (M <= 16)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -254,6 +261,73 @@ def cpu_baseline(wl, sample_layers=None):
     }
 
 
+def attention_bench(args):
+    """spec_verify_attention on the Llama-3.1-8B layer shape: B sequences,
+    K+1 = 5 query positions each, a cache of context + 5 tokens, 32 query and
+    8 key/value heads of 128. One step is one call (one layer); the timed
+    steps replay a graph of the call. Bytes: the K/V cache read once, plus
+    queries and outputs."""
+    import math
+    import numpy as np
+    import torch
+    import oracle
+    import speculative_decoding_verification_gemm_amd as sv
+    from synth import device as sd
+
+    dev = torch.device("cuda:0")
+    B, K, H, Hkv, D = args.batch, K_DRAFT, 32, 8, 128
+    T = args.context + K + 1
+    q = sd.normal_bf16((B, K + 1, H, D), 1.0, args.seed + 1, dev)
+    k = sd.normal_bf16((B, T, Hkv, D), 1.0, args.seed + 2, dev)
+    v = sd.normal_bf16((B, T, Hkv, D), 1.0, args.seed + 3, dev)
+    out = torch.empty((B, K + 1, H, D), dtype=torch.bfloat16, device=dev)
+    nb = sv.lib.spec_verify_attention_workspace_bytes(B, K, T, H, Hkv, D)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+    call = lambda: sv.verify_attention(q, k, v, out=out, workspace=ws)  # noqa: E731
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    n = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    kv_bytes = 2 * B * T * Hkv * D * 2
+    io_bytes = 2 * q.numel() * 2
+    gbs = (kv_bytes + io_bytes) / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "verify attention: K/V cache bytes read per second (Llama-3.1-8B layer)",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) queries, keys and values)",
+        "config": {"workload": f"verify attention, {B} sequences x {K + 1} queries, cache of "
+                               f"{T} tokens, {H}/{Hkv} heads of {D}",
+                   "global_batch": B, "cache_tokens": T, "workspace_bytes": nb},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": kv_bytes + io_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on one sequence of the same inputs (bounded sample)
+        qb, kb, vb = sd.to_bits(q[:1]), sd.to_bits(k[:1]), sd.to_bits(v[:1])
+        t0 = time.perf_counter()
+        oracle.verify_attention(qb, kb, vb, 1 / math.sqrt(D))
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": 2 * T * Hkv * D * 2 / dt / 1e9, "unit": "GB/s",
+                                "cores": 1, "kind": "oracle",
+                                "sample": f"1 of {B} sequences ({dt:.2f} s), fp64 numpy"}
+    print(json.dumps(line), flush=True)
+
+
 def copy_calibration(reps=5):
     """Copy 1 GiB device to device `reps` times: each copy reads and writes
     exactly 2^30 bytes, so the counters of one copy dispatch give the ratio
@@ -283,6 +357,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.attention:
+        attention_bench(args)
         return
     import torch
     import synth
