@@ -5,7 +5,7 @@ Argument marshalling only: every call passes device pointers of caller-owned
 torch tensors and torch's current HIP stream to the C ABI declared in
 include/spec_verify.h; all computation runs in the library's HIP kernels.
 Importing this package fails if the library has not been built
-(``python -m speculative_decoding_verification_gemm_amd.build``); there is no
+(``python speculative_decoding_verification_gemm_amd/build.py``); there is no
 fallback.
 """
 
@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing; build it with "
-        "`python -m speculative_decoding_verification_gemm_amd.build`")
+        "`python speculative_decoding_verification_gemm_amd/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
 

@@ -1,10 +1,13 @@
 """Build libspecverify.so in place with hipcc for gfx950.
 
-    python -m speculative_decoding_verification_gemm_amd.build
+    python speculative_decoding_verification_gemm_amd/build.py
+
+Run it as a script (the package's own import needs the built library).
 
 Compiles every source under csrc/ into one shared library next to this file.
 """
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -31,15 +34,19 @@ COMMON = [
 def build(verbose=False):
     """Compile every source and link the shared library; returns its path."""
     with tempfile.TemporaryDirectory(prefix="specverify_build_") as tmp:
-        objs = []
+        objs, cmds = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-            lang = ["-x", "hip"]
-            cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
-            if verbose:
-                print(" ".join(cmd), flush=True)
-            subprocess.run(cmd, check=True)
+            cmds.append([HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
             objs.append(obj)
+        # one hipcc per source, run side by side
+        jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "8"))))
+        with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+            for cmd in cmds:
+                if verbose:
+                    print(" ".join(cmd), flush=True)
+            for f in [pool.submit(subprocess.run, c, check=True) for c in cmds]:
+                f.result()
         tmp_lib = LIB + ".tmp"
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         if verbose:

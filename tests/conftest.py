@@ -28,7 +28,11 @@ def golden():
 @pytest.fixture(scope="session")
 def sv():
     """The binding of libspecverify.so; builds the library first if it is absent."""
-    from speculative_decoding_verification_gemm_amd import build as _build
+    import importlib.util
+    path = os.path.join(ROOT, "speculative_decoding_verification_gemm_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("_specverify_build", path)
+    _build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(_build)
     if not os.path.exists(_build.LIB):
         _build.build()
     import speculative_decoding_verification_gemm_amd as mod
