@@ -243,7 +243,10 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
   // Arrival: every wave's device-scope output stores have completed (the
   // caller waited on vmcnt) before the barrier, so the count only rises once
   // the linear's outputs are visible at device scope.
-  unsigned long long* trace = is_chain ? sync->trace : nullptr;
+  // Global (not flat) stores: a pending flat access would make the
+  // compiler wait for every load in flight wherever it needs a vmcnt wait.
+  SPECV_GLOBAL unsigned long long* trace =
+      is_chain ? gptr_mut<unsigned long long>(sync->trace) : nullptr;
   // Release flags: the last workgroup to arrive at linear l publishes the
   // count to kReleaseLanes flags on separate 64-byte lines, and waiters poll
   // the flag of their lane, so polls do not queue on the line the arrivals
@@ -340,18 +343,21 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
   // address; its values are never used. Issuing the same loads on every
   // path keeps the compiler's vmcnt waits exact, so DEPTH stages really are
   // in flight.
+  // An exhausted cursor points every lane at the first 16 bytes of the
+  // weights, so its loads are served by the cache instead of HBM.
   auto load = [&](u32x4 (&buf)[U][RPL], const LinSched& s, const Cursor& cur)
       __attribute__((always_inline)) {
     const int rb = bid + cur.j * G;
+    const int live = -(int)cur.valid;  // all ones, or zero for an exhausted cursor
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
-      const int row = min(rb * NR + grp * RPL + r, s.N - 1);
+      const int row = min(rb * NR + grp * RPL + r, s.N - 1) & live;
       const SPECV_GLOBAL u32x4* base =
           gptr<u32x4>(static_cast<const char*>(s.w) + (size_t)row * s.K * F::kEsz);
 #pragma unroll
       for (int u = 0; u < U; ++u)
         buf[u][r] = __builtin_nontemporal_load(
-            base + (min(kofs(cur.it, u), s.K - F::kEpl) >> F::kEplShift));
+            base + ((min(kofs(cur.it, u), s.K - F::kEpl) >> F::kEplShift) & live));
     }
   };
 
@@ -515,34 +521,44 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
 
   // One pipeline step on buffer IB: compute stage c, refill the buffer with
   // stage p (DEPTH stages ahead), close the row block / linear if c was its
-  // last stage, advance c.
+  // last stage, advance c. Once c is exhausted a step only issues its
+  // (cache-served) refill. Every step issues the same loads on every path,
+  // so between the refill of a buffer and its next use exactly DEPTH - 1
+  // other stages' loads are issued on every path through the loop, and the
+  // compiler's wait before the products leaves those in flight.
   auto step = [&](auto IB) __attribute__((always_inline)) {
     constexpr int ib = decltype(IB)::value;
     auto& buf = wbuf[ib];
-    if (c.it == 0 && c.j == 0) {
-      // first stage of a linear: its x may depend on the previous linear
-      if (is_chain && c.l > 0) wait(c.l - 1);
-      stage_x(cs, 0);
-      if (trace && tid == 0) trace[((size_t)c.l * G + bid) * 4 + 2] = wall_clock64();
-    } else if (c.it % cs.ipc == 0 && cs.ipc < cs.n_it) {
-      // next activation chunk (chunk 0 again for a new row block), once
-      // every wave is done with the previous one
-      __syncthreads();
-      stage_x(cs, c.it / cs.ipc);
+    const bool live = c.valid;
+    bool closes_rb = false;
+    if (live) {
+      if (c.it == 0 && c.j == 0) {
+        // first stage of a linear: its x may depend on the previous linear
+        if (is_chain && c.l > 0) wait(c.l - 1);
+        stage_x(cs, 0);
+        if (trace && tid == 0) trace[((size_t)c.l * G + bid) * 4 + 2] = wall_clock64();
+      } else if (c.it % cs.ipc == 0 && cs.ipc < cs.n_it) {
+        // next activation chunk (chunk 0 again for a new row block), once
+        // every wave is done with the previous one
+        __syncthreads();
+        stage_x(cs, c.it / cs.ipc);
+      }
+      compute(buf, cs, c);
+      closes_rb = c.it == cs.n_it - 1;
+      if (closes_rb) finish(cs, c);  // output stores precede the refill load
     }
-    compute(buf, cs, c);
-    const bool closes_rb = c.it == cs.n_it - 1;
-    if (closes_rb) finish(cs, c);  // output stores precede the refill load
-    load(buf, ps, p);  // unconditional: an exhausted cursor loads a clamped valid address
+    load(buf, ps, p);  // unconditional (see load)
     if (p.valid) advance(p, ps);
-    if (closes_rb && c.j == cs.my_rb - 1 && is_chain) {
-      if (trace && tid == 0) trace[((size_t)c.l * G + bid) * 4 + 3] = wall_clock64();
-      if (storer) wait_vmcnt<0>();  // output stores complete (and, in order, older loads)
-      arrive(c.l);
+    if (live) {
+      if (closes_rb && c.j == cs.my_rb - 1 && is_chain) {
+        if (trace && tid == 0) trace[((size_t)c.l * G + bid) * 4 + 3] = wall_clock64();
+        if (storer) wait_vmcnt<0>();  // output stores complete (and, in order, older loads)
+        arrive(c.l);
+      }
+      const int l_before = c.l;
+      advance(c, cs);
+      arrive_empty(l_before + 1, c.valid ? c.l : n_lin);
     }
-    const int l_before = c.l;
-    advance(c, cs);
-    arrive_empty(l_before + 1, c.valid ? c.l : n_lin);
   };
 
   zero_acc();
@@ -555,14 +571,11 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
     load(wbuf[decltype(D)::value], ps, p);
     if (p.valid) advance(p, ps);
   });
+  // Whole rounds of DEPTH steps only: a round that c leaves mid-way still
+  // issues its remaining refills, so no path re-enters the loop with fewer
+  // loads in flight than the waits assume.
   while (c.valid) {
-    bool more = true;
-    static_for<DEPTH>([&](auto D) __attribute__((always_inline)) {
-      if (more) {
-        step(D);
-        more = c.valid;
-      }
-    });
+    static_for<DEPTH>([&](auto D) __attribute__((always_inline)) { step(D); });
   }
   // Refills past the end are never consumed; let them land before exit.
   wait_vmcnt<0>();
