@@ -62,6 +62,11 @@ def parse():
                     help="cached tokens before the verify positions (--attention)")
     ap.add_argument("--w8", action="store_true",
                     help="FP8 E4M3 weights with per-row scales for every linear (M <= 16)")
+    ap.add_argument("--lm-head", choices=["chain", "fused"], default="chain",
+                    help="chain: the lm-head is the last linear of the chain launch and "
+                         "spec_verify reads its logits; fused: the chain holds the stack only "
+                         "and spec_verify runs the lm-head with the target rows' softmax "
+                         "statistics fused into its epilogue (bf16 weights, M <= 16)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (the known-size "
                          "reference that scales FETCH_SIZE / WRITE_SIZE counters)")
@@ -100,12 +105,13 @@ def load_traffic(name):
 class Workload:
     """Device-resident inputs of one verify step."""
 
-    def __init__(self, stack, B, K, seed, dev, w8=False):
+    def __init__(self, stack, B, K, seed, dev, w8=False, fused_lm_head=False):
         import torch
         import synth
         from synth import device as sd
 
         self.stack, self.B, self.K, self.dev, self.w8 = stack, B, K, dev, w8
+        self.fused_lm_head = fused_lm_head  # lm-head runs inside spec_verify
         self.M = B * (K + 1)
         self.linears = []  # (name, x, w, y)
         self.scales = []   # FP8 weights: per-row scales of each linear
@@ -161,7 +167,8 @@ class Workload:
                         self.target_logits.view(self.M, self.V)))
         else:
             lin = [(x, w, y) for _, x, w, y in self.linears]
-            lin.append((self.hidden, self.lm_head, self.target_logits.view(self.M, self.V)))
+            if not self.fused_lm_head:
+                lin.append((self.hidden, self.lm_head, self.target_logits.view(self.M, self.V)))
         self.chain = sv.Chain(lin, self.dev)
 
     def gemm_phase(self, sv):
@@ -173,12 +180,14 @@ class Workload:
                 sv.verify_gemm_w8(x, w, sc, out=y)
             else:
                 sv.verify_gemm(x, w, out=y)
-        self.lm_head_gemm(sv)
+        if not self.fused_lm_head:
+            self.lm_head_gemm(sv)
 
     def sampling_phase(self, sv):
+        lm = {"hidden": self.hidden, "lm_head": self.lm_head} if self.fused_lm_head else {}
         sv.verify(self.target_logits, self.draft_logits, self.draft_tokens, self.u_accept,
                   self.u_sample, workspace=self.workspace, out_tokens=self.out_tokens,
-                  n_emitted=self.n_emitted)
+                  n_emitted=self.n_emitted, **lm)
 
     def gemm_bytes(self):
         """Algorithmic HBM bytes of the GEMM phase: every weight once, every
@@ -187,18 +196,22 @@ class Workload:
         for (_, x, w, y), sc in zip(self.linears, self.scales):
             total += w.numel() * w.element_size() + 2 * x.numel() + 2 * y.numel()
             total += 0 if sc is None else 4 * sc.numel()
-        total += self.lm_head.numel() * self.lm_head.element_size() + 2 * self.hidden.numel()
-        total += 4 * self.target_logits.numel() + (0 if self.lm_scale is None else 4 * self.V)
+        if not self.fused_lm_head:
+            total += self.lm_head_bytes()
         return total
+
+    def lm_head_bytes(self):
+        return (self.lm_head.numel() * self.lm_head.element_size() + 2 * self.hidden.numel()
+                + 4 * self.target_logits.numel() + (0 if self.lm_scale is None else 4 * self.V))
 
     def gemm_flops(self):
         n = sum(2 * x.shape[0] * w.numel() for _, x, w, _ in self.linears)
-        return n + 2 * self.M * self.lm_head.numel()
+        return n + (0 if self.fused_lm_head else 2 * self.M * self.lm_head.numel())
 
     def n_gemm_launches(self):
         if getattr(self, "chain", None) is not None:
             return 1
-        return len(self.linears) + 1
+        return len(self.linears) + (0 if self.fused_lm_head else 1)
 
 
 def cpu_baseline(wl, sample_layers=None):
@@ -373,7 +386,11 @@ def main():
         print(f"--w8 covers M <= 16 (the weight-streaming kernel); B={B} gives M={B * (K + 1)}",
               file=sys.stderr)
         sys.exit(2)
-    wl = Workload(stack, B, K, args.seed, dev, w8=args.w8)
+    fused = args.lm_head == "fused"
+    if fused and (args.w8 or B * (K + 1) > 16):
+        print("--lm-head fused covers bf16 weights at M <= 16", file=sys.stderr)
+        sys.exit(2)
+    wl = Workload(stack, B, K, args.seed, dev, w8=args.w8, fused_lm_head=fused)
     wl.make_drafts(sv, synth.draft_noise_sigma(key, 0.8), args.seed)
     use_chain = not args.no_chain and wl.M <= 16
     if use_chain:
@@ -427,7 +444,8 @@ def main():
     gemm_flops = wl.gemm_flops()
     launches = wl.n_gemm_launches()
     achieved = gemm_bytes / (ms_gemm * 1e-3) / 1e9
-    traffic = load_traffic(f"traffic_gemm_stream_{'w8_' if args.w8 else ''}{args.workload}_b{B}")
+    traffic = load_traffic(f"traffic_gemm_stream_{'w8_' if args.w8 else ''}{args.workload}_b{B}"
+                           + ("_stack" if fused else ""))
     # The GEMM phase is bound by whichever floor is higher: reading the
     # weights at the HBM peak, or the FLOPs at the dense bf16 MFMA peak.
     mfma_bound = gemm_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > gemm_bytes / (HBM_PEAK_GBS * 1e9)
@@ -469,11 +487,13 @@ def main():
             "vocab": wl.V,
             "graph": not args.no_graph,
             "gemm_launch": "chain" if use_chain else "per-linear",
+            "lm_head": ("in spec_verify, softmax statistics fused into its epilogue" if fused
+                        else "last linear of the GEMM phase"),
             "weights": "fp8_e4m3 + fp32 row scale" if args.w8 else "bf16",
         },
         "pct_hbm_peak_in_verify": 100.0 * achieved / HBM_PEAK_GBS,
         "ms_gemm_phase": ms_gemm,
-        "ms_sampling_phase": ms_samp,
+        "ms_sampling_phase": ms_samp,  # with --lm-head fused: lm-head + sampling
         "sampling_share": ms_samp / ms_step,
         "ms_step_p10_p50_p90": [t_step[n // 10], med(t_step), t_step[(9 * n) // 10]],
         "wall_s": wall,
@@ -484,8 +504,10 @@ def main():
         "roofline": {
             **roof,
             "kernel": (("gemm_stream FP8-weight chain" if args.w8 else "gemm_stream chain")
-                       + " (all stack linears + lm-head in one launch)" if use_chain
-                       else "per-linear spec_verify_gemm launches (stack linears + lm-head)"),
+                       + (" (all stack linears in one launch)" if fused else
+                          " (all stack linears + lm-head in one launch)") if use_chain
+                       else "per-linear spec_verify_gemm launches (stack linears"
+                       + ("" if fused else " + lm-head") + ")"),
             "traffic": traffic,
             "hbm_gbs": achieved,
             "hbm_frac": achieved / HBM_PEAK_GBS,

@@ -507,11 +507,32 @@ int spec_verify_warped(const uint16_t* hidden, const uint16_t* lm_head, int d,
   int cus = 0;
   if ((rc = check_device(&cus)) != SPEC_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (lm_head && (rc = run_gemm(hidden, lm_head, target_logits, false, M, d, V, cus, s)) != SPEC_OK)
-    return rc;
+  // With the streaming lm-head (M within its positions) the target rows'
+  // softmax statistics are folded into the GEMM's epilogue, so the logits
+  // are never re-read for them.
+  specv::LogitStats tstats{};
+  int parts = 0;
+  if (lm_head && M <= specv::kMaxStreamM) {
+    tstats = specv::target_stats_slot(workspace, B, K, V, t_target);
+    parts = cus * stream_wgs_per_cu(M);
+    if (!tstats.pmax || parts > specv::kMaxStatParts) {
+      tstats = specv::LogitStats{};
+      parts = 0;
+    }
+  }
+  if (lm_head) {
+    if (parts > 0)
+      rc = launched(specv::launch_gemm_stream(hidden, lm_head, nullptr, target_logits, false,
+                                              false, M, d, V, parts, s, &tstats),
+                    "spec_verify lm-head");
+    else
+      rc = run_gemm(hidden, lm_head, target_logits, false, M, d, V, cus, s);
+    if (rc != SPEC_OK) return rc;
+  }
   return launched(specv::launch_verify_sampling(target_logits, draft_logits, draft_tokens, u_accept,
                                                 u_sample, B, K, V, out_tokens, n_emitted,
-                                                workspace, t_target, t_draft, s),
+                                                workspace, t_target, t_draft, s,
+                                                parts > 0 ? &tstats : nullptr, parts),
                   "spec_verify sampling");
 }
 

@@ -44,6 +44,9 @@
 // needs clearing between launches; a bounded spin turns a stalled barrier
 // into an error flag instead of a hang.
 
+#include <limits.h>
+#include <math.h>
+
 #include <type_traits>
 
 #include "common.h"
@@ -203,7 +206,8 @@ struct Cursor {
 template <int M, int RPL, int U, int KCMAX, int DEPTH, bool W8>
 __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinear single,
                                                                      const StreamLinear* chain,
-                                                                     int n_lin, ChainSync* sync) {
+                                                                     int n_lin, ChainSync* sync,
+                                                                     LogitStats st) {
   using S = Stream<M, RPL, U, KCMAX, W8>;
   using F = WFmt<W8>;
   constexpr int NR = S::NR, EPI = S::EPI;
@@ -215,6 +219,14 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, sub = lane & 15;
   const int bid = blockIdx.x, G = gridDim.x;
   const bool is_chain = chain != nullptr;
+  // Fused softmax statistics of the outputs (single launch of a logits
+  // linear): the thread of row 0 of each position's 16-row group keeps the
+  // workgroup's running maximum, fp64 sum of exp((l - max) * inv) and first
+  // index of the maximum.
+  const bool want_stats = !is_chain && st.pmax != nullptr;
+  float st_max = -INFINITY;
+  double st_sum = 0.0;
+  int st_arg = INT_MAX;
   unsigned* counts = is_chain ? reinterpret_cast<unsigned*>(sync + 1) : nullptr;
   if (is_chain &&
       (sync->magic != (W8 ? kChainMagicW8 : kChainMagic) || sync->n != n_lin || sync->M != M)) {
@@ -439,6 +451,42 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
       }
     }
   };
+  // One row block's outputs v of one position, held by the 16 consecutive
+  // threads of its rows (rows past N are left out), folded into the running
+  // statistics of the group's row-0 thread. Sums are fp64, relative to the
+  // running maximum, in row-block order: deterministic.
+  auto fold_stats = [&](float v, bool ok, int row, int rr) __attribute__((always_inline)) {
+    const float lv = ok ? v : -INFINITY;
+    float bm = lv;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o, 16));
+    if (st.greedy) {
+      int a = (ok && lv == bm) ? row : INT_MAX;
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) a = min(a, __shfl_xor(a, o, 16));
+      if (rr == 0 && bm != -INFINITY) {
+        if (bm > st_max) {
+          st_max = bm;
+          st_arg = a;
+        } else if (bm == st_max) {
+          st_arg = min(st_arg, a);
+        }
+      }
+    } else {
+      double e = ok ? exp(((double)lv - (double)bm) * st.inv) : 0.0;
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) e += __shfl_xor(e, o, 16);
+      if (rr == 0 && bm != -INFINITY) {
+        if (bm > st_max) {
+          st_sum = st_sum * exp(((double)st_max - (double)bm) * st.inv) + e;
+          st_max = bm;
+        } else {
+          st_sum += e * exp(((double)bm - (double)st_max) * st.inv);
+        }
+      }
+    }
+  };
+
   // Row block done: partial sums reduced within each lane group (DPP), then
   // across the waves through LDS in wave order, and stored. Alternate row
   // blocks use alternate LDS buffers, so one barrier per row block suffices:
@@ -477,8 +525,9 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
     for (int i = tid; i < NR * M; i += kStreamThreads) {
       const int m = i / NR, rr = i - m * NR;
       const int row = rb * NR + rr;
+      float v = 0.0f;
       if (row < s.N) {
-        float v = red[rr * M + m];
+        v = red[rr * M + m];
 #pragma unroll
         for (int w = 1; w < kStreamWaves; ++w) v += red[(w * NR + rr) * M + m];  // wave order
         if constexpr (W8) {
@@ -501,6 +550,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
           gptr_mut<float>(s.y)[o] = v;
         }
       }
+      if (want_stats) fold_stats(v, row < s.N, row, rr);
     }
     zero_acc();
   };
@@ -579,6 +629,12 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
   }
   // Refills past the end are never consumed; let them land before exit.
   wait_vmcnt<0>();
+  if (want_stats && tid < NR * M && tid % NR == 0) {
+    const size_t o = (size_t)(tid / NR) * st.stride + bid;
+    gptr_mut<float>(st.pmax)[o] = st_max;
+    gptr_mut<double>(st.psum)[o] = st_sum;
+    gptr_mut<int32_t>(st.parg)[o] = st_arg;
+  }
 
   // exit: the last workgroup out advances the generation
   if (is_chain) {
@@ -598,14 +654,14 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
 
 template <int M, int RPL, int U, int KCMAX, int DEPTH, bool W8>
 static hipError_t launch_m(const StreamLinear& single, const StreamLinear* chain, int n_lin,
-                           ChainSync* sync, int grid, hipStream_t s) {
+                           ChainSync* sync, const LogitStats& st, int grid, hipStream_t s) {
   using S = Stream<M, RPL, U, KCMAX, W8>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH, W8>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLdsBytes);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((gemm_stream_kernel<M, RPL, U, KCMAX, DEPTH, W8>), dim3(grid),
-                     dim3(kStreamThreads), S::kLdsBytes, s, single, chain, n_lin, sync);
+                     dim3(kStreamThreads), S::kLdsBytes, s, single, chain, n_lin, sync, st);
   return hipGetLastError();
 }
 
@@ -702,13 +758,13 @@ int stream_max_wgs_per_cu(int M, bool w8) {
 }
 
 static hipError_t launch_gemm_stream_any(const StreamLinear& single, const StreamLinear* chain,
-                                         int n_lin, ChainSync* sync, int M, bool w8, int grid,
-                                         hipStream_t s) {
+                                         int n_lin, ChainSync* sync, const LogitStats& st, int M,
+                                         bool w8, int grid, hipStream_t s) {
   if (w8) {
     switch (M) {
 #define SPECV_CASE8(MM, RPL, U, KC, D) \
   case MM:                             \
-    return launch_m<MM, RPL, U, KC, D, true>(single, chain, n_lin, sync, grid, s);
+    return launch_m<MM, RPL, U, KC, D, true>(single, chain, n_lin, sync, st, grid, s);
       SPECV_STREAM_W8_TABLE(SPECV_CASE8)
 #undef SPECV_CASE8
       default:
@@ -718,7 +774,7 @@ static hipError_t launch_gemm_stream_any(const StreamLinear& single, const Strea
   switch (M) {
 #define SPECV_CASE(MM, RPL, U, KC, D) \
   case MM:                            \
-    return launch_m<MM, RPL, U, KC, D, false>(single, chain, n_lin, sync, grid, s);
+    return launch_m<MM, RPL, U, KC, D, false>(single, chain, n_lin, sync, st, grid, s);
     SPECV_STREAM_TABLE(SPECV_CASE)
 #undef SPECV_CASE
     default:
@@ -728,17 +784,25 @@ static hipError_t launch_gemm_stream_any(const StreamLinear& single, const Strea
 
 hipError_t launch_gemm_stream(const uint16_t* x, const void* w, const float* w_scale, void* y,
                               bool out_bf16, bool w8, int M, int K, int N, int grid,
-                              hipStream_t s) {
+                              hipStream_t s, const LogitStats* stats) {
   StreamLinear d{x, w, w_scale, y, K, N, out_bf16 ? 1 : 0, 0};
   const int n_rb = (N + (int)stream_rows_per_block(M) - 1) / (int)stream_rows_per_block(M);
-  if (grid > n_rb) grid = n_rb;
-  return launch_gemm_stream_any(d, nullptr, 1, nullptr, M, w8, grid, s);
+  LogitStats st{};
+  if (stats && stats->pmax && !out_bf16) {
+    // every workgroup writes its partials, so keep the whole grid (those
+    // without row blocks write empty ones)
+    if (grid > stats->stride) return hipErrorInvalidValue;
+    st = *stats;
+  } else if (grid > n_rb) {
+    grid = n_rb;
+  }
+  return launch_gemm_stream_any(d, nullptr, 1, nullptr, st, M, w8, grid, s);
 }
 
 hipError_t launch_gemm_chain(const StreamLinear* chain, int n_lin, ChainSync* sync, int M, bool w8,
                              int grid, hipStream_t s) {
   StreamLinear none{nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0};
-  return launch_gemm_stream_any(none, chain, n_lin, sync, M, w8, grid, s);
+  return launch_gemm_stream_any(none, chain, n_lin, sync, LogitStats{}, M, w8, grid, s);
 }
 
 }  // namespace specv

@@ -57,13 +57,31 @@ __host__ __device__ inline size_t chain_counts_bytes(int n) {
   return chain_release_offset(n) * 4 + (size_t)n * kReleaseLanes * 64;
 }
 
+// Softmax statistics of a logits linear, fused into the streaming kernel's
+// epilogue: every workgroup folds the outputs of its row blocks into a
+// running (max, sum of exp((l - max) * inv)) per output position -- or, for
+// a greedy row, the first index of the maximum -- and writes one partial per
+// position. Row m's partials are at [m * stride, m * stride + grid); a
+// workgroup without row blocks writes (-inf, 0, INT_MAX).
+struct LogitStats {
+  float* pmax;    // nullptr: no statistics
+  double* psum;
+  int32_t* parg;
+  double inv;     // inverse temperature (unused when greedy)
+  int greedy;
+  int stride;     // partials per position; at least the grid
+};
+// Most workgroups a fused-statistics launch may use (partials per position).
+constexpr int kMaxStatParts = 1024;
+
 size_t stream_rows_per_block(int M);
 int stream_max_wgs_per_cu(int M, bool w8);
 // Streaming kernel, one linear: bf16 weights (w_scale null) or FP8 E4M3
 // weights with per-row scales (w8).
+// `stats` (nullable): fused softmax statistics of y (fp32 y only).
 hipError_t launch_gemm_stream(const uint16_t* x, const void* w, const float* w_scale, void* y,
                               bool out_bf16, bool w8, int M, int K, int N, int grid,
-                              hipStream_t s);
+                              hipStream_t s, const LogitStats* stats = nullptr);
 hipError_t launch_gemm_chain(const StreamLinear* chain, int n_lin, ChainSync* sync, int M, bool w8,
                              int grid, hipStream_t s);
 hipError_t launch_gemm_skinny(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
@@ -93,10 +111,18 @@ hipError_t launch_sample_probs(const float* p, const float* q, const int32_t* n_
 size_t verify_workspace_bytes(int B, int K, int V);
 // t_target, t_draft: temperatures (> 0), or 0 for greedy (one-hot at the
 // row's first maximum).
+// `target_stats` (nullable): the target rows' statistics were written by
+// the lm-head launch (target_stats_slot), so only the draft rows are scanned
+// for theirs; `parts` partials per target row.
 hipError_t launch_verify_sampling(const float* target_logits, const float* draft_logits,
                                   const int32_t* tokens, const float* u_accept,
                                   const float* u_sample, int B, int K, int V, int32_t* out_tokens,
                                   int32_t* n_emitted, void* workspace, float t_target,
-                                  float t_draft, hipStream_t s);
+                                  float t_draft, hipStream_t s,
+                                  const LogitStats* target_stats = nullptr, int parts = 0);
+// Where the lm-head launch of spec_verify writes the target rows' fused
+// statistics inside its workspace; pmax is nullptr when B * (K + 1) exceeds
+// the streaming kernel's positions.
+LogitStats target_stats_slot(void* workspace, int B, int K, int V, float t_target);
 
 }  // namespace specv

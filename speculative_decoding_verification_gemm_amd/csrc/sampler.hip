@@ -385,6 +385,11 @@ struct VerifyWs {
   int32_t* nacc;  // [B]
   double* rsum;   // [B][C] residual (or bonus p) chunk sums
   double* qsum;   // [B][C] p chunk sums for the empty-residual fallback
+  // target rows' statistics fused into the lm-head launch: [B(K+1)][kMaxStatParts]
+  // (null when B(K+1) exceeds the streaming kernel's positions)
+  float* tmax;
+  double* tsum;
+  int32_t* targ;
 };
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -413,8 +418,33 @@ static VerifyWs carve(void* base, int B, int K, int V, size_t* total) {
   off = align256(off + (size_t)B * C * sizeof(double));
   ws.qsum = reinterpret_cast<double*>(p + off);
   off = align256(off + (size_t)B * C * sizeof(double));
+  const size_t M = (size_t)B * (K + 1);
+  ws.tmax = nullptr;
+  ws.tsum = nullptr;
+  ws.targ = nullptr;
+  if (M <= (size_t)kMaxStreamM) {
+    const size_t P = M * kMaxStatParts;
+    ws.tmax = reinterpret_cast<float*>(p + off);
+    off = align256(off + P * sizeof(float));
+    ws.tsum = reinterpret_cast<double*>(p + off);
+    off = align256(off + P * sizeof(double));
+    ws.targ = reinterpret_cast<int32_t*>(p + off);
+    off = align256(off + P * sizeof(int32_t));
+  }
   if (total) *total = off;
   return ws;
+}
+
+LogitStats target_stats_slot(void* workspace, int B, int K, int V, float t_target) {
+  const VerifyWs ws = carve(workspace, B, K, V, nullptr);
+  LogitStats st{};
+  st.pmax = ws.tmax;
+  st.psum = ws.tsum;
+  st.parg = ws.targ;
+  st.greedy = t_target == 0.0f;
+  st.inv = st.greedy ? 0.0 : 1.0 / (double)t_target;
+  st.stride = kMaxStatParts;
+  return st;
 }
 
 size_t verify_workspace_bytes(int B, int K, int V) {
@@ -430,15 +460,18 @@ __device__ __forceinline__ const float* verify_row(const float* tl, const float*
   return row < n_target ? tl + (size_t)row * V : dl + (size_t)(row - n_target) * V;
 }
 
+// row0: first row scanned (B(K+1) when the target rows' statistics come from
+// the lm-head launch, so only draft rows are scanned).
 __global__ __launch_bounds__(kScanThreads) void stats_partial_kernel(const float* __restrict__ tl,
                                                                      const float* __restrict__ dl,
                                                                      int B, int K, int V,
-                                                                     VerifyWs ws, Warp wp) {
+                                                                     VerifyWs ws, Warp wp,
+                                                                     int row0) {
   __shared__ double red_d[kScanThreads / kWave];
   __shared__ float red_f[kScanThreads / kWave];
   __shared__ int red_i[kScanThreads / kWave];
   const int C = (V + kChunk - 1) / kChunk;
-  const int row = blockIdx.x / C, c = blockIdx.x - row * C;
+  const int row = row0 + (int)blockIdx.x / C, c = blockIdx.x - (row - row0) * C;
   const bool target = row < B * (K + 1);
   const bool greedy = target ? wp.gt : wp.gd;
   const double inv = target ? wp.it : wp.id;
@@ -476,38 +509,71 @@ __global__ __launch_bounds__(kScanThreads) void stats_partial_kernel(const float
   }
 }
 
+// Row statistics from partials: the maximum over partials, the fp64 sum of
+// psum * exp((pmax - max) * inv) in a fixed order (lane-strided, then a
+// fixed shuffle tree) and, for greedy rows, the smallest first-index among
+// partials holding the maximum. Chunk partials (contiguous chunks) and the
+// lm-head's per-workgroup partials merge alike; empty partials hold -inf.
+__device__ __forceinline__ void merge_partials(const float* pm, const double* ps, const int32_t* pa,
+                                               int n, bool greedy, double inv, float* M_out,
+                                               double* S_out, int* arg_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float M = -INFINITY;
+  for (int c = lane; c < n; c += kWave) M = fmaxf(M, pm[c]);
+  M = wave_max_f32(M);
+  double S = 0.0;
+  int arg = INT_MAX;
+  if (greedy) {
+    for (int c = lane; c < n; c += kWave)
+      if (pm[c] == M) arg = min(arg, (int)pa[c]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) arg = min(arg, __shfl_xor(arg, o, kWave));
+    S = 1.0;
+  } else {
+    for (int c = lane; c < n; c += kWave)
+      if (pm[c] != -INFINITY) S += ps[c] * exp(((double)pm[c] - (double)M) * inv);
+    S = wave_sum_f64(S);
+  }
+  *M_out = M;
+  *S_out = S;
+  *arg_out = greedy ? (arg == INT_MAX ? -1 : arg) : -1;
+}
+
+// tstats: the target rows' per-workgroup partials from the lm-head launch
+// (tparts of them per row, stride kMaxStatParts), or tparts = 0 to use the
+// chunk partials of stats_partial_kernel for every row.
 __global__ __launch_bounds__(kWave) void verify_accept_kernel(
     const float* __restrict__ tl, const float* __restrict__ dl, const int32_t* __restrict__ tokens,
-    const float* __restrict__ u_accept, int B, int K, int V, VerifyWs ws, Warp wp) {
+    const float* __restrict__ u_accept, int B, int K, int V, VerifyWs ws, Warp wp, int tparts) {
   __shared__ float smax[2 * 64 + 1];
   __shared__ double ssum[2 * 64 + 1];
   __shared__ int sarg[2 * 64 + 1];
   const int b = blockIdx.x, lane = threadIdx.x;
   const int C = (V + kChunk - 1) / kChunk;
-  // local index i: 0..K target rows, K+1..2K draft rows
-  for (int i = lane; i < 2 * K + 1; i += kWave) {
+  // local index i: 0..K target rows, K+1..2K draft rows; the whole wave
+  // merges one row's partials at a time
+  for (int i = 0; i < 2 * K + 1; ++i) {
     const int row = i <= K ? b * (K + 1) + i : B * (K + 1) + b * K + (i - K - 1);
     const bool greedy = i <= K ? wp.gt : wp.gd;
     const double inv = i <= K ? wp.it : wp.id;
-    float M = -INFINITY;
-    for (int c = 0; c < C; ++c) M = fmaxf(M, ws.pmax[(size_t)row * C + c]);
-    double S = 0.0;
-    int arg = -1;
-    if (greedy) {  // the first chunk holding the maximum has the first index
-      S = 1.0;
-      for (int c = C - 1; c >= 0; --c)
-        if (ws.pmax[(size_t)row * C + c] == M) arg = ws.parg[(size_t)row * C + c];
+    float M;
+    double S;
+    int arg;
+    if (i <= K && tparts > 0) {
+      const size_t o = (size_t)row * kMaxStatParts;
+      merge_partials(ws.tmax + o, ws.tsum + o, ws.targ + o, tparts, greedy, inv, &M, &S, &arg);
     } else {
-      for (int c = 0; c < C; ++c)
-        S += ws.psum[(size_t)row * C + c] *
-             exp(((double)ws.pmax[(size_t)row * C + c] - (double)M) * inv);
+      const size_t o = (size_t)row * C;
+      merge_partials(ws.pmax + o, ws.psum + o, ws.parg + o, C, greedy, inv, &M, &S, &arg);
     }
-    ws.fmax[row] = M;
-    ws.fsum[row] = S;
-    ws.farg[row] = arg;
-    smax[i] = M;
-    ssum[i] = S;
-    sarg[i] = arg;
+    if (lane == 0) {
+      ws.fmax[row] = M;
+      ws.fsum[row] = S;
+      ws.farg[row] = arg;
+      smax[i] = M;
+      ssum[i] = S;
+      sarg[i] = arg;
+    }
   }
   __syncthreads();
   bool acc = false;
@@ -654,7 +720,8 @@ __global__ __launch_bounds__(kScanThreads) void verify_draw_kernel(
 hipError_t launch_verify_sampling(const float* tl, const float* dl, const int32_t* tokens,
                                   const float* u_accept, const float* u_sample, int B, int K, int V,
                                   int32_t* out_tokens, int32_t* n_emitted, void* workspace,
-                                  float t_target, float t_draft, hipStream_t s) {
+                                  float t_target, float t_draft, hipStream_t s,
+                                  const LogitStats* target_stats, int parts) {
   const VerifyWs ws = carve(workspace, B, K, V, nullptr);
   const int C = (V + kChunk - 1) / kChunk;
   const int R = B * (2 * K + 1);
@@ -663,10 +730,13 @@ hipError_t launch_verify_sampling(const float* tl, const float* dl, const int32_
   wp.gd = t_draft == 0.0f;
   wp.it = wp.gt ? 0.0 : 1.0 / (double)t_target;
   wp.id = wp.gd ? 0.0 : 1.0 / (double)t_draft;
-  hipLaunchKernelGGL(stats_partial_kernel, dim3(R * C), dim3(kScanThreads), 0, s, tl, dl, B, K, V,
-                     ws, wp);
+  const bool fused = target_stats && target_stats->pmax && target_stats->pmax == ws.tmax &&
+                     parts > 0 && parts <= kMaxStatParts;
+  const int row0 = fused ? B * (K + 1) : 0;
+  hipLaunchKernelGGL(stats_partial_kernel, dim3((R - row0) * C), dim3(kScanThreads), 0, s, tl, dl,
+                     B, K, V, ws, wp, row0);
   hipLaunchKernelGGL(verify_accept_kernel, dim3(B), dim3(kWave), 0, s, tl, dl, tokens, u_accept,
-                     B, K, V, ws, wp);
+                     B, K, V, ws, wp, fused ? parts : 0);
   hipLaunchKernelGGL(resid_partial_kernel, dim3(B * C), dim3(kScanThreads), 0, s, tl, dl, B, K, V,
                      ws, wp);
   hipLaunchKernelGGL(verify_draw_kernel, dim3(B), dim3(kScanThreads), 0, s, tl, dl, tokens,
