@@ -10,6 +10,8 @@
 #include "common.h"
 #include "internal.h"
 
+#define SPECV_TILE_GLOBAL __attribute__((address_space(1)))
+
 namespace specv {
 
 // ---------------------------------------------------------------------------
@@ -128,6 +130,212 @@ __global__ __launch_bounds__(kMfmaThreads) void gemm_mfma_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined tile kernel (K a multiple of 64): eight waves, LDS ring filled by
+// direct-to-LDS loads
+// ---------------------------------------------------------------------------
+//
+// Both operands reach LDS as whole 128-byte lines: one load instruction of a
+// wave moves 8 rows x 128 bytes (64 reduction elements) straight into LDS
+// (global_load_lds, no registers). Inside a row the eight 16-byte units are
+// stored XOR-swizzled by the row index mod 8, so the fragment reads of
+// v_mfma_f32_16x16x32_bf16 (lane l: row l % 16, unit l / 16) hit eight
+// distinct bank groups in every eight lanes. S tile stages are in flight;
+// each wave waits (vmcnt) for its own loads of the stage it computes on and
+// a workgroup barrier makes every wave's loads visible. The barrier is a
+// bare s_barrier: a memory fence there would make the compiler wait for all
+// loads in flight. Tiles are numbered so that the workgroups of one XCD
+// (bid mod 8) take consecutive tiles, which share weight tiles in that XCD's
+// L2.
+
+constexpr int kTileThreads = 512;
+constexpr int kTileBK = 64;  // reduction elements per stage (one 128-byte line per row)
+
+template <int BM, int BN, int WM, int S>
+struct TileCfg {
+  static constexpr int WN = 8 / WM;
+  static constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  static constexpr int ROWS = BM + BN;         // LDS rows per stage (x rows, then w rows)
+  static constexpr int L = ROWS / 64;          // load instructions per wave per stage
+  static constexpr int STAGE_BYTES = ROWS * 128;
+  static constexpr int LDS_BYTES = S * STAGE_BYTES;
+  static_assert(TM >= 1 && TN >= 1 && BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
+  static_assert(ROWS % 64 == 0, "whole load instructions per wave");
+  static_assert(S >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring");
+};
+
+__device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Address-space casts live in device helpers: the kernel body is also
+// checked by the host pass, where they are not valid.
+__device__ __forceinline__ void tile_load_lds(const uint16_t* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const SPECV_TILE_GLOBAL void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+template <class T>
+__device__ __forceinline__ void tile_store(void* y, size_t i, T v) {
+  ((SPECV_TILE_GLOBAL T*)y)[i] = v;
+}
+
+template <int N>
+__device__ __forceinline__ void tile_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WM, int S, bool OUT_BF16>
+__global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y, int M,
+    int N, int K, int n_tiles, int per_xcd) {
+  using C = TileCfg<BM, BN, WM, S>;
+  extern __shared__ u32x4 lds[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // XCD-grouped tile order: workgroup bid runs on XCD bid % 8
+  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (t >= n_tiles) return;
+  const int MT = (M + BM - 1) / BM;
+  const int tm = t % MT, tn = t / MT;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int n_k = K / kTileBK;
+
+  // This lane's source row and unit for each of its L load instructions: the
+  // instruction covers LDS rows 8g .. 8g+7 (g = wave + 8q); lane l writes
+  // LDS row 8g + l/8, stored unit l%8, which holds the row's global unit
+  // (l%8) ^ (row % 8).
+  const uint16_t* src[C::L];
+#pragma unroll
+  for (int q = 0; q < C::L; ++q) {
+    const int r = 8 * (wave + 8 * q) + (lane >> 3);
+    const int u = (lane & 7) ^ (r & 7);
+    const uint16_t* p;
+    if (r < BM)
+      p = X + (size_t)min(m0 + r, M - 1) * K + u * 8;
+    else
+      p = W + (size_t)min(n0 + (r - BM), N - 1) * K + u * 8;
+    src[q] = p;
+  }
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    // stages past the end reload the last one into a slot nobody reads
+    const int kc = min(kt, n_k - 1);
+    const int slot = kt % S;
+#pragma unroll
+    for (int q = 0; q < C::L; ++q) {
+      tile_load_lds(src[q] + (size_t)kc * kTileBK,
+                    reinterpret_cast<char*>(lds) + slot * C::STAGE_BYTES + 8 * (wave + 8 * q) * 128);
+    }
+  };
+
+  f32x4 acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s);
+
+  for (int kt = 0; kt < n_k; ++kt) {
+    tile_wait_vmcnt<(S - 2) * C::L>();  // this wave's loads of stage kt have landed
+    tile_barrier();                     // everyone's; and stage kt-1's slot is free
+    issue(kt + S - 1);
+    const char* base = reinterpret_cast<const char*>(lds) + (kt % S) * C::STAGE_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int unit = kk * 4 + (lane >> 4);
+      bf16x8 a[C::TM], b[C::TN];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        const int r = wm * (BM / WM) + i * 16 + (lane & 15);
+        a[i] = *reinterpret_cast<const bf16x8*>(base + r * 128 + ((unit ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int r = BM + wn * (BN / C::WN) + j * 16 + (lane & 15);
+        b[j] = *reinterpret_cast<const bf16x8*>(base + r * 128 + ((unit ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  tile_wait_vmcnt<0>();  // the reloads past the end land before the workgroup leaves
+
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int col = n0 + wn * (BN / C::WN) + j * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + r;
+        if (row < M && col < N) {
+          const float v = acc[i][j][r];
+          if (OUT_BF16)
+            tile_store<uint16_t>(Y, (size_t)row * N + col, f32_to_bf16_bits(v));
+          else
+            tile_store<float>(Y, (size_t)row * N + col, v);
+        }
+      }
+    }
+}
+
+template <int BM, int BN, int WM, int S>
+static hipError_t launch_tile_t(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16,
+                                int M, int K, int N, hipStream_t s) {
+  using C = TileCfg<BM, BN, WM, S>;
+  const int n_tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int per_xcd = (n_tiles + 7) / 8;
+  const dim3 grid(8 * per_xcd);
+  static const hipError_t a1 = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, true>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  static const hipError_t a2 = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, false>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  if (a1 != hipSuccess) return a1;
+  if (a2 != hipSuccess) return a2;
+  if (out_bf16)
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, true>), grid, dim3(kTileThreads),
+                       C::LDS_BYTES, s, x, w, y, M, N, K, n_tiles, per_xcd);
+  else
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, false>), grid, dim3(kTileThreads),
+                       C::LDS_BYTES, s, x, w, y, M, N, K, n_tiles, per_xcd);
+  return hipGetLastError();
+}
+
+// Tile shapes (BM, BN, waves along M, stages), indexed as in the launch
+// switch of launch_gemm_mfma.
+static const int kTileShapes[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128},
+                                     {128, 64},  {64, 128},  {64, 64}};
+
+// Time model of one launch, per reduction element: a tile costs
+// a * (BM + BN) (operand lines into LDS and out to the matrix cores) plus
+// b * BM * BN (the products), and the tiles run in ceil(tiles / CUs) rounds.
+// a and b were fitted to measured Llama-shaped linears at M = 320 and 1280
+// on MI355X; the model only ranks shapes.
+static int pick_tile(int M, int N, int cus) {
+  const double a = 3.6e-5, b = 8.1e-8;
+  const int n = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
+  int best = n - 1;
+  double best_t = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const int bm = kTileShapes[i][0], bn = kTileShapes[i][1];
+    const long tiles = (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    const long rounds = (tiles + cus - 1) / cus;
+    const double t = rounds * (a * (bm + bn) + b * (double)bm * bn);
+    if (i == 0 || t < best_t) {
+      best_t = t;
+      best = i;
+    }
+  }
+  return best;
+}
+
 template <int BM, int BN, int WM>
 static hipError_t launch_mfma_t(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
                                 int K, int N, hipStream_t s) {
@@ -143,6 +351,21 @@ static hipError_t launch_mfma_t(const uint16_t* x, const uint16_t* w, void* y, b
 
 hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
                             int K, int N, hipStream_t s) {
+  if (K % kTileBK == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    switch (pick_tile(M, N, cus)) {
+      case 0: return launch_tile_t<256, 256, 4, 2>(x, w, y, out_bf16, M, K, N, s);
+      case 1: return launch_tile_t<256, 128, 4, 3>(x, w, y, out_bf16, M, K, N, s);
+      case 2: return launch_tile_t<128, 256, 2, 3>(x, w, y, out_bf16, M, K, N, s);
+      case 3: return launch_tile_t<128, 128, 2, 4>(x, w, y, out_bf16, M, K, N, s);
+      case 4: return launch_tile_t<128, 64, 4, 4>(x, w, y, out_bf16, M, K, N, s);
+      case 5: return launch_tile_t<64, 128, 2, 4>(x, w, y, out_bf16, M, K, N, s);
+      default: return launch_tile_t<64, 64, 2, 4>(x, w, y, out_bf16, M, K, N, s);
+    }
+  }
   if (M <= 32) return launch_mfma_t<32, 64, 1>(x, w, y, out_bf16, M, K, N, s);
   if (M <= 128) return launch_mfma_t<64, 64, 2>(x, w, y, out_bf16, M, K, N, s);
   return launch_mfma_t<128, 128, 2>(x, w, y, out_bf16, M, K, N, s);

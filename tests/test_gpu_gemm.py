@@ -96,6 +96,20 @@ def test_mfma_kernel(sv, dev, M):
         check(y, oracle.linear(x, w), od, f"mfma M={M} {od}")
 
 
+@pytest.mark.parametrize("M,d_in,d_out", [(129, 64, 777), (200, 1024, 777), (256, 512, 4112),
+                                           (320, 1024, 300), (513, 128, 1000),
+                                           (1280, 1024, 777)])
+def test_tile_kernel(sv, dev, M, d_in, d_out):
+    """The pipelined tile kernel (d_in a multiple of 64): ragged M and N
+    tails, one or many stages, each tile shape the dispatcher picks."""
+    import torch
+    x, w = synth.linear_inputs(300 + M, f"tile{d_in}.{d_out}", M, d_in, d_out)
+    ref = oracle.linear(x, w)
+    for od in (torch.float32, torch.bfloat16):
+        y = run_host(sv, dev, x, w, od)
+        check(y, ref, od, f"tile M={M} {d_in}->{d_out} {od}")
+
+
 def test_edge_shapes(sv, dev):
     import torch
     for M, d_in, d_out in [(1, 8, 1), (5, 8, 3), (16, 16, 1), (17, 8, 1), (2, 2048 + 8, 65)]:
@@ -156,7 +170,7 @@ def test_batch_sweep_lm_head_m1280(sv, dev):
     check(y, ref, torch.float32, "sweep M=1280 lm-head")
 
 
-@pytest.mark.parametrize("M", [5, 80])
+@pytest.mark.parametrize("M", [5, 80, 320])
 def test_deterministic(sv, dev, M):
     import torch
     from synth import device as sd
