@@ -149,20 +149,37 @@ __global__ __launch_bounds__(kMfmaThreads) void gemm_mfma_kernel(
 // L2.
 
 constexpr int kTileThreads = 512;
-constexpr int kTileBK = 64;  // reduction elements per stage (one 128-byte line per row)
+constexpr int kTileKAlign = 64;  // the kernel needs K to be a multiple of this
 
-template <int BM, int BN, int WM, int S>
+// BK reduction elements per stage: 64 (a whole 128-byte line of each row) or
+// 32 (half a line; the other half follows in the next stage, from L2), which
+// halves a stage so that more of them fit in LDS.
+template <int BM, int BN, int WM, int S, int BK>
 struct TileCfg {
   static constexpr int WN = 8 / WM;
   static constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
-  static constexpr int ROWS = BM + BN;         // LDS rows per stage (x rows, then w rows)
-  static constexpr int L = ROWS / 64;          // load instructions per wave per stage
-  static constexpr int STAGE_BYTES = ROWS * 128;
+  static constexpr int ROWS = BM + BN;           // LDS rows per stage (x rows, then w rows)
+  static constexpr int UPR = BK / 8;             // 16-byte units per row
+  static constexpr int RPI = 64 / UPR;           // rows per load instruction
+  static constexpr int RPL = 128 / (2 * BK);     // rows per 128-byte bank line
+  static constexpr int ROW_BYTES = 2 * BK;
+  static constexpr int L = ROWS / (8 * RPI);     // load instructions per wave per stage
+  static constexpr int STAGE_BYTES = ROWS * ROW_BYTES;
   static constexpr int LDS_BYTES = S * STAGE_BYTES;
+  static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(TM >= 1 && TN >= 1 && BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
-  static_assert(ROWS % 64 == 0, "whole load instructions per wave");
+  static_assert(ROWS % (8 * RPI) == 0, "whole load instructions per wave");
   static_assert(S >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring");
 };
+// Stored position of unit u of LDS row r, XOR-swizzled so that a fragment
+// read (16 consecutive rows at one unit) is free of bank conflicts whether
+// the banks serve 128 bytes (eight lanes) or 256 bytes (sixteen lanes) at a
+// time: eight consecutive rows map to distinct 16-byte slots of a 128-byte
+// bank line, and the second eight rows of the 16 to the opposite slots.
+template <class C>
+__device__ __forceinline__ int tile_unit_pos(int r, int u) {
+  return u ^ ((r / C::RPL) % C::UPR) ^ ((r / (C::RPL * C::UPR)) & 1);
+}
 
 __device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -185,11 +202,11 @@ __device__ __forceinline__ void tile_wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int S, bool OUT_BF16>
+template <int BM, int BN, int WM, int S, int BK, bool OUT_BF16>
 __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y, int M,
     int N, int K, int n_tiles, int per_xcd) {
-  using C = TileCfg<BM, BN, WM, S>;
+  using C = TileCfg<BM, BN, WM, S, BK>;
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // XCD-grouped tile order: workgroup bid runs on XCD bid % 8
@@ -199,17 +216,18 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(
   const int tm = t % MT, tn = t / MT;
   const int m0 = tm * BM, n0 = tn * BN;
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int n_k = K / kTileBK;
+  const int n_k = K / BK;
 
   // This lane's source row and unit for each of its L load instructions: the
-  // instruction covers LDS rows 8g .. 8g+7 (g = wave + 8q); lane l writes
-  // LDS row 8g + l/8, stored unit l%8, which holds the row's global unit
-  // (l%8) ^ (row % 8).
+  // instruction covers LDS rows RPI*g .. RPI*g + RPI-1 (g = wave + 8q); lane
+  // l writes LDS row RPI*g + l/UPR at stored unit l%UPR, which holds the
+  // row's global unit tile_unit_pos(row, l%UPR) (the swizzle is its own
+  // inverse).
   const uint16_t* src[C::L];
 #pragma unroll
   for (int q = 0; q < C::L; ++q) {
-    const int r = 8 * (wave + 8 * q) + (lane >> 3);
-    const int u = (lane & 7) ^ (r & 7);
+    const int r = C::RPI * (wave + 8 * q) + lane / C::UPR;
+    const int u = tile_unit_pos<C>(r, lane % C::UPR);
     const uint16_t* p;
     if (r < BM)
       p = X + (size_t)min(m0 + r, M - 1) * K + u * 8;
@@ -223,8 +241,8 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(
     const int slot = kt % S;
 #pragma unroll
     for (int q = 0; q < C::L; ++q) {
-      tile_load_lds(src[q] + (size_t)kc * kTileBK,
-                    reinterpret_cast<char*>(lds) + slot * C::STAGE_BYTES + 8 * (wave + 8 * q) * 128);
+      tile_load_lds(src[q] + (size_t)kc * BK, reinterpret_cast<char*>(lds) + slot * C::STAGE_BYTES +
+                                                  C::RPI * (wave + 8 * q) * C::ROW_BYTES);
     }
   };
 
@@ -243,18 +261,20 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(
     issue(kt + S - 1);
     const char* base = reinterpret_cast<const char*>(lds) + (kt % S) * C::STAGE_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < BK / 32; ++kk) {
       const int unit = kk * 4 + (lane >> 4);
       bf16x8 a[C::TM], b[C::TN];
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
         const int r = wm * (BM / WM) + i * 16 + (lane & 15);
-        a[i] = *reinterpret_cast<const bf16x8*>(base + r * 128 + ((unit ^ (r & 7)) << 4));
+        a[i] = *reinterpret_cast<const bf16x8*>(base + r * C::ROW_BYTES +
+                                                 (tile_unit_pos<C>(r, unit) << 4));
       }
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         const int r = BM + wn * (BN / C::WN) + j * 16 + (lane & 15);
-        b[j] = *reinterpret_cast<const bf16x8*>(base + r * 128 + ((unit ^ (r & 7)) << 4));
+        b[j] = *reinterpret_cast<const bf16x8*>(base + r * C::ROW_BYTES +
+                                                 (tile_unit_pos<C>(r, unit) << 4));
       }
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
@@ -284,26 +304,26 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(
     }
 }
 
-template <int BM, int BN, int WM, int S>
+template <int BM, int BN, int WM, int S, int BK>
 static hipError_t launch_tile_t(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16,
                                 int M, int K, int N, hipStream_t s) {
-  using C = TileCfg<BM, BN, WM, S>;
+  using C = TileCfg<BM, BN, WM, S, BK>;
   const int n_tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int per_xcd = (n_tiles + 7) / 8;
   const dim3 grid(8 * per_xcd);
   static const hipError_t a1 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, true>),
+      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, true>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   static const hipError_t a2 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, false>),
+      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, false>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
   if (out_bf16)
-    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, true>), grid, dim3(kTileThreads),
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, true>), grid, dim3(kTileThreads),
                        C::LDS_BYTES, s, x, w, y, M, N, K, n_tiles, per_xcd);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, false>), grid, dim3(kTileThreads),
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, false>), grid, dim3(kTileThreads),
                        C::LDS_BYTES, s, x, w, y, M, N, K, n_tiles, per_xcd);
   return hipGetLastError();
 }
@@ -351,19 +371,19 @@ static hipError_t launch_mfma_t(const uint16_t* x, const uint16_t* w, void* y, b
 
 hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
                             int K, int N, hipStream_t s) {
-  if (K % kTileBK == 0) {
+  if (K % kTileKAlign == 0) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
     switch (pick_tile(M, N, cus)) {
-      case 0: return launch_tile_t<256, 256, 4, 2>(x, w, y, out_bf16, M, K, N, s);
-      case 1: return launch_tile_t<256, 128, 4, 3>(x, w, y, out_bf16, M, K, N, s);
-      case 2: return launch_tile_t<128, 256, 2, 3>(x, w, y, out_bf16, M, K, N, s);
-      case 3: return launch_tile_t<128, 128, 2, 4>(x, w, y, out_bf16, M, K, N, s);
-      case 4: return launch_tile_t<128, 64, 4, 4>(x, w, y, out_bf16, M, K, N, s);
-      case 5: return launch_tile_t<64, 128, 2, 4>(x, w, y, out_bf16, M, K, N, s);
-      default: return launch_tile_t<64, 64, 2, 4>(x, w, y, out_bf16, M, K, N, s);
+      case 0: return launch_tile_t<256, 256, 4, 2, 64>(x, w, y, out_bf16, M, K, N, s);
+      case 1: return launch_tile_t<256, 128, 4, 3, 64>(x, w, y, out_bf16, M, K, N, s);
+      case 2: return launch_tile_t<128, 256, 2, 3, 64>(x, w, y, out_bf16, M, K, N, s);
+      case 3: return launch_tile_t<128, 128, 2, 4, 64>(x, w, y, out_bf16, M, K, N, s);
+      case 4: return launch_tile_t<128, 64, 4, 4, 64>(x, w, y, out_bf16, M, K, N, s);
+      case 5: return launch_tile_t<64, 128, 2, 4, 64>(x, w, y, out_bf16, M, K, N, s);
+      default: return launch_tile_t<64, 64, 2, 4, 64>(x, w, y, out_bf16, M, K, N, s);
     }
   }
   if (M <= 32) return launch_mfma_t<32, 64, 1>(x, w, y, out_bf16, M, K, N, s);
