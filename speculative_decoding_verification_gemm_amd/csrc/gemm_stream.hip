@@ -259,21 +259,34 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
   // compiler wait for every load in flight wherever it needs a vmcnt wait.
   SPECV_GLOBAL unsigned long long* trace =
       is_chain ? gptr_mut<unsigned long long>(sync->trace) : nullptr;
-  // Release flags: the last workgroup to arrive at linear l publishes the
-  // count to kReleaseLanes flags on separate 64-byte lines, and waiters poll
-  // the flag of their lane, so polls do not queue on the line the arrivals
-  // update.
+  // Arrivals are counted in two levels: each workgroup bumps the counter of
+  // its group (bid mod kArriveGroups, one 64-byte line each), and the last of
+  // a group bumps the linear's counter. When every workgroup finishes a
+  // linear at nearly the same moment, no counter serializes more than a
+  // group's worth of atomics. The last group to arrive publishes the target
+  // to kReleaseLanes flags on separate lines, and waiters poll the flag of
+  // their lane, so polls do not queue on the lines the arrivals update.
   unsigned* release = is_chain ? counts + chain_release_offset(n_lin) : nullptr;
-  auto flag = [&](int l, int lane_id) __attribute__((always_inline)) { return release + ((size_t)l * kReleaseLanes + lane_id) * 16; };
+  auto flag = [&](int l, int lane_id) __attribute__((always_inline)) {
+    return release + ((size_t)l * kBarrierLines + lane_id) * 16;
+  };
+  const int n_groups = G < kArriveGroups ? G : kArriveGroups;
   auto arrive = [&](int l) __attribute__((always_inline)) {
     __syncthreads();
     if (tid == 0) {
       if (trace) trace[((size_t)l * G + bid) * 4] = wall_clock64();
-      const unsigned prev =
-          __hip_atomic_fetch_add(&counts[l], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev + 1u == target) {
-        for (int x = 0; x < kReleaseLanes; ++x)
-          __hip_atomic_store(flag(l, x), target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int g = bid % kArriveGroups;
+      const unsigned gen1 = target / (unsigned)G;  // launches including this one
+      const unsigned gsize = (unsigned)((G - g + kArriveGroups - 1) / kArriveGroups);
+      unsigned* gc = release + ((size_t)l * kBarrierLines + kReleaseLanes + g) * 16;
+      const unsigned gp = __hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (gp + 1u == gen1 * gsize) {
+        const unsigned prev =
+            __hip_atomic_fetch_add(&counts[l], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev + 1u == gen1 * (unsigned)n_groups) {
+          for (int x = 0; x < kReleaseLanes; ++x)
+            __hip_atomic_store(flag(l, x), target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
   };

@@ -47,14 +47,16 @@ static_assert(sizeof(ChainSync) == 64, "chain header is one cache line");
 constexpr unsigned kChainMagic = 0x53504348u;    // "SPCH": bf16 weights
 constexpr unsigned kChainMagicW8 = 0x53503848u;  // "SP8H": FP8 E4M3 weights
 // Chain workspace after the header: n arrival counters, then (64-byte
-// aligned) n x kReleaseLanes release flags, one 64-byte line each, then the
-// descriptors.
+// aligned) per linear kReleaseLanes release flags and kArriveGroups group
+// arrival counters, one 64-byte line each, then the descriptors.
 constexpr int kReleaseLanes = 8;
+constexpr int kArriveGroups = 8;
+constexpr int kBarrierLines = kReleaseLanes + kArriveGroups;  // per linear
 __host__ __device__ inline size_t chain_release_offset(int n) {  // in unsigned words from counts
   return (((size_t)n * 4 + 63) & ~(size_t)63) / 4;
 }
 __host__ __device__ inline size_t chain_counts_bytes(int n) {
-  return chain_release_offset(n) * 4 + (size_t)n * kReleaseLanes * 64;
+  return chain_release_offset(n) * 4 + (size_t)n * kBarrierLines * 64;
 }
 
 // Softmax statistics of a logits linear, fused into the streaming kernel's
