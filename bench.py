@@ -67,6 +67,12 @@ def parse():
                          "spec_verify reads its logits; fused: the chain holds the stack only "
                          "and spec_verify runs the lm-head with the target rows' softmax "
                          "statistics fused into its epilogue (bf16 weights, M <= 16)")
+    ap.add_argument("--stress", action="store_true",
+                    help="sampling-stress workload: B=64, K=8, V=128256, target logits "
+                         "N(0, 3^2), draft rows calibrated to alpha in {0.6, 0.81, 0.9}; "
+                         "--rounds verification rounds per alpha")
+    ap.add_argument("--rounds", type=int, default=100000,
+                    help="rounds per alpha for --stress")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (the known-size "
                          "reference that scales FETCH_SIZE / WRITE_SIZE counters)")
@@ -341,6 +347,102 @@ def attention_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def stress_bench(args):
+    """The sampling-stress workload: fixed target logits N(0, 3^2) for B = 64
+    sequences of K = 8 drafts over V = 128256; each draft row's noise scale
+    is bisected so that its acceptance rate sum_x min(p, q) equals alpha.
+    Every round draws fresh drafts x_j ~ q_j and fresh uniforms, then runs
+    spec_verify. Reports tokens per round against 1 + sum_i prod_{j<=i}
+    alpha_j (which equals (1 - alpha^(K+1)) / (1 - alpha) here) and the
+    verify call's time against the bytes it must read."""
+    import math
+    import torch
+    import synth
+    import speculative_decoding_verification_gemm_amd as sv
+
+    dev = torch.device("cuda:0")
+    B, K, V, seed = 64, 8, 128256, 2027
+    tl = torch.from_numpy(synth.normals(seed, "stress.target", (B, K + 1, V), 3.0)).to(dev)
+    z = torch.from_numpy(synth.normals(seed, "stress.noise", (B, K, V))).to(dev)
+    p = torch.softmax(tl[:, :K].double(), dim=-1)
+    ws = sv.new_workspace(B, K, V, dev)
+    out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    # bytes one call must move: every target and draft logit once for the
+    # statistics, plus the one target and draft row of each sequence that the
+    # residual or bonus draw re-reads
+    call_bytes = 4 * V * B * (2 * K + 1) + 2 * 4 * V * B
+    results, ms_total, rounds_total = [], 0.0, 0
+    for alpha in (0.6, 0.81, 0.9):
+        lo = torch.zeros((B, K), dtype=torch.float64, device=dev)
+        hi = torch.full((B, K), 8.0, dtype=torch.float64, device=dev)
+        for _ in range(44):
+            mid = 0.5 * (lo + hi)
+            a = torch.minimum(p, torch.softmax((tl[:, :K] + mid.float()[..., None] * z).double(),
+                                               dim=-1)).sum(-1)
+            lo, hi = torch.where(a > alpha, mid, lo), torch.where(a > alpha, hi, mid)
+        sigma = (0.5 * (lo + hi)).float()
+        dl = (tl[:, :K] + sigma[..., None] * z).contiguous()
+        q = torch.softmax(dl.double(), dim=-1)
+        a = torch.minimum(p, q).sum(-1)
+        expect = float((1.0 + torch.cumprod(a, dim=1).sum(1)).mean())
+        cq = torch.cumsum(q, dim=-1).reshape(B * K, V)
+        del q
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed + int(alpha * 100))
+        tot = torch.zeros((), dtype=torch.float64, device=dev)
+        tot2 = torch.zeros((), dtype=torch.float64, device=dev)
+        ev = []
+        for r in range(args.rounds):
+            u_draft = torch.rand((B * K, 1), generator=gen, device=dev)
+            tok = torch.searchsorted(cq, u_draft.double() * cq[:, -1:], right=True)
+            tok = tok.clamp_(max=V - 1).reshape(B, K).int()
+            u_acc = torch.rand((B, K), generator=gen, device=dev)
+            u_smp = torch.rand((B, K + 1), generator=gen, device=dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            sv.verify(tl, dl, tok, u_acc, u_smp, workspace=ws, out_tokens=out, n_emitted=n)
+            e1.record()
+            ev.append((e0, e1))
+            nd = n.double()
+            tot += nd.sum()
+            tot2 += (nd * nd).sum()
+            if len(ev) >= 2000:
+                torch.cuda.synchronize()
+                ms_total += sum(x.elapsed_time(y) for x, y in ev)
+                rounds_total += len(ev)
+                ev = []
+            if r % 20000 == 0:
+                print(f"alpha={alpha}: round {r}", file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        ms_total += sum(x.elapsed_time(y) for x, y in ev)
+        rounds_total += len(ev)
+        cnt = args.rounds * B
+        mean = float(tot) / cnt
+        se = math.sqrt(max(float(tot2) / cnt - mean * mean, 0.0) / cnt)
+        results.append({"alpha": alpha, "rounds": args.rounds, "sequence_rounds": cnt,
+                        "tokens_per_round": mean, "expected": expect,
+                        "closed_form": (1 - alpha ** (K + 1)) / (1 - alpha), "se": se,
+                        "z": (mean - expect) / se if se > 0 else 0.0,
+                        "max_row_alpha_error": float((a - alpha).abs().max())})
+        del dl, cq
+    ms = ms_total / rounds_total
+    gbs = call_bytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "sampling-stress verification rounds/s (B=64, K=8, V=128256)",
+        "value": 1e3 / ms, "unit": "rounds/s", "n_gpus": 1, "steps": rounds_total, "warmup": 0,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 logits, f64 decisions", "data": "synthetic (seeded N(0,3^2) logits, "
+        "per-row calibrated draft noise)",
+        "config": {"workload": "sampling stress: spec_verify on fixed logits, fresh drafts "
+                               "and uniforms every round", "global_batch": B, "draft_tokens_K": K,
+                   "vocab": V},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_call": call_bytes},
+        "alphas": results}), flush=True)
+
+
 def copy_calibration(reps=5):
     """Copy 1 GiB device to device `reps` times: each copy reads and writes
     exactly 2^30 bytes, so the counters of one copy dispatch give the ratio
@@ -373,6 +475,9 @@ def main():
         return
     if args.attention:
         attention_bench(args)
+        return
+    if args.stress:
+        stress_bench(args)
         return
     import torch
     import synth

@@ -460,15 +460,32 @@ __device__ __forceinline__ const float* verify_row(const float* tl, const float*
   return row < n_target ? tl + (size_t)row * V : dl + (size_t)(row - n_target) * V;
 }
 
+// e^d for the bulk sums of the statistics and residual passes: the
+// exponent is split in fp64 as d * log2(e) = n + f with n an integer and
+// |f| <= 1/2, 2^f comes from the fp32 exp2 (a few ulp) and 2^n is exact, so
+// the relative error stays near 1e-7 -- two orders under the 1e-5 band in
+// which decisions count as ties -- at a small fraction of an fp64 exp's
+// cost. The probabilities a decision reads (p(x), q(x), the draw's weights)
+// are still evaluated with the fp64 exp.
+__device__ __forceinline__ double exp_sum_term(double d) {
+  const double y = fmax(d * 1.4426950408889634, -2000.0);  // log2(e); below -1075 the term is 0
+  const double n = rint(y);
+  return ldexp((double)exp2f((float)(y - n)), (int)n);
+}
+
 // row0: first row scanned (B(K+1) when the target rows' statistics come from
-// the lm-head launch, so only draft rows are scanned).
+// the lm-head launch, so only draft rows are scanned). One pass over the
+// chunk from memory: thread t reads entries t, t + 256, ... into registers
+// (every load instruction of a wave reads 256 contiguous bytes); the chunk
+// maximum is reduced first, then the fp64 sums of exp((l - max) * inv) in a
+// fixed order (shuffle tree, then waves in order): deterministic.
 __global__ __launch_bounds__(kScanThreads) void stats_partial_kernel(const float* __restrict__ tl,
                                                                      const float* __restrict__ dl,
                                                                      int B, int K, int V,
                                                                      VerifyWs ws, Warp wp,
                                                                      int row0) {
-  __shared__ double red_d[kScanThreads / kWave];
-  __shared__ float red_f[kScanThreads / kWave];
+  __shared__ float red_m[kScanThreads / kWave];
+  __shared__ double red_s[kScanThreads / kWave];
   __shared__ int red_i[kScanThreads / kWave];
   const int C = (V + kChunk - 1) / kChunk;
   const int row = row0 + (int)blockIdx.x / C, c = blockIdx.x - (row - row0) * C;
@@ -476,36 +493,57 @@ __global__ __launch_bounds__(kScanThreads) void stats_partial_kernel(const float
   const bool greedy = target ? wp.gt : wp.gd;
   const double inv = target ? wp.it : wp.id;
   const float* l = verify_row(tl, dl, row, B, K, V);
-  const int v0 = c * kChunk + threadIdx.x * kPerThread;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int v0 = c * kChunk + tid;
   float x[kPerThread];
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    x[i] = (v0 + i < V) ? l[v0 + i] : -INFINITY;
+    const int v = v0 + i * kScanThreads;
+    x[i] = v < V ? l[v] : -INFINITY;
     m = fmaxf(m, x[i]);
   }
-  const float cm = block_max_f32<kScanThreads>(m, red_f);
   if (greedy) {  // first index of the chunk maximum
     int first = INT_MAX;
 #pragma unroll
     for (int i = kPerThread - 1; i >= 0; --i)
-      if (v0 + i < V && x[i] == cm) first = v0 + i;
-    const int cf = block_min_i32<kScanThreads>(first, red_i);
-    if (threadIdx.x == 0) {
+      if (x[i] == m && x[i] != -INFINITY) first = v0 + i * kScanThreads;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float m2 = __shfl_xor(m, o, kWave);
+      const int f2 = __shfl_xor(first, o, kWave);
+      if (m2 > m || (m2 == m && f2 < first)) first = f2;
+      m = fmaxf(m, m2);
+    }
+    if (lane == 0) {
+      red_m[wave] = m;
+      red_i[wave] = first;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float cm = red_m[0];
+      int cf = red_i[0];
+      for (int w = 1; w < kScanThreads / kWave; ++w)
+        if (red_m[w] > cm || (red_m[w] == cm && red_i[w] < cf)) {
+          cm = red_m[w];
+          cf = red_i[w];
+        }
       ws.pmax[(size_t)row * C + c] = cm;
       ws.psum[(size_t)row * C + c] = 1.0;
       ws.parg[(size_t)row * C + c] = cf;
     }
     return;
   }
-  double s = 0.0;
+  // the chunk maximum first (exact in fp32), then every sum relative to it
+  const float cm = block_max_f32<kScanThreads>(m, red_m);
+  double sum = 0.0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i)
-    if (v0 + i < V) s += exp(((double)x[i] - (double)cm) * inv);
-  const double cs = block_sum_f64<kScanThreads>(s, red_d);
-  if (threadIdx.x == 0) {
+    if (x[i] != -INFINITY) sum += exp_sum_term(((double)x[i] - (double)cm) * inv);
+  sum = block_sum_f64<kScanThreads>(sum, red_s);
+  if (tid == 0) {
     ws.pmax[(size_t)row * C + c] = cm;
-    ws.psum[(size_t)row * C + c] = cs;
+    ws.psum[(size_t)row * C + c] = sum;
   }
 }
 
@@ -542,17 +580,19 @@ __device__ __forceinline__ void merge_partials(const float* pm, const double* ps
 // tstats: the target rows' per-workgroup partials from the lm-head launch
 // (tparts of them per row, stride kMaxStatParts), or tparts = 0 to use the
 // chunk partials of stats_partial_kernel for every row.
-__global__ __launch_bounds__(kWave) void verify_accept_kernel(
+constexpr int kAcceptWaves = 4;
+
+__global__ __launch_bounds__(kAcceptWaves * kWave) void verify_accept_kernel(
     const float* __restrict__ tl, const float* __restrict__ dl, const int32_t* __restrict__ tokens,
     const float* __restrict__ u_accept, int B, int K, int V, VerifyWs ws, Warp wp, int tparts) {
   __shared__ float smax[2 * 64 + 1];
   __shared__ double ssum[2 * 64 + 1];
   __shared__ int sarg[2 * 64 + 1];
-  const int b = blockIdx.x, lane = threadIdx.x;
+  const int b = blockIdx.x, lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int C = (V + kChunk - 1) / kChunk;
-  // local index i: 0..K target rows, K+1..2K draft rows; the whole wave
-  // merges one row's partials at a time
-  for (int i = 0; i < 2 * K + 1; ++i) {
+  // local index i: 0..K target rows, K+1..2K draft rows; each wave merges
+  // whole rows' partials, rows dealt round-robin to the waves
+  for (int i = wave; i < 2 * K + 1; i += kAcceptWaves) {
     const int row = i <= K ? b * (K + 1) + i : B * (K + 1) + b * K + (i - K - 1);
     const bool greedy = i <= K ? wp.gt : wp.gd;
     const double inv = i <= K ? wp.it : wp.id;
@@ -576,6 +616,7 @@ __global__ __launch_bounds__(kWave) void verify_accept_kernel(
     }
   }
   __syncthreads();
+  if (wave != 0) return;
   bool acc = false;
   if (lane < K) {
     const int x = tokens[(size_t)b * K + lane];
@@ -629,17 +670,20 @@ __global__ __launch_bounds__(kScanThreads) void resid_partial_kernel(
   const int b = blockIdx.x / C, c = blockIdx.x - b * C;
   const int n = ws.nacc[b];
   const LogitWeights w = verify_weights(tl, dl, b, n, B, K, V, ws, true, wp);
-  const int v0 = c * kChunk + threadIdx.x * kPerThread;
+  const double isp = 1.0 / w.sp, isq = 1.0 / w.sq;
+  // entries t, t + 256, ...: every load instruction of a wave reads 256
+  // contiguous bytes
+  const int v0 = c * kChunk + threadIdx.x;
   double tr = 0.0, tp = 0.0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    const int v = v0 + i;
+    const int v = v0 + i * kScanThreads;
     if (v < V) {
-      const double pv = exp(((double)w.lp[v] - w.mp) * w.ip) / w.sp;
+      const double pv = exp_sum_term(((double)w.lp[v] - w.mp) * w.ip) * isp;
       tp += pv;
       if (w.lq) {
         const double qv = w.qarg >= 0 ? (v == w.qarg ? 1.0 : 0.0)
-                                      : exp(((double)w.lq[v] - w.mq) * w.iq) / w.sq;
+                                      : exp_sum_term(((double)w.lq[v] - w.mq) * w.iq) * isq;
         const double r = pv - qv;
         tr += r > 0.0 ? r : 0.0;
       }
@@ -672,30 +716,67 @@ __global__ __launch_bounds__(kScanThreads) void verify_draw_kernel(
       s_chunk = -2;
       s_use_p = 0;
     }
-  } else if (threadIdx.x == 0) {
+  } else if (threadIdx.x < kWave) {
+    // The chunk that holds T = u * Z, found by the first wave: lane l sums
+    // its own run of chunks, a shuffle scan gives each run's base, and the
+    // first run that passes T is walked chunk by chunk (as pick_chunk would
+    // walk all of them; only the rounding of the running sum differs).
+    const int lane = threadIdx.x;
     const double* rs = ws.rsum + (size_t)b * C;
     const double* ps = ws.qsum + (size_t)b * C;
-    double Z = 0.0;
-    for (int c = 0; c < C; ++c) Z += rs[c];
-    int use_p = 0;
-    if (!(Z > 0.0)) {  // empty residual: fall back to p of the same row
-      use_p = 1;
-      Z = 0.0;
-      for (int c = 0; c < C; ++c) Z += ps[c];
+    const int per = (C + kWave - 1) / kWave;
+    const int c0 = min(lane * per, C), c1 = min(c0 + per, C);
+    double lr = 0.0, lp = 0.0;
+    for (int c = c0; c < c1; ++c) {
+      lr += rs[c];
+      lp += ps[c];
     }
+    double Z = wave_sum_f64(lr);
+    const int use_p = !(Z > 0.0);  // empty residual: fall back to p of the same row
+    if (use_p) Z = wave_sum_f64(lp);
+    const double* sc = use_p ? ps : rs;
+    const double loc = use_p ? lp : lr;
     const double T = (double)u_sample[(size_t)b * (K + 1) + n] * Z;
-    double base = 0.0;
-    int chunk = -1;
-    if (Z > 0.0) {
-      if (use_p)
-        chunk = pick_chunk([&](int c) { return ps[c]; }, C, T, &base);
-      else
-        chunk = pick_chunk([&](int c) { return rs[c]; }, C, T, &base);
+    double inc = loc;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const double y = __shfl_up(inc, o, kWave);
+      if (lane >= o) inc += y;
     }
-    s_base = base;
-    s_T = T;
-    s_chunk = chunk;
-    s_use_p = use_p;
+    const double run0 = inc - loc;  // this lane's base
+    const unsigned long long hit = __ballot(loc > 0.0 && run0 + loc > T);
+    const unsigned long long pos = __ballot(loc > 0.0);
+    // the lane that walks its run: the first that passes T, else (rounding)
+    // the last with weight
+    const int owner = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : -1);
+    if (lane == 0) {
+      s_T = T;
+      s_use_p = use_p;
+      s_chunk = -1;
+      s_base = 0.0;
+    }
+    if (Z > 0.0 && lane == owner) {
+      double run = run0, last_base = 0.0;
+      int chunk = -1, last_pos = -1;
+      for (int c = c0; c < c1; ++c) {
+        const double w = sc[c];
+        if (w > 0.0) {
+          if (hit && run + w > T) {
+            chunk = c;
+            break;
+          }
+          last_pos = c;
+          last_base = run;
+        }
+        run += w;
+      }
+      if (chunk < 0) {
+        chunk = last_pos;
+        run = last_base;
+      }
+      s_chunk = chunk;
+      s_base = run;
+    }
   }
   __syncthreads();
   const int chunk = s_chunk;
@@ -735,8 +816,8 @@ hipError_t launch_verify_sampling(const float* tl, const float* dl, const int32_
   const int row0 = fused ? B * (K + 1) : 0;
   hipLaunchKernelGGL(stats_partial_kernel, dim3((R - row0) * C), dim3(kScanThreads), 0, s, tl, dl,
                      B, K, V, ws, wp, row0);
-  hipLaunchKernelGGL(verify_accept_kernel, dim3(B), dim3(kWave), 0, s, tl, dl, tokens, u_accept,
-                     B, K, V, ws, wp, fused ? parts : 0);
+  hipLaunchKernelGGL(verify_accept_kernel, dim3(B), dim3(kAcceptWaves * kWave), 0, s, tl, dl,
+                     tokens, u_accept, B, K, V, ws, wp, fused ? parts : 0);
   hipLaunchKernelGGL(resid_partial_kernel, dim3(B * C), dim3(kScanThreads), 0, s, tl, dl, B, K, V,
                      ws, wp);
   hipLaunchKernelGGL(verify_draw_kernel, dim3(B), dim3(kScanThreads), 0, s, tl, dl, tokens,
