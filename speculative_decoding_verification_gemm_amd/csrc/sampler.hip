@@ -171,9 +171,23 @@ struct ProbWeights {
   }
 };
 
+// e^d for the bulk sums of the statistics, residual and draw passes: the
+// exponent is split in fp64 as d * log2(e) = n + f with n an integer and
+// |f| <= 1/2, 2^f comes from the fp32 exp2 (a few ulp) and 2^n is exact, so
+// the relative error stays near 1e-7 -- two orders under the 1e-5 band in
+// which decisions count as ties -- at a small fraction of an fp64 exp's
+// cost. The accept test's p(x) and q(x) use the fp64 exp.
+__device__ __forceinline__ double exp_sum_term(double d) {
+  const double y = fmax(d * 1.4426950408889634, -2000.0);  // log2(e); below -1075 the term is 0
+  const double n = rint(y);
+  return ldexp((double)exp2f((float)(y - n)), (int)n);
+}
+
 // Weights of a draw from logits: p(v) = exp((l_p[v] - m_p) / T_p) / s_p,
 // minus q(v) for a residual. ip, iq are the inverse temperatures (1 at
-// T = 1); a greedy draft (T_q = 0) is one-hot at qarg.
+// T = 1); a greedy draft (T_q = 0) is one-hot at qarg. The residual pass and
+// the draw evaluate the same weights, so the chunk sums that pick a chunk
+// and the running sum inside it agree up to summation order.
 struct LogitWeights {
   const float* lp;
   const float* lq;  // null for a plain draw from p
@@ -181,9 +195,10 @@ struct LogitWeights {
   double ip = 1.0, iq = 1.0;
   int qarg = -1;    // >= 0: the draft is one-hot at this token
   __device__ __forceinline__ double operator()(int v) const {
-    const double pv = exp(((double)lp[v] - mp) * ip) / sp;
+    const double pv = exp_sum_term(((double)lp[v] - mp) * ip) * (1.0 / sp);
     if (!lq) return pv;
-    const double qv = qarg >= 0 ? (v == qarg ? 1.0 : 0.0) : exp(((double)lq[v] - mq) * iq) / sq;
+    const double qv =
+        qarg >= 0 ? (v == qarg ? 1.0 : 0.0) : exp_sum_term(((double)lq[v] - mq) * iq) * (1.0 / sq);
     const double r = pv - qv;
     return r > 0.0 ? r : 0.0;
   }
@@ -460,19 +475,6 @@ __device__ __forceinline__ const float* verify_row(const float* tl, const float*
   return row < n_target ? tl + (size_t)row * V : dl + (size_t)(row - n_target) * V;
 }
 
-// e^d for the bulk sums of the statistics and residual passes: the
-// exponent is split in fp64 as d * log2(e) = n + f with n an integer and
-// |f| <= 1/2, 2^f comes from the fp32 exp2 (a few ulp) and 2^n is exact, so
-// the relative error stays near 1e-7 -- two orders under the 1e-5 band in
-// which decisions count as ties -- at a small fraction of an fp64 exp's
-// cost. The probabilities a decision reads (p(x), q(x), the draw's weights)
-// are still evaluated with the fp64 exp.
-__device__ __forceinline__ double exp_sum_term(double d) {
-  const double y = fmax(d * 1.4426950408889634, -2000.0);  // log2(e); below -1075 the term is 0
-  const double n = rint(y);
-  return ldexp((double)exp2f((float)(y - n)), (int)n);
-}
-
 // row0: first row scanned (B(K+1) when the target rows' statistics come from
 // the lm-head launch, so only draft rows are scanned). One pass over the
 // chunk from memory: thread t reads entries t, t + 256, ... into registers
@@ -672,7 +674,7 @@ __global__ __launch_bounds__(kScanThreads) void resid_partial_kernel(
   const LogitWeights w = verify_weights(tl, dl, b, n, B, K, V, ws, true, wp);
   const double isp = 1.0 / w.sp, isq = 1.0 / w.sq;
   // entries t, t + 256, ...: every load instruction of a wave reads 256
-  // contiguous bytes
+  // contiguous bytes; each weight is computed as LogitWeights computes it
   const int v0 = c * kChunk + threadIdx.x;
   double tr = 0.0, tp = 0.0;
 #pragma unroll
