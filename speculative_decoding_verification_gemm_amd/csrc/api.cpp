@@ -139,9 +139,12 @@ int run_gemm(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M
   if (M <= specv::kMaxStreamM)
     e = specv::launch_gemm_stream(x, w, nullptr, y, out_bf16, false, M, d_in, d_out,
                                   cus * stream_wgs_per_cu(M), s);
+  else if (d_in % 64 == 0 || M > specv::kMaxSkinnyM)
+    // the pipelined tile kernel (d_in a multiple of 64; measured faster than
+    // the weight-streaming MFMA kernel at every M from 17 up)
+    e = specv::launch_gemm_mfma(x, w, y, out_bf16, M, d_in, d_out, s);
   else
-    e = M <= specv::kMaxSkinnyM ? specv::launch_gemm_skinny(x, w, y, out_bf16, M, d_in, d_out, s)
-                                : specv::launch_gemm_mfma(x, w, y, out_bf16, M, d_in, d_out, s);
+    e = specv::launch_gemm_skinny(x, w, y, out_bf16, M, d_in, d_out, s);
   return launched(e, "spec_verify_gemm");
 }
 

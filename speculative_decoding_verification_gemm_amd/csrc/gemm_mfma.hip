@@ -131,8 +131,8 @@ __global__ __launch_bounds__(kMfmaThreads) void gemm_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined tile kernel (K a multiple of 64): eight waves, LDS ring filled by
-// direct-to-LDS loads
+// Pipelined tile kernel (K a multiple of 64): NW waves (eight for the large
+// tiles), LDS ring filled by direct-to-LDS loads
 // ---------------------------------------------------------------------------
 //
 // Both operands reach LDS as whole 128-byte lines: one load instruction of a
@@ -148,27 +148,26 @@ __global__ __launch_bounds__(kMfmaThreads) void gemm_mfma_kernel(
 // (bid mod 8) take consecutive tiles, which share weight tiles in that XCD's
 // L2.
 
-constexpr int kTileThreads = 512;
 constexpr int kTileKAlign = 64;  // the kernel needs K to be a multiple of this
 
 // BK reduction elements per stage: 64 (a whole 128-byte line of each row) or
 // 32 (half a line; the other half follows in the next stage, from L2), which
 // halves a stage so that more of them fit in LDS.
-template <int BM, int BN, int WM, int S, int BK>
+template <int BM, int BN, int WM, int S, int BK, int NW>
 struct TileCfg {
-  static constexpr int WN = 8 / WM;
+  static constexpr int WN = NW / WM;             // NW waves: WM along M, WN along N
   static constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
   static constexpr int ROWS = BM + BN;           // LDS rows per stage (x rows, then w rows)
   static constexpr int UPR = BK / 8;             // 16-byte units per row
   static constexpr int RPI = 64 / UPR;           // rows per load instruction
   static constexpr int RPL = 128 / (2 * BK);     // rows per 128-byte bank line
   static constexpr int ROW_BYTES = 2 * BK;
-  static constexpr int L = ROWS / (8 * RPI);     // load instructions per wave per stage
+  static constexpr int L = ROWS / (NW * RPI);    // load instructions per wave per stage
   static constexpr int STAGE_BYTES = ROWS * ROW_BYTES;
   static constexpr int LDS_BYTES = S * STAGE_BYTES;
   static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(TM >= 1 && TN >= 1 && BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
-  static_assert(ROWS % (8 * RPI) == 0, "whole load instructions per wave");
+  static_assert(WM * WN == NW && ROWS % (NW * RPI) == 0, "whole load instructions per wave");
   static_assert(S >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring");
 };
 // Stored position of unit u of LDS row r, XOR-swizzled so that a fragment
@@ -202,11 +201,11 @@ __device__ __forceinline__ void tile_wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int S, int BK, bool OUT_BF16>
-__global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(
+template <int BM, int BN, int WM, int S, int BK, int NW, bool OUT_BF16>
+__global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y, int M,
     int N, int K, int n_tiles, int per_xcd) {
-  using C = TileCfg<BM, BN, WM, S, BK>;
+  using C = TileCfg<BM, BN, WM, S, BK, NW>;
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // XCD-grouped tile order: workgroup bid runs on XCD bid % 8
@@ -219,14 +218,14 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(
   const int n_k = K / BK;
 
   // This lane's source row and unit for each of its L load instructions: the
-  // instruction covers LDS rows RPI*g .. RPI*g + RPI-1 (g = wave + 8q); lane
+  // instruction covers LDS rows RPI*g .. RPI*g + RPI-1 (g = wave + NW*q); lane
   // l writes LDS row RPI*g + l/UPR at stored unit l%UPR, which holds the
   // row's global unit tile_unit_pos(row, l%UPR) (the swizzle is its own
   // inverse).
   const uint16_t* src[C::L];
 #pragma unroll
   for (int q = 0; q < C::L; ++q) {
-    const int r = C::RPI * (wave + 8 * q) + lane / C::UPR;
+    const int r = C::RPI * (wave + NW * q) + lane / C::UPR;
     const int u = tile_unit_pos<C>(r, lane % C::UPR);
     const uint16_t* p;
     if (r < BM)
@@ -242,7 +241,7 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(
 #pragma unroll
     for (int q = 0; q < C::L; ++q) {
       tile_load_lds(src[q] + (size_t)kc * BK, reinterpret_cast<char*>(lds) + slot * C::STAGE_BYTES +
-                                                  C::RPI * (wave + 8 * q) * C::ROW_BYTES);
+                                                  C::RPI * (wave + NW * q) * C::ROW_BYTES);
     }
   };
 
@@ -304,44 +303,47 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(
     }
 }
 
-template <int BM, int BN, int WM, int S, int BK>
+template <int BM, int BN, int WM, int S, int BK, int NW = 8>
 static hipError_t launch_tile_t(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16,
                                 int M, int K, int N, hipStream_t s) {
-  using C = TileCfg<BM, BN, WM, S, BK>;
+  using C = TileCfg<BM, BN, WM, S, BK, NW>;
   const int n_tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int per_xcd = (n_tiles + 7) / 8;
   const dim3 grid(8 * per_xcd);
   static const hipError_t a1 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, true>),
+      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, true>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   static const hipError_t a2 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, false>),
+      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, false>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
   if (out_bf16)
-    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, true>), grid, dim3(kTileThreads),
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, true>), grid, dim3(NW * 64),
                        C::LDS_BYTES, s, x, w, y, M, N, K, n_tiles, per_xcd);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, false>), grid, dim3(kTileThreads),
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, false>), grid, dim3(NW * 64),
                        C::LDS_BYTES, s, x, w, y, M, N, K, n_tiles, per_xcd);
   return hipGetLastError();
 }
 
-// Tile shapes (BM, BN, waves along M, stages), indexed as in the launch
-// switch of launch_gemm_mfma.
-static const int kTileShapes[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128},
-                                     {128, 64},  {64, 128},  {64, 64}};
+// Tile shapes (BM, BN), indexed as in the launch switch of
+// launch_gemm_mfma; the first seven use eight waves, the last three (for
+// linears with few positions and few output rows) two or four, so that
+// several of them share a CU.
+static const int kTileShapes[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128}, {128, 64},
+                                     {64, 128},  {64, 64},   {64, 32},   {32, 32},   {32, 16}};
 
 // Time model of one launch, per reduction element: a tile costs
 // a * (BM + BN) (operand lines into LDS and out to the matrix cores) plus
 // b * BM * BN (the products), and the tiles run in ceil(tiles / CUs) rounds.
 // a and b were fitted to measured Llama-shaped linears at M = 320 and 1280
-// on MI355X; the model only ranks shapes.
+// on MI355X; at M = 20 to 128 the shape the model picks was the fastest
+// measured, or within 5% of it, for every Llama-3.1-8B linear.
 static int pick_tile(int M, int N, int cus) {
   const double a = 3.6e-5, b = 8.1e-8;
   const int n = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
-  int best = n - 1;
+  int best = 0;
   double best_t = 0.0;
   for (int i = 0; i < n; ++i) {
     const int bm = kTileShapes[i][0], bn = kTileShapes[i][1];
@@ -383,7 +385,10 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
       case 3: return launch_tile_t<128, 128, 2, 4, 64>(x, w, y, out_bf16, M, K, N, s);
       case 4: return launch_tile_t<128, 64, 4, 4, 64>(x, w, y, out_bf16, M, K, N, s);
       case 5: return launch_tile_t<64, 128, 2, 4, 64>(x, w, y, out_bf16, M, K, N, s);
-      default: return launch_tile_t<64, 64, 2, 4, 64>(x, w, y, out_bf16, M, K, N, s);
+      case 6: return launch_tile_t<64, 64, 2, 4, 64>(x, w, y, out_bf16, M, K, N, s);
+      case 7: return launch_tile_t<64, 32, 2, 4, 64, 4>(x, w, y, out_bf16, M, K, N, s);
+      case 8: return launch_tile_t<32, 32, 2, 6, 64, 4>(x, w, y, out_bf16, M, K, N, s);
+      default: return launch_tile_t<32, 16, 2, 6, 64, 2>(x, w, y, out_bf16, M, K, N, s);
     }
   }
   if (M <= 32) return launch_mfma_t<32, 64, 1>(x, w, y, out_bf16, M, K, N, s);
