@@ -140,8 +140,9 @@ int run_gemm(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M
     e = specv::launch_gemm_stream(x, w, nullptr, y, out_bf16, false, M, d_in, d_out,
                                   cus * stream_wgs_per_cu(M), s);
   else if (d_in % 64 == 0 || M > specv::kMaxSkinnyM)
-    // the pipelined tile kernel (d_in a multiple of 64; measured faster than
-    // the weight-streaming MFMA kernel at every M from 17 up)
+    // the pipelined tile kernel when d_in is a multiple of 64 (measured
+    // faster than the weight-streaming MFMA kernel at every M from 17 up),
+    // else the register-staged tile kernel
     e = specv::launch_gemm_mfma(x, w, y, out_bf16, M, d_in, d_out, s);
   else
     e = specv::launch_gemm_skinny(x, w, y, out_bf16, M, d_in, d_out, s);

@@ -12,9 +12,8 @@ namespace specv {
 // Largest number of verify positions handled by the vector-ALU streaming
 // kernel; larger M uses the MFMA kernel.
 constexpr int kMaxStreamM = 16;
-// Largest M for the weight-streaming MFMA kernel (gemm_skinny.hip), which
-// serves d_in not a multiple of 64; the tiled MFMA kernel takes every other
-// M above kMaxStreamM.
+// Largest M for the weight-streaming MFMA kernel (gemm_skinny.hip); larger M
+// uses the tiled MFMA kernel.
 constexpr int kMaxSkinnyM = 128;
 
 // One linear of a streaming launch (single call, or one descriptor of a
