@@ -171,17 +171,18 @@ struct ProbWeights {
   }
 };
 
-// e^d for the bulk sums of the statistics, residual and draw passes: the
-// exponent is split in fp64 as d * log2(e) = n + f with n an integer and
-// |f| <= 1/2, 2^f comes from the fp32 exp2 (a few ulp) and 2^n is exact, so
-// the relative error stays near 1e-7 -- two orders under the 1e-5 band in
-// which decisions count as ties -- at a small fraction of an fp64 exp's
-// cost. The accept test's p(x) and q(x) use the fp64 exp.
-__device__ __forceinline__ double exp_sum_term(double d) {
-  const double y = fmax(d * 1.4426950408889634, -2000.0);  // log2(e); below -1075 the term is 0
-  const double n = rint(y);
-  return ldexp((double)exp2f((float)(y - n)), (int)n);
+// e^((l - m) * inv) for the bulk sums of the statistics, residual and draw
+// passes, as 2^y with y = (l - m) * sc, sc = inv * log2(e), in fp32 and
+// v_exp_f32. The error of y grows with |l - m|, but the terms that carry a
+// sum (l - m above about -10 at inv = 1) keep a relative error under about
+// 5e-7, more than an order under the 1e-5 band in which decisions count as
+// ties; terms under 2^-126 of the maximum's flush to zero, far below what
+// an fp64 sum of terms near 1 resolves. The sums themselves are fp64. The
+// accept test's p(x) and q(x) use the fp64 exp.
+__device__ __forceinline__ double exp_term(float l, float m, float sc) {
+  return (double)exp2f((l - m) * sc);
 }
+__host__ __device__ inline float exp_scale(double inv) { return (float)(inv * 1.4426950408889634); }
 
 // Weights of a draw from logits: p(v) = exp((l_p[v] - m_p) / T_p) / s_p,
 // minus q(v) for a residual. ip, iq are the inverse temperatures (1 at
@@ -191,14 +192,14 @@ __device__ __forceinline__ double exp_sum_term(double d) {
 struct LogitWeights {
   const float* lp;
   const float* lq;  // null for a plain draw from p
-  double mp, sp, mq, sq;
-  double ip = 1.0, iq = 1.0;
+  float mp, mq;     // row maxima
+  double sp, sq;    // row sums of exp((l - max) * inv)
+  float scp, scq;   // exp_scale of the inverse temperatures
   int qarg = -1;    // >= 0: the draft is one-hot at this token
   __device__ __forceinline__ double operator()(int v) const {
-    const double pv = exp_sum_term(((double)lp[v] - mp) * ip) * (1.0 / sp);
+    const double pv = exp_term(lp[v], mp, scp) * (1.0 / sp);
     if (!lq) return pv;
-    const double qv =
-        qarg >= 0 ? (v == qarg ? 1.0 : 0.0) : exp_sum_term(((double)lq[v] - mq) * iq) * (1.0 / sq);
+    const double qv = qarg >= 0 ? (v == qarg ? 1.0 : 0.0) : exp_term(lq[v], mq, scq) * (1.0 / sq);
     const double r = pv - qv;
     return r > 0.0 ? r : 0.0;
   }
@@ -475,12 +476,44 @@ __device__ __forceinline__ const float* verify_row(const float* tl, const float*
   return row < n_target ? tl + (size_t)row * V : dl + (size_t)(row - n_target) * V;
 }
 
+// Entry of the chunk held in slot i of thread t. VEC (V a multiple of 4,
+// 16-byte aligned rows): thread t holds entries 4 (t + 256 j) .. +3 for
+// j = 0..3, so every load instruction of a wave reads 1 KB contiguous;
+// otherwise entries t, t + 256, ... (256 contiguous bytes per instruction).
+template <bool VEC>
+__device__ __forceinline__ int chunk_entry(int c, int t, int i) {
+  return VEC ? c * kChunk + ((i / 4) * kScanThreads + t) * 4 + (i % 4)
+             : c * kChunk + t + i * kScanThreads;
+}
+template <bool VEC>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ l, int c, int t, int V,
+                                           float (&x)[kPerThread]) {
+  if constexpr (VEC) {
+#pragma unroll
+    for (int j = 0; j < kPerThread / 4; ++j) {
+      const int v = chunk_entry<true>(c, t, 4 * j);
+      const float4 q = v < V ? *reinterpret_cast<const float4*>(l + v)
+                             : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      x[4 * j] = q.x;
+      x[4 * j + 1] = q.y;
+      x[4 * j + 2] = q.z;
+      x[4 * j + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int v = chunk_entry<false>(c, t, i);
+      x[i] = v < V ? l[v] : -INFINITY;
+    }
+  }
+}
+
 // row0: first row scanned (B(K+1) when the target rows' statistics come from
 // the lm-head launch, so only draft rows are scanned). One pass over the
-// chunk from memory: thread t reads entries t, t + 256, ... into registers
-// (every load instruction of a wave reads 256 contiguous bytes); the chunk
-// maximum is reduced first, then the fp64 sums of exp((l - max) * inv) in a
-// fixed order (shuffle tree, then waves in order): deterministic.
+// chunk from memory into registers (load_chunk); the chunk maximum is
+// reduced first, then the fp64 sums of exp((l - max) * inv) in a fixed order
+// (per thread, a shuffle tree, then waves in order): deterministic.
+template <bool VEC>
 __global__ __launch_bounds__(kScanThreads) void stats_partial_kernel(const float* __restrict__ tl,
                                                                      const float* __restrict__ dl,
                                                                      int B, int K, int V,
@@ -496,20 +529,16 @@ __global__ __launch_bounds__(kScanThreads) void stats_partial_kernel(const float
   const double inv = target ? wp.it : wp.id;
   const float* l = verify_row(tl, dl, row, B, K, V);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int v0 = c * kChunk + tid;
   float x[kPerThread];
+  load_chunk<VEC>(l, c, tid, V, x);
   float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int v = v0 + i * kScanThreads;
-    x[i] = v < V ? l[v] : -INFINITY;
-    m = fmaxf(m, x[i]);
-  }
+  for (int i = 0; i < kPerThread; ++i) m = fmaxf(m, x[i]);
   if (greedy) {  // first index of the chunk maximum
     int first = INT_MAX;
 #pragma unroll
-    for (int i = kPerThread - 1; i >= 0; --i)
-      if (x[i] == m && x[i] != -INFINITY) first = v0 + i * kScanThreads;
+    for (int i = kPerThread - 1; i >= 0; --i)  // slots hold ascending entries
+      if (x[i] == m && x[i] != -INFINITY) first = chunk_entry<VEC>(c, tid, i);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float m2 = __shfl_xor(m, o, kWave);
@@ -538,10 +567,11 @@ __global__ __launch_bounds__(kScanThreads) void stats_partial_kernel(const float
   }
   // the chunk maximum first (exact in fp32), then every sum relative to it
   const float cm = block_max_f32<kScanThreads>(m, red_m);
+  const float sc = exp_scale(inv);
   double sum = 0.0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i)
-    if (x[i] != -INFINITY) sum += exp_sum_term(((double)x[i] - (double)cm) * inv);
+    if (x[i] != -INFINITY) sum += exp_term(x[i], cm, sc);
   sum = block_sum_f64<kScanThreads>(sum, red_s);
   if (tid == 0) {
     ws.pmax[(size_t)row * C + c] = cm;
@@ -647,8 +677,8 @@ __device__ __forceinline__ LogitWeights verify_weights(const float* tl, const fl
   w.lp = tl + (size_t)trow * V;
   w.mp = ws.fmax[trow];
   w.sp = ws.fsum[trow];
-  w.ip = wp.it;
-  w.iq = wp.id;
+  w.scp = exp_scale(wp.it);
+  w.scq = exp_scale(wp.id);
   if (with_q && n < K) {
     const int drow = B * (K + 1) + b * K + n;
     w.lq = dl + (size_t)(b * K + n) * V;
@@ -657,12 +687,13 @@ __device__ __forceinline__ LogitWeights verify_weights(const float* tl, const fl
     w.qarg = wp.gd ? ws.farg[drow] : -1;
   } else {
     w.lq = nullptr;
-    w.mq = 0.0;
+    w.mq = 0.0f;
     w.sq = 1.0;
   }
   return w;
 }
 
+template <bool VEC>
 __global__ __launch_bounds__(kScanThreads) void resid_partial_kernel(
     const float* __restrict__ tl, const float* __restrict__ dl, int B, int K, int V, VerifyWs ws,
     Warp wp) {
@@ -673,19 +704,21 @@ __global__ __launch_bounds__(kScanThreads) void resid_partial_kernel(
   const int n = ws.nacc[b];
   const LogitWeights w = verify_weights(tl, dl, b, n, B, K, V, ws, true, wp);
   const double isp = 1.0 / w.sp, isq = 1.0 / w.sq;
-  // entries t, t + 256, ...: every load instruction of a wave reads 256
-  // contiguous bytes; each weight is computed as LogitWeights computes it
-  const int v0 = c * kChunk + threadIdx.x;
+  // the chunk's logits as stats_partial loads them; each weight is computed
+  // as LogitWeights computes it
+  float xp[kPerThread], xq[kPerThread];
+  load_chunk<VEC>(w.lp, c, threadIdx.x, V, xp);
+  if (w.lq && w.qarg < 0) load_chunk<VEC>(w.lq, c, threadIdx.x, V, xq);
   double tr = 0.0, tp = 0.0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    const int v = v0 + i * kScanThreads;
+    const int v = chunk_entry<VEC>(c, threadIdx.x, i);
     if (v < V) {
-      const double pv = exp_sum_term(((double)w.lp[v] - w.mp) * w.ip) * isp;
+      const double pv = exp_term(xp[i], w.mp, w.scp) * isp;
       tp += pv;
       if (w.lq) {
         const double qv = w.qarg >= 0 ? (v == w.qarg ? 1.0 : 0.0)
-                                      : exp_sum_term(((double)w.lq[v] - w.mq) * w.iq) * isq;
+                                      : exp_term(xq[i], w.mq, w.scq) * isq;
         const double r = pv - qv;
         tr += r > 0.0 ? r : 0.0;
       }
@@ -816,12 +849,22 @@ hipError_t launch_verify_sampling(const float* tl, const float* dl, const int32_
   const bool fused = target_stats && target_stats->pmax && target_stats->pmax == ws.tmax &&
                      parts > 0 && parts <= kMaxStatParts;
   const int row0 = fused ? B * (K + 1) : 0;
-  hipLaunchKernelGGL(stats_partial_kernel, dim3((R - row0) * C), dim3(kScanThreads), 0, s, tl, dl,
-                     B, K, V, ws, wp, row0);
+  // 16-byte loads when every row starts on a 16-byte boundary
+  const bool vec = V % 4 == 0 && ((reinterpret_cast<uintptr_t>(tl) | reinterpret_cast<uintptr_t>(dl)) & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL(stats_partial_kernel<true>, dim3((R - row0) * C), dim3(kScanThreads), 0, s,
+                       tl, dl, B, K, V, ws, wp, row0);
+  else
+    hipLaunchKernelGGL(stats_partial_kernel<false>, dim3((R - row0) * C), dim3(kScanThreads), 0, s,
+                       tl, dl, B, K, V, ws, wp, row0);
   hipLaunchKernelGGL(verify_accept_kernel, dim3(B), dim3(kAcceptWaves * kWave), 0, s, tl, dl,
                      tokens, u_accept, B, K, V, ws, wp, fused ? parts : 0);
-  hipLaunchKernelGGL(resid_partial_kernel, dim3(B * C), dim3(kScanThreads), 0, s, tl, dl, B, K, V,
-                     ws, wp);
+  if (vec)
+    hipLaunchKernelGGL(resid_partial_kernel<true>, dim3(B * C), dim3(kScanThreads), 0, s, tl, dl, B,
+                       K, V, ws, wp);
+  else
+    hipLaunchKernelGGL(resid_partial_kernel<false>, dim3(B * C), dim3(kScanThreads), 0, s, tl, dl, B,
+                       K, V, ws, wp);
   hipLaunchKernelGGL(verify_draw_kernel, dim3(B), dim3(kScanThreads), 0, s, tl, dl, tokens,
                      u_sample, B, K, V, out_tokens, n_emitted, ws, wp);
   return hipGetLastError();
