@@ -153,22 +153,31 @@ constexpr int kTileKAlign = 64;  // the kernel needs K to be a multiple of this
 // BK reduction elements per stage: 64 (a whole 128-byte line of each row) or
 // 32 (half a line; the other half follows in the next stage, from L2), which
 // halves a stage so that more of them fit in LDS.
-template <int BM, int BN, int WM, int S, int BK, int NW>
+// KS > 1 splits the reduction inside the workgroup: the waves form KS
+// groups of NW / KS, group g takes k-tiles g, g + KS, ... through a ring of
+// its own, and the KS partial tiles are added through LDS in group order at
+// the end (deterministic). A small tile then still has NW waves' loads in
+// flight.
+template <int BM, int BN, int WM, int S, int BK, int NW, int KS = 1>
 struct TileCfg {
-  static constexpr int WN = NW / WM;             // NW waves: WM along M, WN along N
+  static constexpr int NWG = NW / KS;            // waves per k-group
+  static constexpr int WN = NWG / WM;            // a group's waves: WM along M, WN along N
   static constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
   static constexpr int ROWS = BM + BN;           // LDS rows per stage (x rows, then w rows)
   static constexpr int UPR = BK / 8;             // 16-byte units per row
   static constexpr int RPI = 64 / UPR;           // rows per load instruction
   static constexpr int RPL = 128 / (2 * BK);     // rows per 128-byte bank line
   static constexpr int ROW_BYTES = 2 * BK;
-  static constexpr int L = ROWS / (NW * RPI);    // load instructions per wave per stage
+  static constexpr int L = ROWS / (NWG * RPI);   // load instructions per wave per stage
   static constexpr int STAGE_BYTES = ROWS * ROW_BYTES;
-  static constexpr int LDS_BYTES = S * STAGE_BYTES;
+  static constexpr int RING_BYTES = KS * S * STAGE_BYTES;
+  static constexpr int RED_BYTES = KS > 1 ? KS * BM * BN * 4 : 0;  // partial tiles, after the ring
+  static constexpr int LDS_BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
   static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(TM >= 1 && TN >= 1 && BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
-  static_assert(WM * WN == NW && ROWS % (NW * RPI) == 0, "whole load instructions per wave");
-  static_assert(S >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring");
+  static_assert(NWG * KS == NW && WM * WN == NWG && ROWS % (NWG * RPI) == 0,
+                "whole load instructions per wave");
+  static_assert(S >= 2 && LDS_BYTES <= 160 * 1024 && NW * 64 <= 1024, "LDS ring, workgroup");
 };
 // Stored position of unit u of LDS row r, XOR-swizzled so that a fragment
 // read (16 consecutive rows at one unit) is free of bank conflicts whether
@@ -201,11 +210,11 @@ __device__ __forceinline__ void tile_wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int S, int BK, int NW, bool OUT_BF16>
+template <int BM, int BN, int WM, int S, int BK, int NW, int KS, bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y, int M,
     int N, int K, int n_tiles, int per_xcd) {
-  using C = TileCfg<BM, BN, WM, S, BK, NW>;
+  using C = TileCfg<BM, BN, WM, S, BK, NW, KS>;
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // XCD-grouped tile order: workgroup bid runs on XCD bid % 8
@@ -214,18 +223,20 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
   const int MT = (M + BM - 1) / BM;
   const int tm = t % MT, tn = t / MT;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int kg = wave / C::NWG, wr = wave % C::NWG;  // k-group, wave inside it
+  const int wm = wr / C::WN, wn = wr % C::WN;
   const int n_k = K / BK;
+  const int n_j = (n_k + KS - 1) / KS;  // ring steps; group kg's step st is k-tile st * KS + kg
 
   // This lane's source row and unit for each of its L load instructions: the
-  // instruction covers LDS rows RPI*g .. RPI*g + RPI-1 (g = wave + NW*q); lane
+  // instruction covers LDS rows RPI*g .. RPI*g + RPI-1 (g = wr + NWG*q); lane
   // l writes LDS row RPI*g + l/UPR at stored unit l%UPR, which holds the
   // row's global unit tile_unit_pos(row, l%UPR) (the swizzle is its own
   // inverse).
   const uint16_t* src[C::L];
 #pragma unroll
   for (int q = 0; q < C::L; ++q) {
-    const int r = C::RPI * (wave + NW * q) + lane / C::UPR;
+    const int r = C::RPI * (wr + C::NWG * q) + lane / C::UPR;
     const int u = tile_unit_pos<C>(r, lane % C::UPR);
     const uint16_t* p;
     if (r < BM)
@@ -234,14 +245,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
       p = W + (size_t)min(n0 + (r - BM), N - 1) * K + u * 8;
     src[q] = p;
   }
-  auto issue = [&](int kt) __attribute__((always_inline)) {
-    // stages past the end reload the last one into a slot nobody reads
-    const int kc = min(kt, n_k - 1);
-    const int slot = kt % S;
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    // k-tiles past the end reload the last one into a slot nobody reads
+    const int kc = min(st * KS + kg, n_k - 1);
+    const int slot = kg * S + st % S;
 #pragma unroll
     for (int q = 0; q < C::L; ++q) {
       tile_load_lds(src[q] + (size_t)kc * BK, reinterpret_cast<char*>(lds) + slot * C::STAGE_BYTES +
-                                                  C::RPI * (wave + NW * q) * C::ROW_BYTES);
+                                                  C::RPI * (wr + C::NWG * q) * C::ROW_BYTES);
     }
   };
 
@@ -254,11 +265,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
 #pragma unroll
   for (int s = 0; s < S - 1; ++s) issue(s);
 
-  for (int kt = 0; kt < n_k; ++kt) {
-    tile_wait_vmcnt<(S - 2) * C::L>();  // this wave's loads of stage kt have landed
-    tile_barrier();                     // everyone's; and stage kt-1's slot is free
-    issue(kt + S - 1);
-    const char* base = reinterpret_cast<const char*>(lds) + (kt % S) * C::STAGE_BYTES;
+  for (int st = 0; st < n_j; ++st) {
+    tile_wait_vmcnt<(S - 2) * C::L>();  // this wave's loads of step st have landed
+    tile_barrier();                     // everyone's; and step st-1's slots are free
+    issue(st + S - 1);
+    if (KS > 1 && st * KS + kg >= n_k) continue;  // this group has no k-tile left
+    const char* base = reinterpret_cast<const char*>(lds) + (kg * S + st % S) * C::STAGE_BYTES;
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       const int unit = kk * 4 + (lane >> 4);
@@ -284,6 +296,38 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
   }
   tile_wait_vmcnt<0>();  // the reloads past the end land before the workgroup leaves
 
+  if constexpr (KS > 1) {
+    // partial tiles of the k-groups into LDS (over the ring, once every wave
+    // is done with it), then each output is the sum over groups in order
+    float* red = reinterpret_cast<float*>(lds);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < C::TN; ++jj) {
+        const int col = wn * (BN / C::WN) + jj * 16 + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + r;
+          red[(kg * BM + row) * BN + col] = acc[i][jj][r];
+        }
+      }
+    __syncthreads();
+    for (int e = tid; e < BM * BN; e += NW * 64) {
+      const int row = m0 + e / BN, col = n0 + e % BN;
+      float v = red[e];
+#pragma unroll
+      for (int g = 1; g < KS; ++g) v += red[g * BM * BN + e];
+      if (row < M && col < N) {
+        if (OUT_BF16)
+          tile_store<uint16_t>(Y, (size_t)row * N + col, f32_to_bf16_bits(v));
+        else
+          tile_store<float>(Y, (size_t)row * N + col, v);
+      }
+    }
+    return;
+  }
+
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -303,26 +347,26 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
     }
 }
 
-template <int BM, int BN, int WM, int S, int BK, int NW = 8>
+template <int BM, int BN, int WM, int S, int BK, int NW = 8, int KS = 1>
 static hipError_t launch_tile_t(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16,
                                 int M, int K, int N, hipStream_t s) {
-  using C = TileCfg<BM, BN, WM, S, BK, NW>;
+  using C = TileCfg<BM, BN, WM, S, BK, NW, KS>;
   const int n_tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int per_xcd = (n_tiles + 7) / 8;
   const dim3 grid(8 * per_xcd);
   static const hipError_t a1 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, true>),
+      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, true>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   static const hipError_t a2 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, false>),
+      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, false>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
   if (out_bf16)
-    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, true>), grid, dim3(NW * 64),
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, true>), grid, dim3(NW * 64),
                        C::LDS_BYTES, s, x, w, y, M, N, K, n_tiles, per_xcd);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, false>), grid, dim3(NW * 64),
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, false>), grid, dim3(NW * 64),
                        C::LDS_BYTES, s, x, w, y, M, N, K, n_tiles, per_xcd);
   return hipGetLastError();
 }
@@ -378,7 +422,23 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
-    switch (pick_tile(M, N, cus)) {
+    const int pick = pick_tile(M, N, cus);
+    const long tiles = (long)((M + kTileShapes[pick][0] - 1) / kTileShapes[pick][0]) *
+                       ((N + kTileShapes[pick][1] - 1) / kTileShapes[pick][1]);
+    if (tiles <= cus) {
+      // One round of small tiles: the same tile with the reduction split over
+      // k-groups of eight waves in all, so that each CU has as many loads in
+      // flight as a large tile's (measured on the Llama linears at M = 20 to
+      // 128: O and down 15-30 % faster, QKV 5-20 %).
+      switch (pick) {
+        case 6: return launch_tile_t<64, 64, 2, 4, 64, 8, 2>(x, w, y, out_bf16, M, K, N, s);
+        case 7: return launch_tile_t<64, 32, 2, 4, 64, 8, 2>(x, w, y, out_bf16, M, K, N, s);
+        case 8: return launch_tile_t<32, 32, 2, 4, 64, 8, 2>(x, w, y, out_bf16, M, K, N, s);
+        case 9: return launch_tile_t<32, 16, 2, 4, 64, 8, 4>(x, w, y, out_bf16, M, K, N, s);
+        default: break;
+      }
+    }
+    switch (pick) {
       case 0: return launch_tile_t<256, 256, 4, 2, 64>(x, w, y, out_bf16, M, K, N, s);
       case 1: return launch_tile_t<256, 128, 4, 3, 64>(x, w, y, out_bf16, M, K, N, s);
       case 2: return launch_tile_t<128, 256, 2, 3, 64>(x, w, y, out_bf16, M, K, N, s);
