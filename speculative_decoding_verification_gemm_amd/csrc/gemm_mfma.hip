@@ -372,18 +372,20 @@ static hipError_t launch_tile_t(const uint16_t* x, const uint16_t* w, void* y, b
 }
 
 // Tile shapes (BM, BN), indexed as in the launch switch of
-// launch_gemm_mfma; the first seven use eight waves, the last three (for
-// linears with few positions and few output rows) two or four, so that
-// several of them share a CU.
-static const int kTileShapes[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128}, {128, 64},
-                                     {64, 128},  {64, 64},   {64, 32},   {32, 32},   {32, 16}};
+// launch_gemm_mfma; the first seven use eight waves, the last four (for
+// linears with few positions) two or four, so that several of them share a
+// CU.
+static const int kTileShapes[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128},
+                                     {128, 64},  {64, 128},  {64, 64},   {64, 32},
+                                     {32, 32},   {32, 16},   {32, 64}};
 
 // Time model of one launch, per reduction element: a tile costs
 // a * (BM + BN) (operand lines into LDS and out to the matrix cores) plus
 // b * BM * BN (the products), and the tiles run in ceil(tiles / CUs) rounds.
 // a and b were fitted to measured Llama-shaped linears at M = 320 and 1280
-// on MI355X; at M = 20 to 128 the shape the model picks was the fastest
-// measured, or within 5% of it, for every Llama-3.1-8B linear.
+// on MI355X. At M = 20 to 128 the shapes it picks for the Llama-3.1-8B
+// linears were checked against every small shape forced in turn: the pick
+// was the fastest, or within about 10 % of it.
 static int pick_tile(int M, int N, int cus) {
   const double a = 3.6e-5, b = 8.1e-8;
   const int n = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
@@ -448,7 +450,8 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
       case 6: return launch_tile_t<64, 64, 2, 4, 64>(x, w, y, out_bf16, M, K, N, s);
       case 7: return launch_tile_t<64, 32, 2, 4, 64, 4>(x, w, y, out_bf16, M, K, N, s);
       case 8: return launch_tile_t<32, 32, 2, 6, 64, 4>(x, w, y, out_bf16, M, K, N, s);
-      default: return launch_tile_t<32, 16, 2, 6, 64, 2>(x, w, y, out_bf16, M, K, N, s);
+      case 9: return launch_tile_t<32, 16, 2, 6, 64, 2>(x, w, y, out_bf16, M, K, N, s);
+      default: return launch_tile_t<32, 64, 1, 4, 64, 4>(x, w, y, out_bf16, M, K, N, s);
     }
   }
   if (M <= 32) return launch_mfma_t<32, 64, 1>(x, w, y, out_bf16, M, K, N, s);
