@@ -171,7 +171,7 @@ struct TileCfg {
   static constexpr int L = ROWS / (NWG * RPI);   // load instructions per wave per stage
   static constexpr int STAGE_BYTES = ROWS * ROW_BYTES;
   static constexpr int RING_BYTES = KS * S * STAGE_BYTES;
-  static constexpr int RED_BYTES = KS > 1 ? KS * BM * BN * 4 : 0;  // partial tiles, after the ring
+  static constexpr int RED_BYTES = KS > 1 ? KS * BM * BN * 4 : 0;  // partial tiles, over the drained ring
   static constexpr int LDS_BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
   static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(TM >= 1 && TN >= 1 && BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
