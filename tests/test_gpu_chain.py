@@ -140,3 +140,41 @@ def test_chain_graph_replay(sv, dev):
         torch.cuda.synchronize()
         assert all(torch.equal(a, y) for a, (_, _, y) in zip(want, lin))
     assert ch.error() == 0
+
+
+@pytest.mark.parametrize("stack_name", ["LLAMA_8B", "LLAMA_70B_16L"])
+def test_chain_full_stack_sampled(sv, dev, stack_name):
+    """The whole stack in one chain launch, as the step benchmark runs it:
+    every linear of every layer, then the fp32 lm-head, at M = 5 with the
+    workload's weight distribution. A sample of output columns of every
+    linear (first and last 4 plus 24 random ones) against the fp64 oracle."""
+    import torch
+    from synth import device as sd
+    stack = getattr(synth, stack_name)
+    M = 5
+    lin = []
+    for i, (_, d_in, d_out) in enumerate(stack.all_linears()):
+        last = i == len(stack.all_linears()) - 1
+        x = sd.normal_bf16((M, d_in), 1.0, 9000 + 2 * i, dev)
+        w = sd.normal_bf16((d_out, d_in), synth.WEIGHT_STD, 9001 + 2 * i, dev)
+        y = torch.empty((M, d_out), dtype=torch.float32 if last else torch.bfloat16, device=dev)
+        lin.append((x, w, y))
+    ch = sv.Chain(lin, dev)
+    for _ in range(2):  # a second launch reuses the counters (generations)
+        ch.run()
+        torch.cuda.synchronize()
+        assert ch.error() == 0
+    rng = np.random.default_rng(1)
+    worst = 0.0
+    for i, (x, w, y) in enumerate(lin):
+        n = w.shape[0]
+        cols = np.unique(np.concatenate([np.arange(4), np.arange(n - 4, n), rng.integers(0, n, 24)]))
+        idx = torch.from_numpy(cols).to(dev)
+        ref = oracle.linear(sd.to_bits(x), sd.to_bits(w.index_select(0, idx)))
+        got = y.index_select(1, idx).float().cpu().numpy().astype(np.float64)
+        e = rel_err(got, ref)
+        worst = max(worst, e)
+        assert e <= 2e-2, (i, e)
+    print(f"{stack_name}: {len(lin)} linears, worst sampled rel err {worst:.2e}", flush=True)
+    del lin, ch
+    torch.cuda.empty_cache()
