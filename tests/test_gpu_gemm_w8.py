@@ -175,3 +175,34 @@ def test_w8_chain_plan_mismatch_is_reported(sv, dev):
     torch.cuda.synchronize()
     assert ch.error() == 2
     assert bool((y == 7.0).all())
+
+
+def test_w8_chain_full_8b_stack_sampled(sv, dev):
+    """The whole Llama-8B-shaped stack with FP8 weights in one chain launch,
+    as the FP8 step benchmark runs it (every linear, then the fp32 lm-head,
+    M = 5); the oracle checks 32 sampled output columns of every linear."""
+    import torch
+    stack = synth.LLAMA_8B
+    shapes = [(d_in, d_out, torch.bfloat16) for _, d_in, d_out in stack.all_linears()]
+    shapes[-1] = (shapes[-1][0], shapes[-1][1], torch.float32)
+    lin = _w8_chain_linears(dev, 5, shapes, 7000)
+    ch = sv.Chain(lin, dev)
+    ch.run()
+    torch.cuda.synchronize()
+    assert ch.error() == 0
+    from synth import device as sd
+    rng = np.random.default_rng(2)
+    worst = 0.0
+    for i, (x, w, s, y) in enumerate(lin):
+        n = w.shape[0]
+        rows = np.unique(np.concatenate([np.arange(4), np.arange(n - 4, n), rng.integers(0, n, 24)]))
+        idx = torch.from_numpy(rows).to(dev)
+        ref = oracle.linear_w8(sd.to_bits(x), w.index_select(0, idx).cpu().numpy(),
+                               s.index_select(0, idx).cpu().numpy())
+        got = y.index_select(1, idx).float().cpu().numpy().astype(np.float64)
+        e = rel_err(got, ref)
+        worst = max(worst, e)
+        assert e <= TOL, (i, e)
+    print(f"w8 8B stack: {len(lin)} linears, worst sampled rel err {worst:.2e}", flush=True)
+    del lin, ch
+    torch.cuda.empty_cache()
