@@ -204,9 +204,23 @@ int chain_prepare(int n, int M, void* workspace, size_t workspace_bytes, bool w8
   // arrival, at the end of the wait for the previous linear, and when the
   // first activation chunk is staged, and when the last output stores of
   // the linear have been issued.
+  // The address must lie in one device allocation that holds
+  // (n + 1) * grid * 4 records; anything else is rejected.
   if (const char* env = getenv("SPECV_CHAIN_TRACE")) {
-    unsigned long long v = strtoull(env, nullptr, 0);
-    hdr.trace = reinterpret_cast<unsigned long long*>(v);
+    void* const v = reinterpret_cast<void*>(strtoull(env, nullptr, 0));
+    int cus = 0;
+    rc = check_device(&cus);
+    const size_t need = (size_t)(n + 1) * cus * stream_wgs_per_cu(M, w8) * 4 * sizeof(uint64_t);
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (rc != SPEC_OK || hipMemGetAddressRange(&base, &size, v) != hipSuccess ||
+        static_cast<char*>(v) + need > static_cast<char*>(base) + size) {
+      free(img);
+      (void)hipGetLastError();
+      return fail(SPEC_ERR_INVALID_ARGUMENT,
+                  "SPECV_CHAIN_TRACE is not a device buffer of %zu bytes", need);
+    }
+    hdr.trace = static_cast<unsigned long long*>(v);
   }
   memcpy(img, &hdr, sizeof(hdr));
   hipError_t e = hipMemcpy(workspace, img, bytes, hipMemcpyHostToDevice);

@@ -178,3 +178,24 @@ def test_chain_full_stack_sampled(sv, dev, stack_name):
     print(f"{stack_name}: {len(lin)} linears, worst sampled rel err {worst:.2e}", flush=True)
     del lin, ch
     torch.cuda.empty_cache()
+
+
+def test_chain_trace_buffer_is_validated(sv, dev, monkeypatch):
+    """The diagnostic trace address from SPECV_CHAIN_TRACE is checked on the
+    host before any launch (it must lie in a device allocation with room for
+    the records): an address outside device memory is rejected with an
+    error; a large enough buffer receives the records."""
+    import torch
+    lin = make_linears(dev, 5, [(512, 256, torch.float32), (256, 128, torch.float32)], 4)
+    monkeypatch.setenv("SPECV_CHAIN_TRACE", "0x10")
+    with pytest.raises(sv.SpecVerifyError):
+        sv.Chain(lin, dev)
+    G = torch.cuda.get_device_properties(0).multi_processor_count * 2
+    big = torch.zeros(3 * G * 4, dtype=torch.int64, device=dev)
+    monkeypatch.setenv("SPECV_CHAIN_TRACE", str(big.data_ptr()))
+    ch = sv.Chain(lin, dev)
+    ch.run()
+    torch.cuda.synchronize()
+    assert ch.error() == 0
+    assert int((big != 0).sum()) > 0
+    monkeypatch.delenv("SPECV_CHAIN_TRACE")
