@@ -142,7 +142,9 @@ struct LinSched {
   int K, N;
   int n_it;    // pipeline stages per row block (ceil(K / elems per stage))
   int n_rb;    // row blocks of the linear
-  int my_rb;   // row blocks this workgroup owns (bid, bid + G, ...)
+  int my_rb;   // row blocks this workgroup owns (bid, bid + G, ..., see sched)
+  int q;       // whole rounds of G row blocks
+  int extra;   // this workgroup's row block in the last, partial round, or -1
   int kc;      // activation chunk length (multiple of a stage)
   int ipc;     // stages per chunk
   int xs;      // LDS row stride of the activation chunk, elements (multiple of 512)
@@ -176,7 +178,15 @@ struct Stream {
     s.n_it = (d.K + EPI - 1) / EPI;
     s.n_rb = (d.N + NR - 1) / NR;
     const int bid = blockIdx.x, G = gridDim.x;
-    s.my_rb = s.n_rb > bid ? (s.n_rb - bid + G - 1) / G : 0;
+    // Whole rounds of G row blocks go round-robin (block bid + j G). The r
+    // blocks of a last, partial round go to workgroups on even XCDs first
+    // (bid mod 8 even): those stream 5-8 % faster than the odd ones, so the
+    // extra block lands where it costs least.
+    s.q = s.n_rb / G;
+    const int r = s.n_rb - s.q * G;
+    const int rank = G % 2 != 0 ? bid : (bid & 1) ? (G >> 1) + (bid >> 1) : (bid >> 1);
+    s.extra = rank < r ? s.q * G + rank : -1;
+    s.my_rb = s.q + (s.extra >= 0 ? 1 : 0);
     if (d.K <= KCMAX) {
       // the whole reduction dimension is staged once; LDS rows hold K
       // rounded up to a 512-element block, which may be less than the
@@ -372,7 +382,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
   // weights, so its loads are served by the cache instead of HBM.
   auto load = [&](u32x4 (&buf)[U][RPL], const LinSched& s, const Cursor& cur)
       __attribute__((always_inline)) {
-    const int rb = bid + cur.j * G;
+    const int rb = cur.j < s.q ? bid + cur.j * G : s.extra;
     const int live = -(int)cur.valid;  // all ones, or zero for an exhausted cursor
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
@@ -520,7 +530,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
         for (int m = 0; m < M; ++m) red[(wave * NR + grp * RPL + r) * M + m] = acc[r][m];
     }
     __syncthreads();
-    const int rb = bid + cur.j * G;
+    const int rb = cur.j < s.q ? bid + cur.j * G : s.extra;
     // FP8 weights: the row block's scales through the scalar cache (uniform
     // addresses, counted on lgkmcnt), so no wait on the weight loads in
     // flight; each thread then picks its row's scale.
