@@ -66,7 +66,7 @@ def parse():
                     help="chain: the lm-head is the last linear of the chain launch and "
                          "spec_verify reads its logits; fused: the chain holds the stack only "
                          "and spec_verify runs the lm-head with the target rows' softmax "
-                         "statistics fused into its epilogue (bf16 weights, M <= 16)")
+                         "statistics fused into its epilogue (bf16 weights, M <= 8)")
     ap.add_argument("--stress", action="store_true",
                     help="sampling-stress workload: B=64, K=8, V=128256, target logits "
                          "N(0, 3^2), draft rows calibrated to alpha in {0.6, 0.81, 0.9}; "
@@ -492,12 +492,14 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     fused = args.lm_head == "fused"
-    if fused and (args.w8 or B * (K + 1) > 16):
-        print("--lm-head fused covers bf16 weights at M <= 16", file=sys.stderr)
+    if fused and (args.w8 or B * (K + 1) > 8):
+        print("--lm-head fused covers bf16 weights at M <= 8", file=sys.stderr)
         sys.exit(2)
     wl = Workload(stack, B, K, args.seed, dev, w8=args.w8, fused_lm_head=fused)
     wl.make_drafts(sv, synth.draft_noise_sigma(key, 0.8), args.seed)
-    use_chain = not args.no_chain and wl.M <= 16
+    # the chain runs the streaming kernel: bf16 up to 8 positions (above, the
+    # per-linear tile kernel is faster), FP8 weights up to 16 (its only kernel)
+    use_chain = not args.no_chain and wl.M <= (16 if args.w8 else 8)
     if use_chain:
         wl.make_chain(sv)
 

@@ -133,10 +133,21 @@ int check_bkv(int B, int K, int V) {
   return SPEC_OK;
 }
 
+// Single launches with d_in a multiple of 64 use the streaming kernel up to
+// this many positions and the tile kernel above: on the Llama-3.1-8B
+// linears the tile kernel was measured faster for every linear from 9
+// positions up (the whole stack at M = 10: 3.26 against 4.60 ms, at 16:
+// 3.34 against 6.14 ms), as the streaming kernel's dot products grow with M.
+// Other d_in keep the streaming kernel up to kMaxStreamM.
+constexpr int kMaxStreamGemmM = 8;
+bool use_stream(int M, int d_in) {
+  return M <= specv::kMaxStreamM && (M <= kMaxStreamGemmM || d_in % 64 != 0);
+}
+
 int run_gemm(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M, int d_in,
              int d_out, int cus, hipStream_t s) {
   hipError_t e;
-  if (M <= specv::kMaxStreamM)
+  if (use_stream(M, d_in))
     e = specv::launch_gemm_stream(x, w, nullptr, y, out_bf16, false, M, d_in, d_out,
                                   cus * stream_wgs_per_cu(M), s);
   else if (d_in % 64 == 0 || M > specv::kMaxSkinnyM)
@@ -525,12 +536,12 @@ int spec_verify_warped(const uint16_t* hidden, const uint16_t* lm_head, int d,
   int cus = 0;
   if ((rc = check_device(&cus)) != SPEC_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // With the streaming lm-head (M within its positions) the target rows'
-  // softmax statistics are folded into the GEMM's epilogue, so the logits
-  // are never re-read for them.
+  // With the streaming lm-head (where spec_verify_gemm would use it) the
+  // target rows' softmax statistics are folded into the GEMM's epilogue, so
+  // the logits are never re-read for them.
   specv::LogitStats tstats{};
   int parts = 0;
-  if (lm_head && M <= specv::kMaxStreamM) {
+  if (lm_head && use_stream(M, d)) {
     tstats = specv::target_stats_slot(workspace, B, K, V, t_target);
     parts = cus * stream_wgs_per_cu(M);
     if (!tstats.pmax || parts > specv::kMaxStatParts) {

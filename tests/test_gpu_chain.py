@@ -38,7 +38,12 @@ def make_linears(dev, M, shapes, seed, chained=False):
 
 @pytest.mark.parametrize("M", [1, 5, 8, 16])
 def test_chain_matches_single_launches(sv, dev, M):
+    """A chain computes what single launches of the streaming kernel
+    compute, bit for bit. Above 8 positions a single launch with d_in a
+    multiple of 64 runs the tile kernel instead (different summation order),
+    so there the chain is held to the oracle."""
     import torch
+    from synth import device as sd
     shapes = [(1032, 777, torch.bfloat16), (4096, 6144, torch.bfloat16), (8192, 256, torch.float32),
               (14336, 4096, torch.bfloat16), (264, 3000, torch.float32)]
     lin = make_linears(dev, M, shapes, 100 + M)
@@ -47,9 +52,13 @@ def test_chain_matches_single_launches(sv, dev, M):
     torch.cuda.synchronize()
     assert ch.error() == 0
     for x, w, y in lin:
-        ref = sv.verify_gemm(x, w, out_dtype=y.dtype)
-        torch.cuda.synchronize()
-        assert torch.equal(ref, y)
+        if M <= 8 or x.shape[1] % 64 != 0:
+            ref = sv.verify_gemm(x, w, out_dtype=y.dtype)
+            torch.cuda.synchronize()
+            assert torch.equal(ref, y)
+        else:
+            ref = oracle.linear(sd.to_bits(x), sd.to_bits(w))
+            assert rel_err(y.float().cpu().numpy().astype(np.float64), ref) <= 2e-2
 
 
 def test_chain_of_dependent_layers(sv, dev):

@@ -96,13 +96,14 @@ def test_mfma_kernel(sv, dev, M):
         check(y, oracle.linear(x, w), od, f"mfma M={M} {od}")
 
 
-@pytest.mark.parametrize("M,d_in,d_out", [(17, 512, 4095), (20, 4096, 4096), (20, 256, 28672),
+@pytest.mark.parametrize("M,d_in,d_out", [(9, 512, 4095), (16, 256, 28672), (17, 512, 4095),
+                                           (20, 4096, 4096), (20, 256, 28672),
                                            (31, 128, 20000), (47, 256, 5000),
                                            (65, 512, 4097), (129, 64, 777), (200, 1024, 777),
                                            (256, 512, 4112), (320, 1024, 300), (513, 128, 1000),
                                            (1280, 1024, 777)])
 def test_tile_kernel(sv, dev, M, d_in, d_out):
-    """The pipelined tile kernel (d_in a multiple of 64, M above 16): ragged
+    """The pipelined tile kernel (d_in a multiple of 64, M above 8): ragged
     M and N tails, one or many stages (d_in 64 leaves k-groups without a
     k-tile), the two-, four- and eight-wave tile shapes the dispatcher picks
     (32x16, 32x32, 32x64, 64x32, 64x64, 128x64), with and without k-groups."""
