@@ -133,21 +133,28 @@ int check_bkv(int B, int K, int V) {
   return SPEC_OK;
 }
 
-// Single launches with d_in a multiple of 64 use the streaming kernel up to
-// this many positions and the tile kernel above: on the Llama-3.1-8B
-// linears the tile kernel was measured faster for every linear from 9
-// positions up (the whole stack at M = 10: 3.26 against 4.60 ms, at 16:
-// 3.34 against 6.14 ms), as the streaming kernel's dot products grow with M.
-// Other d_in keep the streaming kernel up to kMaxStreamM.
+// Which kernel a single launch uses when d_in is a multiple of 64 (other
+// d_in stream up to kMaxStreamM positions). The streaming kernel's dot
+// products grow with M while the tile kernel's MFMA work does not, and the
+// streaming kernel is at its best on long linears, where every CU walks many
+// row blocks. Measured on the Llama-3.1-8B linears: from 9 positions up the
+// tile kernel is faster on every linear (the whole stack at M = 10: 3.26
+// against 4.60 ms; at 16: 3.34 against 6.14 ms); at 1 to 8 positions it is
+// faster on QKV, O and down (at M = 5: 13.4 against 18.9 us, 10.2 against
+// 14.9, 26.2 against 28.5) and slower on gate/up and the lm-head (47.1
+// against 45.0 us, 179 against 164), which hold 2^26 weights or more.
 constexpr int kMaxStreamGemmM = 8;
-bool use_stream(int M, int d_in) {
-  return M <= specv::kMaxStreamM && (M <= kMaxStreamGemmM || d_in % 64 != 0);
+constexpr long long kStreamMinWeights = 1LL << 26;
+bool use_stream(int M, int d_in, int d_out) {
+  if (M > specv::kMaxStreamM) return false;
+  if (d_in % 64 != 0) return true;
+  return M <= kMaxStreamGemmM && (long long)d_in * d_out >= kStreamMinWeights;
 }
 
 int run_gemm(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M, int d_in,
              int d_out, int cus, hipStream_t s) {
   hipError_t e;
-  if (use_stream(M, d_in))
+  if (use_stream(M, d_in, d_out))
     e = specv::launch_gemm_stream(x, w, nullptr, y, out_bf16, false, M, d_in, d_out,
                                   cus * stream_wgs_per_cu(M), s);
   else if (d_in % 64 == 0 || M > specv::kMaxSkinnyM)
@@ -541,7 +548,7 @@ int spec_verify_warped(const uint16_t* hidden, const uint16_t* lm_head, int d,
   // the logits are never re-read for them.
   specv::LogitStats tstats{};
   int parts = 0;
-  if (lm_head && use_stream(M, d)) {
+  if (lm_head && use_stream(M, d, V)) {
     tstats = specv::target_stats_slot(workspace, B, K, V, t_target);
     parts = cus * stream_wgs_per_cu(M);
     if (!tstats.pmax || parts > specv::kMaxStatParts) {

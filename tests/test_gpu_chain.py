@@ -39,20 +39,23 @@ def make_linears(dev, M, shapes, seed, chained=False):
 @pytest.mark.parametrize("M", [1, 5, 8, 16])
 def test_chain_matches_single_launches(sv, dev, M):
     """A chain computes what single launches of the streaming kernel
-    compute, bit for bit. Above 8 positions a single launch with d_in a
-    multiple of 64 runs the tile kernel instead (different summation order),
-    so there the chain is held to the oracle."""
+    compute, bit for bit. A single launch with d_in a multiple of 64 runs the
+    tile kernel instead (different summation order) above 8 positions, or on
+    a linear of fewer than 2^26 weights; there the chain is held to the
+    oracle."""
     import torch
     from synth import device as sd
     shapes = [(1032, 777, torch.bfloat16), (4096, 6144, torch.bfloat16), (8192, 256, torch.float32),
-              (14336, 4096, torch.bfloat16), (264, 3000, torch.float32)]
+              (14336, 4096, torch.bfloat16), (264, 3000, torch.float32),
+              (4096, 16400, torch.bfloat16)]
     lin = make_linears(dev, M, shapes, 100 + M)
     ch = sv.Chain(lin, dev)
     ch.run()
     torch.cuda.synchronize()
     assert ch.error() == 0
     for x, w, y in lin:
-        if M <= 8 or x.shape[1] % 64 != 0:
+        d_in, d_out = x.shape[1], w.shape[0]
+        if d_in % 64 != 0 or (M <= 8 and d_in * d_out >= 1 << 26):
             ref = sv.verify_gemm(x, w, out_dtype=y.dtype)
             torch.cuda.synchronize()
             assert torch.equal(ref, y)

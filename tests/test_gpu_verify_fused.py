@@ -1,6 +1,8 @@
 """GPU parity of spec_verify with the lm-head on the streaming kernel and the
-target rows' softmax statistics fused into its epilogue: B*(K+1) <= 8, or up
-to 16 when d is not a multiple of 64 (where spec_verify_gemm also streams).
+target rows' softmax statistics fused into its epilogue. spec_verify streams
+the lm-head where spec_verify_gemm would: B*(K+1) <= 8 with at least 2^26
+weights (V*d), or up to 16 positions when d is not a multiple of 64; the
+cases below all take that path.
 
 Each workgroup of the lm-head launch folds its logits into a running
 (max, fp64 sum of exp) per position, or the first index of the maximum for a
@@ -23,14 +25,14 @@ pytestmark = pytest.mark.gpu
 
 # B, K, V, d, t_target, t_draft
 CASES = [
-    (1, 4, 1000, 256, 1.0, 1.0),      # 63 row blocks: most workgroups hold no rows
-    (1, 4, 4097, 256, 1.0, 1.0),      # last row block holds a single row
+    (1, 4, 1000, 264, 1.0, 1.0),      # 63 row blocks: most workgroups hold no rows
+    (1, 4, 4097, 264, 1.0, 1.0),      # last row block holds a single row
     (1, 4, 128256, 4096, 1.0, 1.0),   # the Llama-3.1-8B lm-head at M = 5
-    (2, 4, 128256, 4104, 1.0, 1.0),   # M = 10 (d not a multiple of 64)
+    (2, 4, 128256, 4104, 1.0, 1.0),   # M = 10
     (3, 4, 32000, 520, 0.7, 1.3),     # M = 15, temperature-warped
-    (1, 4, 32000, 512, 0.0, 1.0),     # greedy target
-    (2, 3, 5000, 256, 1.0, 0.0),      # greedy draft
-    (1, 1, 7, 64, 1.0, 1.0),          # V below one row block, M = 2
+    (1, 4, 32000, 520, 0.0, 1.0),     # greedy target
+    (2, 3, 5000, 264, 1.0, 0.0),      # greedy draft
+    (1, 1, 7, 72, 1.0, 1.0),          # V below one row block, M = 2
     (8, 1, 2000, 264, 1.0, 1.0),      # M = 16, the most positions of the fused path
 ]
 
