@@ -86,8 +86,10 @@ const char* spec_last_error(void);
  *          rounded to nearest even (SPEC_BF16, 2-byte aligned).
  *   Limits: 1 <= M <= 65536, 8 <= d_in <= 2^20 with d_in % 8 == 0,
  *   1 <= d_out <= 2^24.
- * Small M runs a vector-ALU weight-streaming kernel; M above a measured
- * crossover runs a bf16 MFMA kernel. Deterministic: the same inputs give
+ * Few rows on a large linear (M <= 8 with at least 2^26 weights, or
+ * M <= 16 when d_in is not a multiple of 64) run a vector-ALU
+ * weight-streaming kernel; every other shape runs a bf16 MFMA kernel (the
+ * crossovers were measured on MI355X). Deterministic: the same inputs give
  * bitwise identical outputs.
  */
 int spec_verify_gemm(const uint16_t* x, const uint16_t* w, void* y, int y_dtype,
