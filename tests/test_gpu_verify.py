@@ -105,12 +105,15 @@ def test_verify_stress_shape(sv, dev, alpha):
     compare(out, n, ref, f"stress alpha={alpha}")
 
 
-def test_verify_llama8b_with_lm_head(sv, dev):
+@pytest.mark.parametrize("B", [1, 2])
+def test_verify_llama8b_with_lm_head(sv, dev, B):
     """The 8B lm-head 4096 -> 128256 on the GPU, then sampling; the oracle
-    computes its own logits from the same bf16 inputs."""
+    computes its own logits from the same bf16 inputs. B = 1 (M = 5) runs the
+    lm-head on the streaming kernel with the statistics in its epilogue,
+    B = 2 (M = 10) on the tile kernel followed by the statistics pass."""
     import torch
     from synth import device as sd
-    B, K, V, dm = 1, 4, 128256, 4096
+    K, V, dm = 4, 128256, 4096
     lm = sd.normal_bf16((V, dm), synth.WEIGHT_STD, 1234, dev)
     hidden = sd.normal_bf16((B * (K + 1), dm), 1.0, 1235, dev)
     ref_logits = oracle.linear(sd.to_bits(hidden), sd.to_bits(lm)).astype(np.float32)
