@@ -67,6 +67,12 @@ def parse():
                          "spec_verify reads its logits; fused: the chain holds the stack only "
                          "and spec_verify runs the lm-head with the target rows' softmax "
                          "statistics fused into its epilogue (bf16 weights, M <= 8)")
+    ap.add_argument("--t-target", type=float, default=1.0,
+                    help="temperature of the target's distribution in the sampling stage "
+                         "(0: greedy verification)")
+    ap.add_argument("--t-draft", type=float, default=1.0,
+                    help="temperature of the draft's distribution (0: greedy drafts); the draft "
+                         "tokens are drawn from it")
     ap.add_argument("--stress", action="store_true",
                     help="sampling-stress workload: B=64, K=8, V=128256, target logits "
                          "N(0, 3^2), draft rows calibrated to alpha in {0.6, 0.81, 0.9}; "
@@ -118,6 +124,7 @@ class Workload:
 
         self.stack, self.B, self.K, self.dev, self.w8 = stack, B, K, dev, w8
         self.fused_lm_head = fused_lm_head  # lm-head runs inside spec_verify
+        self.t_target, self.t_draft = 1.0, 1.0  # sampling temperatures (0: greedy)
         self.M = B * (K + 1)
         self.linears = []  # (name, x, w, y)
         self.scales = []   # FP8 weights: per-row scales of each linear
@@ -154,7 +161,11 @@ class Workload:
         self.lm_head_gemm(sv)
         tl = self.target_logits[:, :self.K, :]
         self.draft_logits = (tl + sd.normal_f32(tl.shape, sigma, seed * 7 + 5, self.dev)).contiguous()
-        self.draft_tokens = sd.gumbel_max_tokens(self.draft_logits, seed * 7 + 6)
+        if self.t_draft == 0.0:
+            self.draft_tokens = self.draft_logits.argmax(dim=-1).int()
+        else:
+            self.draft_tokens = sd.gumbel_max_tokens(
+                (self.draft_logits / self.t_draft).contiguous(), seed * 7 + 6)
         self.workspace = sv.new_workspace(self.B, self.K, self.V, self.dev)
         torch.cuda.synchronize()
 
@@ -193,7 +204,7 @@ class Workload:
         lm = {"hidden": self.hidden, "lm_head": self.lm_head} if self.fused_lm_head else {}
         sv.verify(self.target_logits, self.draft_logits, self.draft_tokens, self.u_accept,
                   self.u_sample, workspace=self.workspace, out_tokens=self.out_tokens,
-                  n_emitted=self.n_emitted, **lm)
+                  n_emitted=self.n_emitted, t_target=self.t_target, t_draft=self.t_draft, **lm)
 
     def gemm_bytes(self):
         """Algorithmic HBM bytes of the GEMM phase: every weight once, every
@@ -495,7 +506,11 @@ def main():
     if fused and (args.w8 or B * (K + 1) > 8):
         print("--lm-head fused covers bf16 weights at M <= 8", file=sys.stderr)
         sys.exit(2)
+    if not (args.t_target >= 0.0 and args.t_draft >= 0.0):
+        print("temperatures must be >= 0", file=sys.stderr)
+        sys.exit(2)
     wl = Workload(stack, B, K, args.seed, dev, w8=args.w8, fused_lm_head=fused)
+    wl.t_target, wl.t_draft = args.t_target, args.t_draft
     wl.make_drafts(sv, synth.draft_noise_sigma(key, 0.8), args.seed)
     # the chain runs the streaming kernel: bf16 up to 8 positions (above, the
     # per-linear tile kernel is faster), FP8 weights up to 16 (its only kernel)
@@ -564,8 +579,12 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     # Expected tokens per round from each draft row's exact acceptance rate
     # alpha_j = sum_x min(p_j(x), q_j(x)): E[N] = 1 + sum_i prod_{j<=i} alpha_j.
-    p_rows = torch.softmax(wl.target_logits[:, :K, :].double(), dim=-1)
-    q_rows = torch.softmax(wl.draft_logits.double(), dim=-1)
+    def warped(logits, t):
+        if t == 0.0:  # one-hot at the first maximum
+            return torch.nn.functional.one_hot(logits.argmax(dim=-1), logits.shape[-1]).double()
+        return torch.softmax(logits.double() / t, dim=-1)
+    p_rows = warped(wl.target_logits[:, :K, :], args.t_target)
+    q_rows = warped(wl.draft_logits, args.t_draft)
     alpha = torch.minimum(p_rows, q_rows).sum(-1)  # [B][K]
     e_n = (1.0 + torch.cumprod(alpha, dim=1).sum(1)).mean().item()
 
@@ -597,6 +616,7 @@ def main():
             "lm_head": ("in spec_verify, softmax statistics fused into its epilogue" if fused
                         else "last linear of the GEMM phase"),
             "weights": "fp8_e4m3 + fp32 row scale" if args.w8 else "bf16",
+            "temperatures": {"target": args.t_target, "draft": args.t_draft},
         },
         "pct_hbm_peak_in_verify": 100.0 * achieved / HBM_PEAK_GBS,
         "ms_gemm_phase": ms_gemm,
