@@ -175,11 +175,14 @@ def test_batch_sweep_lm_head_m1280(sv, dev):
     check(y, ref, torch.float32, "sweep M=1280 lm-head")
 
 
-@pytest.mark.parametrize("M", [5, 80, 320])
-def test_deterministic(sv, dev, M):
+@pytest.mark.parametrize("M,d_out", [(5, 6144), (5, 16400), (80, 6144), (320, 6144)])
+def test_deterministic(sv, dev, M, d_out):
+    """Two launches give bitwise equal outputs: the tile kernel with and
+    without k-groups (M = 5, 80, 320 on a 6144-row linear) and the streaming
+    kernel (M = 5 on a linear of 2^26 weights or more)."""
     import torch
     from synth import device as sd
-    w = sd.normal_bf16((6144, 4096), 0.02, 3, dev)
+    w = sd.normal_bf16((d_out, 4096), 0.02, 3, dev)
     x = sd.normal_bf16((M, 4096), 1.0, 4, dev)
     a = sv.verify_gemm(x, w)
     b = sv.verify_gemm(x, w)
