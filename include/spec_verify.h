@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 4
+#define SPEC_ABI_VERSION 5
 
 /* Status codes. */
 #define SPEC_OK 0
@@ -146,6 +146,18 @@ int spec_chain_prepare(const spec_linear* linears, int n, int M, void* workspace
  * mismatch computes nothing and sets bit 1 of spec_chain_error). The call
  * is asynchronous and capturable; launches that use the same workspace must
  * be ordered (same stream).
+ *
+ * Precondition: the launch is one persistent workgroup per compute unit
+ * (more where occupancy allows), and its barriers assume that all of them
+ * are resident at once. A launch that shares the GPU with other work that
+ * keeps compute units occupied for long may find some workgroups not yet
+ * started; the waiting ones then give up after a bounded number of polls
+ * (well under a second) instead of hanging, finish the launch, and set bit
+ * 0 of spec_chain_error; the outputs of that launch are then not valid, and
+ * spec_chain_reset brings the workspace back to a consistent state. The
+ * call itself returns SPEC_OK in that case (the failure happens on the
+ * device, after the call has returned): callers that cannot rule out such
+ * sharing should read spec_chain_error after synchronizing.
  */
 int spec_verify_gemm_chain(int n, int M, void* workspace, void* stream);
 
@@ -242,6 +254,20 @@ int spec_verify_attention(const uint16_t* q, const uint16_t* k_cache, const uint
  * a launch did not match the prepared plan.
  */
 int spec_chain_error(void* workspace, int* error);
+
+/*
+ * spec_chain_reset -- set the barrier counters of a prepared chain workspace
+ * to the values they hold after `generation` complete launches, and clear
+ * its error word (synchronous; no launch may be using the workspace). The
+ * descriptors are kept. After a barrier gave up (bit 0 of
+ * spec_chain_error) the counters no longer agree with one another, and every
+ * later launch would give up too; a reset makes the next launch consistent
+ * again. Every counter advances by a fixed amount per launch and is compared
+ * modulo 2^32, so any generation is valid, including those close to the
+ * 32-bit wrap of the counters. Returns SPEC_ERR_INVALID_ARGUMENT if the
+ * workspace holds no prepared chain.
+ */
+int spec_chain_reset(void* workspace, unsigned generation);
 
 /*
  * spec_softmax -- p = softmax(logits) per row, T = 1.

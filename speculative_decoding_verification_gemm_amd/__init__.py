@@ -61,6 +61,7 @@ SIGNATURES = {
     "spec_verify_attention_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i]),
     "spec_verify_attention": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _z, _p]),
     "spec_chain_error": (_i, [_p, ctypes.POINTER(ctypes.c_int)]),
+    "spec_chain_reset": (_i, [_p, ctypes.c_uint]),
     "spec_verify": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _z, _p]),
     "spec_verify_warped": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _f, _f, _p, _p, _p,
                                 _z, _p]),
@@ -381,3 +382,9 @@ class Chain:
         e = ctypes.c_int(0)
         check(lib.spec_chain_error(_ptr(self.workspace), ctypes.byref(e)))
         return e.value
+
+    def reset(self, generation=0):
+        """Counters as after `generation` complete launches, error word
+        cleared (synchronous; spec_chain_reset)."""
+        _torch().cuda.synchronize()
+        check(lib.spec_chain_reset(_ptr(self.workspace), int(generation) & 0xFFFFFFFF))

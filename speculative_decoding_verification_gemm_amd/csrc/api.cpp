@@ -13,6 +13,7 @@
 #include <atomic>
 
 #include "../../include/spec_verify.h"
+#include "chain_sync.h"
 #include "internal.h"
 
 namespace {
@@ -59,8 +60,8 @@ int check_device(int* cus = nullptr) {
 }
 
 // Resident workgroups per CU for the streaming kernel: the occupancy limit,
-// capped at 2 (measured best for the Llama-shaped linears); the
-// SPECV_STREAM_WGS_PER_CU environment variable overrides the cap.
+// capped at 2 (measured best for the Llama-shaped linears). Diagnostic
+// builds (SPECV_DIAGNOSTICS) let SPECV_STREAM_WGS_PER_CU override the cap.
 std::atomic<int> g_stream_occ[2][17];
 int stream_wgs_per_cu(int M, bool w8 = false) {
   int occ = g_stream_occ[w8][M].load(std::memory_order_relaxed);
@@ -69,10 +70,12 @@ int stream_wgs_per_cu(int M, bool w8 = false) {
     g_stream_occ[w8][M].store(occ, std::memory_order_relaxed);
   }
   int cap = 2;
+#if defined(SPECV_DIAGNOSTICS)
   if (const char* env = getenv("SPECV_STREAM_WGS_PER_CU")) {
     const int v = atoi(env);
     if (v > 0) cap = v;
   }
+#endif
   return occ < cap ? occ : cap;
 }
 
@@ -208,8 +211,9 @@ int chain_prepare(int n, int M, void* workspace, size_t workspace_bytes, bool w8
     free(img);
     return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   }
-  int rc = check_device();
-  if (rc != SPEC_OK) {
+  int rc = SPEC_OK;
+  int cus = 0;
+  if ((rc = check_device(&cus)) != SPEC_OK) {
     free(img);
     return rc;
   }
@@ -217,6 +221,9 @@ int chain_prepare(int n, int M, void* workspace, size_t workspace_bytes, bool w8
   hdr.magic = w8 ? specv::kChainMagicW8 : specv::kChainMagic;
   hdr.n = n;
   hdr.M = M;
+  hdr.grid = cus * stream_wgs_per_cu(M, w8);
+  hdr.spin_limit = specv::kChainSpinLimit;
+#if defined(SPECV_DIAGNOSTICS)
   // Diagnostics: SPECV_CHAIN_TRACE=<device address of n * grid * 4 uint64>
   // records, per linear and workgroup, the wall clock (100 MHz ticks) at
   // arrival, at the end of the wait for the previous linear, and when the
@@ -226,12 +233,10 @@ int chain_prepare(int n, int M, void* workspace, size_t workspace_bytes, bool w8
   // (n + 1) * grid * 4 records; anything else is rejected.
   if (const char* env = getenv("SPECV_CHAIN_TRACE")) {
     void* const v = reinterpret_cast<void*>(strtoull(env, nullptr, 0));
-    int cus = 0;
-    rc = check_device(&cus);
-    const size_t need = (size_t)(n + 1) * cus * stream_wgs_per_cu(M, w8) * 4 * sizeof(uint64_t);
+    const size_t need = (size_t)(n + 1) * hdr.grid * 4 * sizeof(uint64_t);
     hipDeviceptr_t base = nullptr;
     size_t size = 0;
-    if (rc != SPEC_OK || hipMemGetAddressRange(&base, &size, v) != hipSuccess ||
+    if (hipMemGetAddressRange(&base, &size, v) != hipSuccess ||
         static_cast<char*>(v) + need > static_cast<char*>(base) + size) {
       free(img);
       (void)hipGetLastError();
@@ -240,6 +245,7 @@ int chain_prepare(int n, int M, void* workspace, size_t workspace_bytes, bool w8
     }
     hdr.trace = static_cast<unsigned long long*>(v);
   }
+#endif
   memcpy(img, &hdr, sizeof(hdr));
   hipError_t e = hipMemcpy(workspace, img, bytes, hipMemcpyHostToDevice);
   free(img);
@@ -415,6 +421,45 @@ int spec_verify_gemm_w8(const uint16_t* x, const uint8_t* w, const float* w_scal
                                             d_out, cus * stream_wgs_per_cu(M, true),
                                             static_cast<hipStream_t>(stream)),
                   "spec_verify_gemm_w8");
+}
+
+int spec_chain_reset(void* workspace, unsigned generation) {
+  clear_error();
+  if (!workspace) return fail(SPEC_ERR_INVALID_ARGUMENT, "null workspace");
+  if (!aligned(workspace, 256)) return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  int rc = check_device();
+  if (rc != SPEC_OK) return rc;
+  specv::ChainSync hdr;
+  hipError_t e = hipMemcpy(&hdr, workspace, sizeof(hdr), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SPEC_ERR_HIP, "chain header read: %s", hipGetErrorString(e));
+  if ((hdr.magic != specv::kChainMagic && hdr.magic != specv::kChainMagicW8) || hdr.n < 1 ||
+      hdr.n > kMaxChain || hdr.grid < 1)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "workspace holds no prepared chain");
+  // Every counter as it stands after `generation` complete launches (the
+  // invariants of chain_sync.h), and the error word cleared.
+  const int n = hdr.n, G = hdr.grid;
+  const int n_groups = G < specv::kArriveGroups ? G : specv::kArriveGroups;
+  const size_t words = specv::chain_counts_bytes(n) / 4;
+  unsigned* img = static_cast<unsigned*>(calloc(words, sizeof(unsigned)));
+  if (!img) return fail(SPEC_ERR_HIP, "host staging allocation failed");
+  const size_t rel = specv::chain_release_offset(n);
+  for (int l = 0; l < n; ++l) {
+    img[l] = generation * (unsigned)n_groups;
+    for (int x = 0; x < specv::kReleaseLanes; ++x)
+      img[rel + ((size_t)l * specv::kBarrierLines + x) * 16] = specv::chain_target(generation, G);
+    for (int g = 0; g < specv::kArriveGroups; ++g)
+      img[rel + ((size_t)l * specv::kBarrierLines + specv::kReleaseLanes + g) * 16] =
+          generation * specv::chain_group_size(G, g, specv::kArriveGroups);
+  }
+  hdr.gen = generation;
+  hdr.exit_count = specv::chain_target(generation, G);
+  hdr.error = 0;
+  char* base = static_cast<char*>(workspace);
+  e = hipMemcpy(base + chain_counts_offset(), img, words * 4, hipMemcpyHostToDevice);
+  free(img);
+  if (e == hipSuccess) e = hipMemcpy(base, &hdr, sizeof(hdr), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return fail(SPEC_ERR_HIP, "chain reset: %s", hipGetErrorString(e));
+  return SPEC_OK;
 }
 
 int spec_chain_error(void* workspace, int* error) {

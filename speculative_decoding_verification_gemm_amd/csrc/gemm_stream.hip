@@ -43,18 +43,24 @@
 // issued per barrier. Counters are generation-based, so the workspace never
 // needs clearing between launches; a bounded spin turns a stalled barrier
 // into an error flag instead of a hang.
+//
+// Diagnostic builds (SPECV_DIAGNOSTICS defined) also record per-workgroup
+// timestamps at every barrier and accept tile-parameter overrides; the
+// library as built for use has neither.
 
 #include <limits.h>
 #include <math.h>
 
 #include <type_traits>
 
+#include "chain_sync.h"
 #include "common.h"
 #include "internal.h"
 
 namespace specv {
 
-#ifndef SPECV_STREAM_WAVES
+#if !defined(SPECV_DIAGNOSTICS) || !defined(SPECV_STREAM_WAVES)
+#undef SPECV_STREAM_WAVES
 #define SPECV_STREAM_WAVES 8
 #endif
 constexpr int kStreamWaves = SPECV_STREAM_WAVES;  // one workgroup per CU
@@ -70,11 +76,7 @@ struct WFmt {
   static constexpr int kEsz = W8 ? 1 : 2;
 };
 constexpr int kCachePolicyDevice = 16;  // buffer-load aux bits: sc1 (device scope)
-constexpr int kSpinLimit = 1 << 18;  // well under a second of polling before a barrier gives up
-#ifndef SPECV_POLL_SLEEP
-#define SPECV_POLL_SLEEP 4
-#endif
-constexpr int kPollSleep = SPECV_POLL_SLEEP;  // s_sleep units (64 clocks each) between polls
+constexpr int kPollSleep = 4;  // s_sleep units (64 clocks each) between polls
 
 // Pointers taken from a descriptor are generic; naming the global address
 // space lets the compiler emit global (not flat) loads and stores, which
@@ -238,8 +240,8 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
   double st_sum = 0.0;
   int st_arg = INT_MAX;
   unsigned* counts = is_chain ? reinterpret_cast<unsigned*>(sync + 1) : nullptr;
-  if (is_chain &&
-      (sync->magic != (W8 ? kChainMagicW8 : kChainMagic) || sync->n != n_lin || sync->M != M)) {
+  if (is_chain && (sync->magic != (W8 ? kChainMagicW8 : kChainMagic) || sync->n != n_lin ||
+                   sync->M != M || sync->grid != G)) {
     if (bid == 0 && tid == 0)
       __hip_atomic_fetch_or(&sync->error, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;  // every workgroup reads the same header and leaves
@@ -256,19 +258,28 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
   };
 
   // ---- barrier between linears (chain mode)
-  unsigned target = 0;
+  // gen1: launches of this chain including this one; every counter target
+  // of the launch derives from it (modulo 2^32, as the counters wrap).
+  unsigned gen1 = 0, target = 0;
+  int spin_limit = 0;
   if (is_chain) {
     if (tid == 0) s_gen = __hip_atomic_load(&sync->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    target = (s_gen + 1u) * (unsigned)G;
+    gen1 = s_gen + 1u;
+    target = chain_target(gen1, G);
+    spin_limit = sync->spin_limit;
   }
   // Arrival: every wave's device-scope output stores have completed (the
   // caller waited on vmcnt) before the barrier, so the count only rises once
   // the linear's outputs are visible at device scope.
   // Global (not flat) stores: a pending flat access would make the
   // compiler wait for every load in flight wherever it needs a vmcnt wait.
-  SPECV_GLOBAL unsigned long long* trace =
+#if defined(SPECV_DIAGNOSTICS)
+  SPECV_GLOBAL unsigned long long* const trace =
       is_chain ? gptr_mut<unsigned long long>(sync->trace) : nullptr;
+#else
+  SPECV_GLOBAL unsigned long long* const trace = nullptr;  // no timestamps
+#endif
   // Arrivals are counted in two levels: each workgroup bumps the counter of
   // its group (bid mod kArriveGroups, one 64-byte line each), and the last of
   // a group bumps the linear's counter. When every workgroup finishes a
@@ -286,14 +297,13 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
     if (tid == 0) {
       if (trace) trace[((size_t)l * G + bid) * 4] = wall_clock64();
       const int g = bid % kArriveGroups;
-      const unsigned gen1 = target / (unsigned)G;  // launches including this one
-      const unsigned gsize = (unsigned)((G - g + kArriveGroups - 1) / kArriveGroups);
+      const unsigned gsize = chain_group_size(G, g, kArriveGroups);
       unsigned* gc = release + ((size_t)l * kBarrierLines + kReleaseLanes + g) * 16;
       const unsigned gp = __hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (gp + 1u == gen1 * gsize) {
+      if (chain_group_complete(gp, gen1, gsize)) {
         const unsigned prev =
             __hip_atomic_fetch_add(&counts[l], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev + 1u == gen1 * (unsigned)n_groups) {
+        if (chain_linear_complete(prev, gen1, n_groups)) {
           for (int x = 0; x < kReleaseLanes; ++x)
             __hip_atomic_store(flag(l, x), target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -304,8 +314,9 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream_kernel(StreamLinea
     if (tid == 0) {
       int spins = 0;
       const unsigned* f = flag(l, bid % kReleaseLanes);
-      while ((int)(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - target) < 0) {
-        if (++spins > kSpinLimit) {
+      while (!chain_released(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                             target)) {
+        if (++spins > spin_limit) {
           __hip_atomic_fetch_or(&sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
@@ -694,7 +705,8 @@ static hipError_t launch_m(const StreamLinear& single, const StreamLinear* chain
 // resident at M = 5); DEPTH register stages of U * RPL 16-byte loads per
 // lane in flight (8 KB per wave per stage; two-wave-per-SIMD register
 // budget).
-#ifndef SPECV_T5
+#if !defined(SPECV_DIAGNOSTICS) || !defined(SPECV_T5)
+#undef SPECV_T5
 #define SPECV_T5(X) X(5, 4, 2, 14336, 4)
 #endif
 #define SPECV_STREAM_TABLE(X) \
@@ -719,7 +731,10 @@ static hipError_t launch_m(const StreamLinear& single, const StreamLinear* chain
 // of U = 2 segments covers 4096 reduction elements in the same 8 loads per
 // lane as a bf16 stage (half the bytes each). KCMAX as for bf16 (the LDS
 // holds bf16 activations either way).
-#ifndef SPECV_STREAM_W8_TABLE
+#if defined(SPECV_DIAGNOSTICS) && defined(SPECV_STREAM_W8_TABLE)
+// (diagnostic build: table given on the command line)
+#else
+#undef SPECV_STREAM_W8_TABLE
 #define SPECV_STREAM_W8_TABLE(X) \
   X(1, 4, 2, 32768, 4)            \
   X(2, 4, 2, 32768, 4)            \

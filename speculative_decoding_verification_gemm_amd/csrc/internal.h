@@ -39,13 +39,17 @@ struct ChainSync {
   unsigned magic;
   int n;                // linears in the plan
   int M;                // rows of every x
-  int reserved[2];
-  unsigned long long* trace;  // optional per-linear timestamps (nullptr: off)
+  int grid;             // workgroups per launch (fixed by the device and M)
+  int spin_limit;       // polls before a barrier wait gives up
+  unsigned long long* trace;  // per-linear timestamps (diagnostic builds only; else null)
   int pad[6];           // header is one 64-byte line
 };
 static_assert(sizeof(ChainSync) == 64, "chain header is one cache line");
 constexpr unsigned kChainMagic = 0x53504348u;    // "SPCH": bf16 weights
 constexpr unsigned kChainMagicW8 = 0x53503848u;  // "SP8H": FP8 E4M3 weights
+// Polls of a release flag (each followed by an s_sleep of about 256 clocks)
+// before a barrier wait gives up and sets error bit 0: well under a second.
+constexpr int kChainSpinLimit = 1 << 18;
 // Chain workspace after the header: n arrival counters, then (64-byte
 // aligned) per linear kReleaseLanes release flags and kArriveGroups group
 // arrival counters, one 64-byte line each, then the descriptors.

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(sv.lib, n), n
 
@@ -33,7 +33,7 @@ def test_binding_covers_exactly_the_header(sv):
 
 
 def test_version_and_status_strings(sv):
-    assert sv.abi_version() == 4
+    assert sv.abi_version() == 5
     for code, name in [(0, b"SPEC_OK"), (-1, b"SPEC_ERR_INVALID_ARGUMENT"),
                        (-2, b"SPEC_ERR_ALIGNMENT"), (-3, b"SPEC_ERR_UNSUPPORTED"),
                        (-4, b"SPEC_ERR_WORKSPACE"), (-5, b"SPEC_ERR_HIP")]:
@@ -225,3 +225,5 @@ def test_chain_rejects(sv):
     assert g(2, 5, A + 8, None) == -4
     import ctypes
     assert sv.lib.spec_chain_error(None, ctypes.byref(ctypes.c_int())) == -1
+    assert sv.lib.spec_chain_reset(None, 0) == -1
+    assert sv.lib.spec_chain_reset(A + 8, 0) == -4

@@ -161,18 +161,23 @@ def test_full_size_lm_head_m5(sv, dev, d_in):
     check(y, ref, torch.float32, f"lm-head {d_in}->128256")
 
 
-@pytest.mark.parametrize("M", [20, 80, 320, 1280])
-@pytest.mark.parametrize("d_in,d_out", [(4096, 28672), (14336, 4096)])
+# The batch sweep of the Llama-3.1-8B shapes (B = 4, 16, 64, 256 at K = 4):
+# every linear at every swept M, so every tile instantiation the dispatcher
+# picks for that workload (64x128 for QKV at M = 320, 128x256 for the
+# lm-head at M = 80, the k-group small tiles at M = 20 and 80, ...) is held
+# to the oracle, in the output type the step uses and in the other one.
+SWEEP_M = [20, 80, 320, 1280]
+SWEEP_LINEARS = LLAMA8B + [(4096, 128256)]
+
+
+@pytest.mark.parametrize("M", SWEEP_M)
+@pytest.mark.parametrize("d_in,d_out", SWEEP_LINEARS)
 def test_batch_sweep_shapes(sv, dev, M, d_in, d_out):
     import torch
-    y, ref = sampled_full_size(sv, dev, M, d_in, d_out, 31 * M + d_in, torch.bfloat16)
-    check(y, ref, torch.bfloat16, f"sweep M={M} {d_in}->{d_out}")
-
-
-def test_batch_sweep_lm_head_m1280(sv, dev):
-    import torch
-    y, ref = sampled_full_size(sv, dev, 1280, 4096, 128256, 5, torch.float32)
-    check(y, ref, torch.float32, "sweep M=1280 lm-head")
+    step_dtype = torch.float32 if d_out == 128256 else torch.bfloat16
+    for od in (step_dtype, torch.bfloat16 if step_dtype == torch.float32 else torch.float32):
+        y, ref = sampled_full_size(sv, dev, M, d_in, d_out, 31 * M + d_in + d_out, od)
+        check(y, ref, od, f"sweep M={M} {d_in}->{d_out} {od}")
 
 
 @pytest.mark.parametrize("M,d_out", [(5, 6144), (5, 16400), (80, 6144), (320, 6144)])

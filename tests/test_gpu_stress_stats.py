@@ -33,7 +33,7 @@ import pytest
 
 import oracle
 import synth
-from oracle import speculative as spec
+from parity import compare_rounds
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -57,18 +57,6 @@ def calibrate(tl, z, alpha):
         lo = torch.where(above, mid, lo)
         hi = torch.where(above, hi, mid)
     return (0.5 * (lo + hi)).float()
-
-
-def compare_exact(out, n, ref, what):
-    band = spec.TIE_BAND
-    steps = np.arange(ref["accept"].shape[1])[None, :]
-    n_tie = ref["n_tie"] | np.any(
-        (ref["accept_margin"] <= band) &
-        (steps <= np.minimum(ref["n_accepted"], ref["accept"].shape[1] - 1)[:, None]), axis=1)
-    tok_tie = n_tie | ref["token_tie"] | (ref["sample_margin"] <= band)
-    assert np.array_equal(n[~n_tie], ref["n_emitted"][~n_tie]), what
-    assert np.array_equal(out[~tok_tie], ref["out_tokens"][~tok_tie]), what
-    return int(tok_tie.sum())
 
 
 @pytest.mark.parametrize("alpha", [0.6, 0.81, 0.9])
@@ -123,8 +111,8 @@ def test_stress_statistics(sv, dev, alpha):
             ref = oracle.verify_batch(tl[s].cpu().numpy(), dl[s].cpu().numpy(),
                                       tok[s].cpu().numpy(), u_acc[s].cpu().numpy(),
                                       u_smp[s].cpu().numpy())
-            n_ties += compare_exact(out[s].cpu().numpy(), n[s].cpu().numpy(), ref,
-                                    f"alpha={alpha} round {r}")
+            n_ties += compare_rounds(out[s].cpu().numpy(), n[s].cpu().numpy(), ref,
+                                     f"alpha={alpha} round {r}", u_smp[s].cpu().numpy())[1]
     cnt = ROUNDS * B
     mean = float(tot) / cnt
     var = float(tot2) / cnt - mean * mean
@@ -143,7 +131,7 @@ def test_stress_statistics(sv, dev, alpha):
     print(f"alpha={alpha}: tokens/round {mean:.5f} expected {expect:.5f} "
           f"(closed form {closed:.5f}) se {se:.5f}; {m} emitted tokens: KS {ks:.2e} "
           f"(crit {ks_crit:.2e}) chi2 {chi2:.1f} (crit {chi2_crit:.1f}); "
-          f"oracle ties {n_ties}", flush=True)
+          f"oracle prefix ties {n_ties}", flush=True)
     assert abs(expect - closed) < 1e-3
     assert abs(mean - expect) < 4 * se
     assert ks < ks_crit

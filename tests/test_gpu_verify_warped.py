@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import synth
-from oracle import speculative as spec
+from parity import compare_rounds
 
 pytestmark = pytest.mark.gpu
 
@@ -40,18 +40,8 @@ def run(sv, dev, tl, dl, tok, ua, us, t_target, t_draft):
     return out.cpu().numpy(), n.cpu().numpy()
 
 
-def compare(out, n, ref, what, band=spec.TIE_BAND):
-    K = ref["accept"].shape[1]
-    n_tie = ref["n_tie"] | np.any(
-        (ref["accept_margin"] <= band) &
-        (np.arange(K)[None, :] <= np.minimum(ref["n_accepted"], K - 1)[:, None]), axis=1)
-    tok_tie = n_tie | ref["token_tie"] | (ref["sample_margin"] <= band)
-    assert np.array_equal(n[~n_tie], ref["n_emitted"][~n_tie]), what
-    assert np.array_equal(out[~tok_tie], ref["out_tokens"][~tok_tie]), what
-    for b in range(len(n)):
-        assert (out[b, n[b]:] == -1).all() and (out[b, :n[b]] >= 0).all(), what
-    print(f"{what}: {len(n)} seqs, {int(tok_tie.sum())} ties, mean emitted {n.mean():.3f}",
-          flush=True)
+def compare(out, n, ref, what, u_sample):
+    compare_rounds(out, n, ref, what, u_sample)
 
 
 def inputs(seed, B, K, V, std, sigma, t_draft):
@@ -68,7 +58,7 @@ def test_warped_tiny(sv, dev, t_target, t_draft):
                  d["u_accept"], d["u_sample"], t_target, t_draft)
     ref = oracle.verify_batch(d["target_logits"], d["draft_logits"], d["draft_tokens"],
                               d["u_accept"], d["u_sample"], t_target=t_target, t_draft=t_draft)
-    compare(out, n, ref, f"tiny T=({t_target}, {t_draft})")
+    compare(out, n, ref, f"tiny T=({t_target}, {t_draft})", d["u_sample"])
 
 
 @pytest.mark.parametrize("t", [0.7, 1.5])
@@ -80,7 +70,7 @@ def test_warped_llama8b_sampling_shape(sv, dev, t):
                  d["u_accept"], d["u_sample"], t, t)
     ref = oracle.verify_batch(d["target_logits"], d["draft_logits"], d["draft_tokens"],
                               d["u_accept"], d["u_sample"], t_target=t, t_draft=t)
-    compare(out, n, ref, f"8B T={t}")
+    compare(out, n, ref, f"8B T={t}", d["u_sample"])
 
 
 @pytest.mark.parametrize("V,t_draft", [(1000, 1.0), (128256, 1.0), (4097, 0.0), (128256, 0.8)])
@@ -131,7 +121,7 @@ def test_greedy_draft(sv, dev, t_target):
                  d["u_accept"], d["u_sample"], t_target, 0.0)
     ref = oracle.verify_batch(d["target_logits"], d["draft_logits"], d["draft_tokens"],
                               d["u_accept"], d["u_sample"], t_target=t_target, t_draft=0.0)
-    compare(out, n, ref, f"greedy draft T_target={t_target}")
+    compare(out, n, ref, f"greedy draft T_target={t_target}", d["u_sample"])
     # a rejected slot never re-emits the rejected draft token
     for b in range(len(n)):
         j = n[b] - 1
