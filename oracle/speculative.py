@@ -283,20 +283,30 @@ def total_variation(p, q):
 
 
 def emitted_law(p, q):
-    """Exact law of the token emitted at one position, and alpha.
+    """Exact law of the token emitted at one position, and the acceptance
+    probability, from the two events of the rule.
 
-    Accepted mass min(p, q) plus the rejected mass (1 - alpha) spread by the
-    normalised residual ("The Algebra and the Proof", The proof). The result
-    equals p; the residual is left as zeros when it has no mass.
+    A proposal x comes from q and is kept with probability
+    a(x) = min(1, p(x)/q(x)); a token with q(x) = 0 is never proposed. So x
+    is emitted by acceptance with probability q(x) a(x). Otherwise -- with
+    probability sum_x q(x) (1 - a(x)) -- the token comes from the normalised
+    residual (p - q)_+ ("The Algebra and the Proof", The proof; "Two Models,
+    One Voice", The rule that makes it exact). The law is the sum of the two
+    parts; the second is zero when the residual has no mass (then nothing is
+    ever rejected). Returns (law, alpha) with alpha = sum_x q(x) a(x).
     """
     p = np.asarray(p, np.float64)
     q = np.asarray(q, np.float64)
-    acc = np.minimum(p, q)
-    alpha = float(acc.sum())
-    res = np.maximum(p - q, 0.0)
-    if res.sum() > 0:
-        res = res / res.sum()
-    return acc + (1.0 - alpha) * res, alpha
+    keep = np.zeros_like(q)
+    proposed = q > 0.0
+    keep[proposed] = np.minimum(1.0, p[proposed] / q[proposed])
+    by_acceptance = q * keep
+    alpha = float(by_acceptance.sum())
+    rejected = float((q * (1.0 - keep)).sum())
+    resid = np.maximum(p - q, 0.0)
+    mass = float(resid.sum())
+    by_resample = rejected * resid / mass if mass > 0.0 else np.zeros_like(p)
+    return by_acceptance + by_resample, alpha
 
 
 def expected_tokens(alpha, K):
