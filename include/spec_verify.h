@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 5
+#define SPEC_ABI_VERSION 6
 
 /* Status codes. */
 #define SPEC_OK 0
@@ -401,6 +401,29 @@ int spec_verify_warped(const uint16_t* hidden, const uint16_t* lm_head, int d,
                        const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
                        int B, int K, int V, float t_target, float t_draft, int32_t* out_tokens,
                        int32_t* n_emitted, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_noalloc -- spec_verify for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same arguments without the workspace, whose
+ * role a static scratch array of the library takes. The call allocates
+ * nothing and computes exactly what spec_verify computes.
+ *
+ * The scratch is a 4 MiB device array inside the library, one copy per GPU,
+ * held until the process ends; its address is looked up once per device on
+ * the first call made with that device current. Shapes whose
+ * spec_verify_workspace_bytes(B, K, V) exceeds 4 MiB are rejected with
+ * SPEC_ERR_WORKSPACE before anything is launched (at V = 128256 that is
+ * about B > 440 at K = 8, B > 790 at K = 4). Every call on one GPU uses that
+ * GPU's copy: calls that can overlap on one GPU (different streams, or
+ * different host threads without ordering) race and must be serialized by
+ * the caller. Nothing needs clearing between calls.
+ */
+int spec_verify_noalloc(const uint16_t* hidden, const uint16_t* lm_head, int d,
+                        float* target_logits, const float* draft_logits,
+                        const int32_t* draft_tokens, const float* u_accept,
+                        const float* u_sample, int B, int K, int V, int32_t* out_tokens,
+                        int32_t* n_emitted, void* stream);
 
 #ifdef __cplusplus
 }

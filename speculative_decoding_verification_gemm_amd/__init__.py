@@ -65,6 +65,7 @@ SIGNATURES = {
     "spec_verify": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _z, _p]),
     "spec_verify_warped": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _f, _f, _p, _p, _p,
                                 _z, _p]),
+    "spec_verify_noalloc": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p]),
 }
 for _name, (_res, _args) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -323,6 +324,36 @@ def verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
                                      _ptr(u_sample), B, K, V, float(t_target), float(t_draft),
                                      _ptr(out_tokens), _ptr(n_emitted), _ptr(workspace),
                                      workspace.numel(), _stream()))
+    return out_tokens, n_emitted
+
+
+def verify_noalloc(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
+                   out_tokens, n_emitted, hidden=None, lm_head=None):
+    """spec_verify_noalloc: verify() without a workspace (the library's
+    static scratch serves instead). The outputs are caller-provided, so this
+    call allocates nothing on the device."""
+    torch = _torch()
+    _need(target_logits, torch.float32, "target_logits", 3)
+    _need(draft_logits, torch.float32, "draft_logits", 3)
+    _need(draft_tokens, torch.int32, "draft_tokens", 2)
+    _need(u_accept, torch.float32, "u_accept", 2)
+    _need(u_sample, torch.float32, "u_sample", 2)
+    _need(out_tokens, torch.int32, "out_tokens", 2)
+    _need(n_emitted, torch.int32, "n_emitted", 1)
+    B, K1, V = target_logits.shape
+    d = 0
+    if lm_head is not None:
+        _need(lm_head, torch.bfloat16, "lm_head", 2)
+        _need(hidden, torch.bfloat16, "hidden", 2)
+        d = lm_head.shape[1]
+        if tuple(lm_head.shape) != (V, d) or tuple(hidden.shape) != (B * K1, d):
+            raise ValueError("hidden / lm_head shapes disagree with the logits")
+    if tuple(out_tokens.shape) != (B, K1) or tuple(n_emitted.shape) != (B,):
+        raise ValueError("out_tokens / n_emitted shapes disagree with the logits")
+    check(lib.spec_verify_noalloc(_ptr(hidden), _ptr(lm_head), d, _ptr(target_logits),
+                                  _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
+                                  _ptr(u_sample), B, K1 - 1, V, _ptr(out_tokens), _ptr(n_emitted),
+                                  _stream()))
     return out_tokens, n_emitted
 
 

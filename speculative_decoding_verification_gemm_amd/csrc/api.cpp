@@ -537,6 +537,47 @@ int spec_residual_sample(const float* p_probs, const float* q_probs, const int32
                   "spec_residual_sample");
 }
 
+}  // extern "C"
+
+namespace {
+
+// The scratch of spec_verify_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends. Kernels receive the address that
+// hipGetSymbolAddress returns on the current device (the array's name is
+// only a host-side stand-in in host code); it is looked up once per device
+// and kept. Every spec_verify_noalloc call on a GPU uses that GPU's copy, so
+// calls that overlap on one GPU race. The sampler writes every scratch word
+// it reads within the same call, so nothing needs clearing between calls.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SPEC_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SPEC_ERR_UNSUPPORTED, "device index %d", dev);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SPEC_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch[dev].store(p, std::memory_order_release);  // same value if two threads race here
+  }
+  *out = p;
+  return SPEC_OK;
+}
+
+int verify_impl(const uint16_t* hidden, const uint16_t* lm_head, int d, float* target_logits,
+                const float* draft_logits, const int32_t* draft_tokens, const float* u_accept,
+                const float* u_sample, int B, int K, int V, float t_target, float t_draft,
+                int32_t* out_tokens, int32_t* n_emitted, void* workspace, size_t workspace_bytes,
+                bool use_scratch, void* stream);
+
+}  // namespace
+
+extern "C" {
+
 size_t spec_verify_workspace_bytes(int B, int K, int V) {
   if (B < 1 || B > kMaxB || K < 1 || K > kMaxK || V < 1 || V > kMaxV) return 0;
   return specv::verify_workspace_bytes(B, K, V);
@@ -557,12 +598,39 @@ int spec_verify_warped(const uint16_t* hidden, const uint16_t* lm_head, int d,
                        int B, int K, int V, float t_target, float t_draft, int32_t* out_tokens,
                        int32_t* n_emitted, void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
+  return verify_impl(hidden, lm_head, d, target_logits, draft_logits, draft_tokens, u_accept,
+                     u_sample, B, K, V, t_target, t_draft, out_tokens, n_emitted, workspace,
+                     workspace_bytes, false, stream);
+}
+
+int spec_verify_noalloc(const uint16_t* hidden, const uint16_t* lm_head, int d,
+                        float* target_logits, const float* draft_logits,
+                        const int32_t* draft_tokens, const float* u_accept,
+                        const float* u_sample, int B, int K, int V, int32_t* out_tokens,
+                        int32_t* n_emitted, void* stream) {
+  clear_error();
+  return verify_impl(hidden, lm_head, d, target_logits, draft_logits, draft_tokens, u_accept,
+                     u_sample, B, K, V, 1.0f, 1.0f, out_tokens, n_emitted, nullptr, 0, true,
+                     stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// spec_verify_warped, and spec_verify_noalloc (use_scratch: the library's
+// static scratch array stands in for the workspace).
+int verify_impl(const uint16_t* hidden, const uint16_t* lm_head, int d, float* target_logits,
+                const float* draft_logits, const int32_t* draft_tokens, const float* u_accept,
+                const float* u_sample, int B, int K, int V, float t_target, float t_draft,
+                int32_t* out_tokens, int32_t* n_emitted, void* workspace, size_t workspace_bytes,
+                bool use_scratch, void* stream) {
   if (!(t_target >= 0.0f) || !(t_draft >= 0.0f) || !std::isfinite(t_target) ||
       !std::isfinite(t_draft))
     return fail(SPEC_ERR_INVALID_ARGUMENT, "temperatures must be finite and >= 0 (got %g, %g)",
                 (double)t_target, (double)t_draft);
   if (!target_logits || !draft_logits || !draft_tokens || !u_accept || !u_sample || !out_tokens ||
-      !n_emitted || !workspace)
+      !n_emitted || (!workspace && !use_scratch))
     return fail(SPEC_ERR_INVALID_ARGUMENT, "null required pointer");
   if ((hidden == nullptr) != (lm_head == nullptr))
     return fail(SPEC_ERR_INVALID_ARGUMENT, "hidden and lm_head must be both given or both NULL");
@@ -582,11 +650,21 @@ int spec_verify_warped(const uint16_t* hidden, const uint16_t* lm_head, int d,
       !aligned(n_emitted, 4))
     return fail(SPEC_ERR_ALIGNMENT, "32-bit arrays must be 4-byte aligned");
   const size_t need = specv::verify_workspace_bytes(B, K, V);
-  if (workspace_bytes < need)
-    return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-  if (!aligned(workspace, 256)) return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (use_scratch) {
+    if (need > kScratchBytes)
+      return fail(SPEC_ERR_WORKSPACE,
+                  "(B, K, V) = (%d, %d, %d) needs %zu bytes of scratch; the library's static "
+                  "scratch holds %zu (use spec_verify with a workspace)",
+                  B, K, V, need, kScratchBytes);
+  } else {
+    if (workspace_bytes < need)
+      return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if (!aligned(workspace, 256))
+      return fail(SPEC_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  }
   int cus = 0;
   if ((rc = check_device(&cus)) != SPEC_OK) return rc;
+  if (use_scratch && (rc = scratch_address(&workspace)) != SPEC_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // With the streaming lm-head (where spec_verify_gemm would use it) the
   // target rows' softmax statistics are folded into the GEMM's epilogue, so
@@ -617,4 +695,4 @@ int spec_verify_warped(const uint16_t* hidden, const uint16_t* lm_head, int d,
                   "spec_verify sampling");
 }
 
-}  // extern "C"
+}  // namespace

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(sv.lib, n), n
 
@@ -33,7 +33,7 @@ def test_binding_covers_exactly_the_header(sv):
 
 
 def test_version_and_status_strings(sv):
-    assert sv.abi_version() == 5
+    assert sv.abi_version() == 6
     for code, name in [(0, b"SPEC_OK"), (-1, b"SPEC_ERR_INVALID_ARGUMENT"),
                        (-2, b"SPEC_ERR_ALIGNMENT"), (-3, b"SPEC_ERR_UNSUPPORTED"),
                        (-4, b"SPEC_ERR_WORKSPACE"), (-5, b"SPEC_ERR_HIP")]:
@@ -118,6 +118,22 @@ def test_verify_rejects(sv):
     assert _verify(sv, B=1 << 20, K=64, V=1 << 20) == -1     # grid bound
     assert _verify(sv, wsb=100) == -4
     assert _verify(sv, ws=A + 16) == -4
+
+
+def test_verify_noalloc_rejects(sv):
+    f = sv.lib.spec_verify_noalloc
+
+    def call(B=1, K=4, V=1000, tl=A, hidden=None, lm=None, d=0, out=A):
+        return f(hidden, lm, d, tl, A, A, A, A, B, K, V, out, A, None)
+    assert call(tl=None) == -1
+    assert call(out=None) == -1
+    assert call(hidden=A) == -1
+    assert call(K=65) == -1
+    assert call(tl=MIS) == -2
+    # beyond the 4 MiB static scratch: rejected on the host, with the sizes
+    assert sv.lib.spec_verify_workspace_bytes(512, 8, 128256) > 4 << 20
+    assert call(B=512, K=8, V=128256) == -4
+    assert b"scratch" in sv.lib.spec_last_error()
 
 
 def test_verify_warped_rejects(sv):
