@@ -13,8 +13,8 @@ synthetic Llama-shaped inputs already resident in HBM:
 Each phase is captured once in a HIP graph; a timed step replays the two
 graphs back to back with HIP events between them on the same stream.
 With --w8 every linear (stack and lm-head) holds FP8 E4M3 weights with a
-per-row scale (weight-only 8-bit storage, bf16 activations and products);
-M <= 16 only. Prints one JSON line: the throughput in verified positions per second, the
+per-row scale (weight-only 8-bit storage, bf16 activations and products):
+one chain launch up to M = 16, per-linear MFMA tile launches above. Prints one JSON line: the throughput in verified positions per second, the
 per-phase times, the roofline of the GEMM phase (algorithmic bytes over its
 measured time, against the 8 TB/s HBM peak; MFMA peak where the FLOPs
 dominate) and the fp64 oracle's rate on the host cores.
@@ -23,11 +23,20 @@ dominate) and the fp64 oracle's rate on the host cores.
                     [--batch B] [--no-graph] [--no-chain] [--no-cpu-baseline] [--w8]
     python bench.py --attention [--batch B] [--context C]
                                          # the verify attention alone
+    python bench.py --stress [--rounds R]  # the sampling-stress workload
+    python bench.py --sweep [--w8]       # the batch sweep B = 1, 4, 16, 64, 256:
+                                         # both roofline fractions per B and the
+                                         # measured memory-to-compute crossover
+    python bench.py --linear 4096x6144 --batch B
+                                         # one linear per launch (for profiles)
+    python bench.py --probe              # the achievable ceilings: HBM read
+                                         # bandwidth and dense bf16 MFMA rate
     python bench.py --copy-calibration   # plain device copy of known size,
                                          # the scale for HBM traffic counters
 """
 
 import argparse
+import contextlib
 import hashlib
 import json
 import os
@@ -61,7 +70,7 @@ def parse():
     ap.add_argument("--context", type=int, default=4096,
                     help="cached tokens before the verify positions (--attention)")
     ap.add_argument("--w8", action="store_true",
-                    help="FP8 E4M3 weights with per-row scales for every linear (M <= 16)")
+                    help="FP8 E4M3 weights with per-row scales for every linear")
     ap.add_argument("--lm-head", choices=["chain", "fused"], default="chain",
                     help="chain: the lm-head is the last linear of the chain launch and "
                          "spec_verify reads its logits; fused: the chain holds the stack only "
@@ -79,6 +88,14 @@ def parse():
                          "--rounds verification rounds per alpha")
     ap.add_argument("--rounds", type=int, default=100000,
                     help="rounds per alpha for --stress")
+    ap.add_argument("--sweep", action="store_true",
+                    help="batch sweep on the workload's shapes: B in --sweep-batches")
+    ap.add_argument("--sweep-batches", default="1,4,16,64,256")
+    ap.add_argument("--linear", default=None,
+                    help="DINxDOUT: time spec_verify_gemm (or _w8) on one linear at M = 5 B, "
+                         "rotating over weight copies that together exceed the 256 MB cache")
+    ap.add_argument("--probe", action="store_true",
+                    help="measure the achievable HBM read bandwidth and dense bf16 MFMA rate")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (the known-size "
                          "reference that scales FETCH_SIZE / WRITE_SIZE counters)")
@@ -229,6 +246,84 @@ class Workload:
         if getattr(self, "chain", None) is not None:
             return 1
         return len(self.linears) + (0 if self.fused_lm_head else 1)
+
+
+def time_steps(wl, sv, n, warmup, graph=True):
+    """Times n steps (GEMM phase, then sampling phase) with HIP events on the
+    stream both phases run on, after `warmup` untimed ones. With graph=True
+    each phase is captured once and replayed. Returns sorted per-step
+    (gemm ms, sampling ms, step ms) and the wall time of the timed loop."""
+    import torch
+    # eager pass (also initialises the library's per-device state)
+    wl.gemm_phase(sv)
+    wl.sampling_phase(sv)
+    torch.cuda.synchronize()
+    if not graph:
+        run_gemm = lambda: wl.gemm_phase(sv)  # noqa: E731
+        run_samp = lambda: wl.sampling_phase(sv)  # noqa: E731
+    else:
+        g_gemm, g_samp = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_gemm):
+            wl.gemm_phase(sv)
+        with torch.cuda.graph(g_samp):
+            wl.sampling_phase(sv)
+        torch.cuda.synchronize()
+        run_gemm, run_samp = g_gemm.replay, g_samp.replay
+    for _ in range(warmup):
+        run_gemm()
+        run_samp()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    t0 = time.perf_counter()
+    for i in range(n):
+        ev[i][0].record()
+        run_gemm()
+        ev[i][1].record()
+        run_samp()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_gemm = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    t_samp = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    t_step = sorted(e[0].elapsed_time(e[2]) for e in ev)
+    return t_gemm, t_samp, t_step, wall
+
+
+def measure_ceilings(sv, dev, read_bytes=4 << 30, reps=5, mfma_iters=2048):
+    """The achievable ceilings beside the published peaks (the library's
+    probe kernels): HBM read bandwidth streaming a buffer larger than the
+    256 MB Infinity Cache, and the dense bf16 MFMA rate of independent
+    16x16x32 and 32x32x16 chains. Each is the mean over `reps` launches."""
+    import torch
+    buf = torch.ones(read_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # bytes in flight per CU = 8 KB x loads per lane x workgroups per CU
+    shapes = {}
+    for wgs in (1, 2):
+        for loads in (1, 2, 4, 8):
+            sv.probe_read(buf, sink, loads, wgs)
+            e0.record()
+            for _ in range(reps):
+                sv.probe_read(buf, sink, loads, wgs)
+            e1.record()
+            torch.cuda.synchronize()
+            shapes[f"{8 * loads * wgs}KB_per_CU({wgs}wg,{loads}ld)"] = \
+                read_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    best = max(shapes, key=shapes.get)
+    out = {"read_gbs": shapes[best], "read_best_shape": best, "read_gbs_by_shape": shapes,
+           "read_bytes": read_bytes}
+    del buf
+    for shape in (16, 32):
+        flops = sv.probe_mfma(shape, mfma_iters, sink)
+        e0.record()
+        for _ in range(reps):
+            sv.probe_mfma(shape, mfma_iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"mfma_bf16_tflops_{shape}x{shape}"] = flops * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    out["mfma_bf16_tflops"] = max(out["mfma_bf16_tflops_16x16"], out["mfma_bf16_tflops_32x32"])
+    return out
 
 
 def cpu_baseline(wl, sample_layers=None):
@@ -384,6 +479,8 @@ def stress_bench(args):
     # residual or bonus draw re-reads
     call_bytes = 4 * V * B * (2 * K + 1) + 2 * 4 * V * B
     results, ms_total, rounds_total = [], 0.0, 0
+    n_check = 0 if args.no_cpu_baseline else 8  # rounds per alpha given to the oracle leg
+    checks = []
     for alpha in (0.6, 0.81, 0.9):
         lo = torch.zeros((B, K), dtype=torch.float64, device=dev)
         hi = torch.full((B, K), 8.0, dtype=torch.float64, device=dev)
@@ -415,6 +512,9 @@ def stress_bench(args):
             sv.verify(tl, dl, tok, u_acc, u_smp, workspace=ws, out_tokens=out, n_emitted=n)
             e1.record()
             ev.append((e0, e1))
+            if r < n_check:
+                checks.append((alpha, dl, tok.cpu().numpy(), u_acc.cpu().numpy(),
+                               u_smp.cpu().numpy(), out.cpu().numpy(), n.cpu().numpy()))
             nd = n.double()
             tot += nd.sum()
             tot2 += (nd * nd).sum()
@@ -436,9 +536,10 @@ def stress_bench(args):
                         "closed_form": (1 - alpha ** (K + 1)) / (1 - alpha), "se": se,
                         "z": (mean - expect) / se if se > 0 else 0.0,
                         "max_row_alpha_error": float((a - alpha).abs().max())})
-        del dl, cq
+        del cq
     ms = ms_total / rounds_total
     gbs = call_bytes / (ms * 1e-3) / 1e9
+    base = stress_cpu_baseline(tl, checks) if checks else None
     print(json.dumps({
         "metric": "sampling-stress verification rounds/s (B=64, K=8, V=128256)",
         "value": 1e3 / ms, "unit": "rounds/s", "n_gpus": 1, "steps": rounds_total, "warmup": 0,
@@ -451,7 +552,192 @@ def stress_bench(args):
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes_per_call": call_bytes},
-        "alphas": results}), flush=True)
+        "alphas": results, "cpu_baseline": base}), flush=True)
+
+
+def stress_cpu_baseline(tl, checks):
+    """The fp64 oracle on a bounded sample of the stress run: the first
+    rounds of each alpha, on the same logits, drafts and uniforms, timed on
+    the host. As a by-product the oracle's decisions are compared with what
+    the GPU emitted in those rounds (tests/parity.py: bit-exact outside the
+    1e-5 tie band, inside it within the band's tokens) and the ties are
+    counted."""
+    import numpy as np
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import compare_rounds
+    tl_h = tl.cpu().numpy()
+    dl_h = {}
+    t_total, seqs, prefix_ties, band_draws = 0.0, 0, 0, 0
+    per_alpha = {}
+    for alpha, dl, tok, ua, us, out, n in checks:
+        if alpha not in dl_h:
+            dl_h[alpha] = dl.cpu().numpy()
+        t0 = time.perf_counter()
+        ref = oracle.verify_batch(tl_h, dl_h[alpha], tok, ua, us)
+        t_total += time.perf_counter() - t0
+        with contextlib.redirect_stdout(sys.stderr):  # keep stdout to the one JSON line
+            b, nt, nb = compare_rounds(out, n, ref, f"stress alpha={alpha}", us)
+        seqs, prefix_ties, band_draws = seqs + b, prefix_ties + nt, band_draws + nb
+        pa = per_alpha.setdefault(str(alpha), {"rounds": 0, "prefix_ties": 0,
+                                               "draws_within_band": 0})
+        pa["rounds"] += 1
+        pa["prefix_ties"] += nt
+        pa["draws_within_band"] += nb
+    rounds = len(checks)
+    return {"value": rounds / t_total, "unit": "rounds/s", "cores": 1, "kind": "oracle",
+            "sample": (f"the first {rounds // max(1, len(dl_h))} rounds of each alpha "
+                       f"({rounds} rounds, {seqs} sequences, {t_total:.1f} s): "
+                       "oracle.verify_batch on the same fp32 logits, drafts and uniforms "
+                       "(fp64 numpy, single-threaded elementwise work)"),
+           "agreement": {"sequences": seqs, "prefix_ties": prefix_ties,
+                         "tokens_exact": seqs - prefix_ties - band_draws,
+                         "tokens_within_band": band_draws, "mismatches": 0,
+                         "per_alpha": per_alpha}}
+
+
+def sweep_bench(args):
+    """The batch sweep on the workload's shapes at K = 4: for each B the
+    whole step (GEMM phase, then sampling) as the default line times it
+    (the chain where it runs, per-linear launches above), the GEMM phase's
+    fraction of the HBM peak (algorithmic bytes / time) and of the dense
+    MFMA peak (FLOPs / time), and the memory-to-compute crossover.
+
+    The crossover is measured as where the two regimes of the measured GEMM
+    time meet: a flat part t0 (the weight read, the smallest B) and a part
+    that grows with the work, slope c per sequence (from the two largest B);
+    B* = t0 / c. The roofline's own crossover is where the intensity
+    B (K+1) FLOP per weight byte (2 B (K+1) with FP8 weights) reaches the
+    ridge, peak FLOP/s / peak bytes/s ("Speculative Decoding: The Algebra
+    and the Proof", Where it breaks; "Guess Several Tokens", Wasted work,
+    and why batching changes the answer)."""
+    import torch
+    import synth
+    import speculative_decoding_verification_gemm_amd as sv
+
+    dev = torch.device("cuda:0")
+    stack = {"llama8b": synth.LLAMA_8B, "llama70b": synth.LLAMA_70B_16L}[args.workload]
+    key = {"llama8b": "llama8b_lm_head", "llama70b": "llama70b_lm_head"}[args.workload]
+    K = K_DRAFT
+    rows = []
+    for B in [int(b) for b in args.sweep_batches.split(",")]:
+        wl = Workload(stack, B, K, args.seed, dev, w8=args.w8)
+        wl.make_drafts(sv, synth.draft_noise_sigma(key, 0.8), args.seed)
+        use_chain = wl.M <= (16 if args.w8 else 8)
+        if use_chain:
+            wl.make_chain(sv)
+        steps = max(5, min(args.steps, int(200 / B)))
+        t_gemm, t_samp, t_step, _ = time_steps(wl, sv, steps, max(2, args.warmup // 4))
+        ms_gemm, ms_samp = sum(t_gemm) / steps, sum(t_samp) / steps
+        by, fl = wl.gemm_bytes(), wl.gemm_flops()
+        rows.append({"B": B, "M": wl.M, "steps": steps,
+                     "gemm_launch": "chain" if use_chain else "per-linear",
+                     "ms_gemm_phase": ms_gemm, "ms_sampling_phase": ms_samp,
+                     "positions_per_s": wl.M / ((ms_gemm + ms_samp) * 1e-3),
+                     "gemm_bytes": by, "gemm_flops": fl,
+                     "hbm_frac": by / (ms_gemm * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                     "mfma_frac": fl / (ms_gemm * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+                     "floor_ms": 1e3 * max(by / (HBM_PEAK_GBS * 1e9),
+                                           fl / (MFMA_BF16_PEAK_TFLOPS * 1e12))})
+        rows[-1]["frac_of_floor"] = rows[-1]["floor_ms"] / ms_gemm
+        if use_chain and wl.chain.error():
+            print("chain reported a device error", file=sys.stderr)
+            sys.exit(3)
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        del wl
+        torch.cuda.empty_cache()
+    ceil = measure_ceilings(sv, dev)
+    t0 = rows[0]["ms_gemm_phase"]
+    big = sorted(rows, key=lambda r: r["B"])[-2:]
+    slope = ((big[1]["ms_gemm_phase"] - big[0]["ms_gemm_phase"]) / (big[1]["B"] - big[0]["B"])
+             if len(big) == 2 and big[1]["B"] != big[0]["B"] else None)
+    bytes_per_weight = 1 if args.w8 else 2
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    print(json.dumps({
+        "metric": f"batch sweep of the verify step ({stack.name} shapes, K={K})",
+        "value": None if not slope else t0 / slope,
+        "unit": "sequences (measured memory-to-compute crossover B*)",
+        "n_gpus": 1, "higher_is_better": None, "vs_baseline": None,
+        "dtype": "bf16 (fp8 e4m3 weights)" if args.w8 else "bf16", "data": "synthetic",
+        "config": {"workload": f"{stack.name} verify step at B in {args.sweep_batches}",
+                   "draft_tokens_K": K, "weights": "fp8_e4m3" if args.w8 else "bf16"},
+        "crossover": {"measured_B": None if not slope else t0 / slope,
+                      "flat_ms": t0, "slope_ms_per_sequence": slope,
+                      "roofline_B": ridge * bytes_per_weight / (2 * (K + 1)),
+                      "ridge_flop_per_byte": ridge},
+        "ceilings": ceil, "rows": rows}), flush=True)
+
+
+def linear_bench(args):
+    """spec_verify_gemm (spec_verify_gemm_w8 with --w8) on one linear, one
+    launch per step, rotating over weight copies that together exceed the
+    256 MB Infinity Cache (so every launch reads its weights from HBM).
+    Output bf16, or fp32 for a linear as wide as the vocabulary."""
+    import torch
+    import synth
+    import speculative_decoding_verification_gemm_amd as sv
+    from synth import device as sd
+
+    dev = torch.device("cuda:0")
+    d_in, d_out = (int(v) for v in args.linear.lower().split("x"))
+    M = args.batch * (K_DRAFT + 1)
+    esz = 1 if args.w8 else 2
+    copies = max(1, min(8, -(-(768 << 20) // (d_in * d_out * esz))))
+    ws, scs = [], []
+    for c in range(copies):
+        if args.w8:
+            ws.append(sd.e4m3_normal_codes((d_out, d_in), synth.W8_CODE_STD, args.seed + c, dev))
+            scs.append(sd.w8_row_scales(d_out, synth.WEIGHT_STD / synth.W8_CODE_STD,
+                                        args.seed + 100 + c, dev))
+        else:
+            ws.append(sd.normal_bf16((d_out, d_in), synth.WEIGHT_STD, args.seed + c, dev))
+    x = sd.normal_bf16((M, d_in), 1.0, args.seed + 999, dev)
+    od = torch.float32 if d_out >= 100000 else torch.bfloat16
+    y = torch.empty((M, d_out), dtype=od, device=dev)
+
+    def call(i):
+        if args.w8:
+            sv.verify_gemm_w8(x, ws[i % copies], scs[i % copies], out=y)
+        else:
+            sv.verify_gemm(x, ws[i % copies], out=y)
+    for i in range(max(args.warmup, copies)):
+        call(i)
+    torch.cuda.synchronize()
+    n = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    by = d_in * d_out * esz + 2 * M * d_in + y.element_size() * M * d_out + \
+        (4 * d_out if args.w8 else 0)
+    fl = 2 * M * d_in * d_out
+    print(json.dumps({
+        "metric": f"one verify linear {d_in}->{d_out} at M={M}", "value": ms * 1e3,
+        "unit": "us per launch", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "higher_is_better": False, "vs_baseline": None,
+        "dtype": "bf16 (fp8 e4m3 weights)" if args.w8 else "bf16", "data": "synthetic",
+        "config": {"workload": f"linear {d_in}->{d_out}, M={M}, {copies} weight copies"},
+        "gbs": by / (ms * 1e-3) / 1e9, "tflops": fl / (ms * 1e-3) / 1e12,
+        "hbm_frac": by / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "mfma_frac": fl / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)}), flush=True)
+
+
+def probe_bench(args):
+    import torch
+    import speculative_decoding_verification_gemm_amd as sv
+    ceil = measure_ceilings(sv, torch.device("cuda:0"), reps=max(5, min(args.steps, 50)))
+    print(json.dumps({
+        "metric": "achievable ceilings: HBM read bandwidth and dense bf16 MFMA rate",
+        "value": ceil["read_gbs"], "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "probe kernels: read-only stream over 4 GiB; independent MFMA "
+                               "chains (16x16x32 and 32x32x16 bf16)"},
+        "read_frac_of_peak": ceil["read_gbs"] / HBM_PEAK_GBS,
+        "mfma_frac_of_peak": ceil["mfma_bf16_tflops"] / MFMA_BF16_PEAK_TFLOPS,
+        "ceilings": ceil}), flush=True)
 
 
 def copy_calibration(reps=5):
@@ -490,6 +776,15 @@ def main():
     if args.stress:
         stress_bench(args)
         return
+    if args.sweep:
+        sweep_bench(args)
+        return
+    if args.linear:
+        linear_bench(args)
+        return
+    if args.probe:
+        probe_bench(args)
+        return
     import torch
     import synth
     import speculative_decoding_verification_gemm_amd as sv
@@ -498,10 +793,6 @@ def main():
     stack = {"llama8b": synth.LLAMA_8B, "llama70b": synth.LLAMA_70B_16L}[args.workload]
     key = {"llama8b": "llama8b_lm_head", "llama70b": "llama70b_lm_head"}[args.workload]
     B, K = args.batch, K_DRAFT
-    if args.w8 and B * (K + 1) > 16:
-        print(f"--w8 covers M <= 16 (the weight-streaming kernel); B={B} gives M={B * (K + 1)}",
-              file=sys.stderr)
-        sys.exit(2)
     fused = args.lm_head == "fused"
     if fused and (args.w8 or B * (K + 1) > 8):
         print("--lm-head fused covers bf16 weights at M <= 8", file=sys.stderr)
@@ -518,49 +809,14 @@ def main():
     if use_chain:
         wl.make_chain(sv)
 
-    # eager pass (also initialises the library's per-device state)
-    wl.gemm_phase(sv)
-    wl.sampling_phase(sv)
-    torch.cuda.synchronize()
-
-    if args.no_graph:
-        run_gemm = lambda: wl.gemm_phase(sv)  # noqa: E731
-        run_samp = lambda: wl.sampling_phase(sv)  # noqa: E731
-    else:
-        g_gemm, g_samp = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_gemm):
-            wl.gemm_phase(sv)
-        with torch.cuda.graph(g_samp):
-            wl.sampling_phase(sv)
-        torch.cuda.synchronize()
-        run_gemm, run_samp = g_gemm.replay, g_samp.replay
-
-    for _ in range(args.warmup):
-        run_gemm()
-        run_samp()
-    torch.cuda.synchronize()
-
     n = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
-    emitted = torch.zeros(B, dtype=torch.int64, device=dev)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(n):
-        ev[i][0].record()
-        run_gemm()
-        ev[i][1].record()
-        run_samp()
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    t_gemm = sorted(e[0].elapsed_time(e[1]) for e in ev)
-    t_samp = sorted(e[1].elapsed_time(e[2]) for e in ev)
-    t_step = sorted(e[0].elapsed_time(e[2]) for e in ev)
-    emitted += wl.n_emitted.long()
+    t_gemm, t_samp, t_step, wall = time_steps(wl, sv, n, args.warmup, not args.no_graph)
+    emitted = wl.n_emitted.long()
     med = lambda a: a[len(a) // 2]  # noqa: E731
     ms_step = sum(t_step) / n
     ms_gemm = sum(t_gemm) / n
     ms_samp = sum(t_samp) / n
+    ceil = measure_ceilings(sv, dev)
 
     gemm_bytes = wl.gemm_bytes()
     gemm_flops = wl.gemm_flops()
@@ -573,10 +829,14 @@ def main():
     mfma_bound = gemm_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > gemm_bytes / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": gemm_flops / (ms_gemm * 1e-3) / 1e12,
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "achievable": ceil["mfma_bf16_tflops"]}
     else:
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "achievable": ceil["read_gbs"]}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    # the same achieved rate against what the probe kernels reach on this part
+    roof["frac_of_achievable"] = roof["achieved"] / roof["achievable"]
     # Expected tokens per round from each draft row's exact acceptance rate
     # alpha_j = sum_x min(p_j(x), q_j(x)): E[N] = 1 + sum_i prod_{j<=i} alpha_j.
     def warped(logits, t):
@@ -619,6 +879,9 @@ def main():
             "temperatures": {"target": args.t_target, "draft": args.t_draft},
         },
         "pct_hbm_peak_in_verify": 100.0 * achieved / HBM_PEAK_GBS,
+        "achievable_gbs": ceil["read_gbs"],
+        "pct_achievable_hbm_in_verify": 100.0 * achieved / ceil["read_gbs"],
+        "ceilings": ceil,
         "ms_gemm_phase": ms_gemm,
         "ms_sampling_phase": ms_samp,  # with --lm-head fused: lm-head + sampling
         "sampling_share": ms_samp / ms_step,

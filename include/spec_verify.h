@@ -181,8 +181,14 @@ int spec_verify_gemm_chain(int n, int M, void* workspace, void* stream);
  *   w_scale  device, float32 [d_out], 4-byte aligned.
  *   y        device, [M][d_out] of y_dtype.
  *   d_in     multiple of 16, in [16, 2^20]; d_out in [1, 2^24].
- *   M        1..16: the weight-streaming regime, where halving the bytes
- *            halves the time. M > 16 returns SPEC_ERR_UNSUPPORTED.
+ *   M        1..65536. Up to 16 positions a vector-ALU weight-streaming
+ *            kernel runs (the regime where halving the bytes halves the
+ *            time); above, the bf16 MFMA tile kernel with the codes widened
+ *            exactly to bf16 on their way to the matrix cores, which needs
+ *            d_in a multiple of 64 (else SPEC_ERR_UNSUPPORTED). There 8-bit
+ *            weights double the FLOPs per weight byte, which halves the
+ *            batch at which the pass stops being bound by the weight read
+ *            (same page).
  * Errors as spec_verify_gemm. Nothing is allocated; the call is
  * asynchronous on `stream`.
  */
@@ -205,7 +211,8 @@ typedef struct spec_linear_w8 {
  * spec_chain_prepare_w8 / spec_verify_gemm_chain_w8 -- spec_chain_prepare
  * and spec_verify_gemm_chain for a chain whose every linear has FP8 E4M3
  * weights (each checked as spec_verify_gemm_w8 checks its arguments). The
- * workspace is sized by spec_chain_workspace_bytes(n) as for a bf16 chain; a
+ * workspace is sized by spec_chain_workspace_bytes(n) as for a bf16 chain,
+ * and M is limited to 16 as for a bf16 chain; a
  * workspace prepared by one kind of prepare call run by the other kind of
  * chain call computes nothing and sets bit 1 of spec_chain_error.
  */
@@ -254,6 +261,36 @@ int spec_verify_attention(const uint16_t* q, const uint16_t* k_cache, const uint
  * a launch did not match the prepared plan.
  */
 int spec_chain_error(void* workspace, int* error);
+
+/*
+ * Measurement helpers: the achievable ceilings that the verify pass's
+ * roofline fractions are quoted beside (the pass is priced against the
+ * published 8 TB/s HBM and 2.5 PFLOP/s dense bf16 figures; "Speculative
+ * Decoding: Guess Several Tokens, Check Them in One Pass", Step 1, and
+ * "Speculative Decoding: The Algebra and the Proof", Where it breaks).
+ *
+ * spec_probe_read -- read `bytes` of device memory at `buf` once, front to
+ * back, with 16-byte non-temporal loads from one persistent grid of
+ * `wgs_per_cu` (1..4) workgroups of eight waves per compute unit, each lane
+ * keeping `loads_per_lane` (1, 2, 4 or 8) loads in flight: 8 KB x loads x
+ * workgroups in flight per compute unit. Nothing is written except,
+ * in practice never, one word of `sink` (a device word the caller owns;
+ * it keeps the loads from being optimised away). Time it with events on
+ * `stream`; bytes / time is the achievable read bandwidth when `bytes` is
+ * well above the 256 MB Infinity Cache (e.g. 4 GiB).
+ *   buf   device, 16-byte aligned; bytes a positive multiple of 16.
+ *
+ * spec_probe_mfma -- independent chains of bf16 MFMAs on register operands
+ * (no memory traffic): `iters` rounds per wave of eight independent
+ * v_mfma_f32_16x16x32_bf16 (shape 16) or four v_mfma_f32_32x32x16_bf16
+ * (shape 32), four waves per workgroup, two workgroups per compute unit. *flops
+ * (host) receives the launch's floating-point operations; flops / time is
+ * the achievable dense bf16 rate. sink as above.
+ * Both are asynchronous on `stream` and allocate nothing.
+ */
+int spec_probe_read(const void* buf, size_t bytes, int loads_per_lane, int wgs_per_cu,
+                    void* sink, void* stream);
+int spec_probe_mfma(int shape, int iters, void* sink, double* flops, void* stream);
 
 /*
  * spec_chain_reset -- set the barrier counters of a prepared chain workspace

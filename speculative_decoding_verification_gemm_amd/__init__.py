@@ -62,6 +62,8 @@ SIGNATURES = {
     "spec_verify_attention": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _z, _p]),
     "spec_chain_error": (_i, [_p, ctypes.POINTER(ctypes.c_int)]),
     "spec_chain_reset": (_i, [_p, ctypes.c_uint]),
+    "spec_probe_read": (_i, [_p, _z, _i, _i, _p, _p]),
+    "spec_probe_mfma": (_i, [_i, _i, _p, ctypes.POINTER(ctypes.c_double), _p]),
     "spec_verify": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _z, _p]),
     "spec_verify_warped": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _f, _f, _p, _p, _p,
                                 _z, _p]),
@@ -325,6 +327,20 @@ def verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
                                      _ptr(out_tokens), _ptr(n_emitted), _ptr(workspace),
                                      workspace.numel(), _stream()))
     return out_tokens, n_emitted
+
+
+def probe_read(buf, sink, loads_per_lane=4, wgs_per_cu=1):
+    """spec_probe_read over the whole of `buf` (a device tensor); `sink` is
+    a device tensor of at least 4 bytes."""
+    check(lib.spec_probe_read(_ptr(buf), buf.numel() * buf.element_size(), int(loads_per_lane),
+                              int(wgs_per_cu), _ptr(sink), _stream()))
+
+
+def probe_mfma(shape, iters, sink):
+    """spec_probe_mfma; returns the launch's floating-point operations."""
+    flops = ctypes.c_double(0.0)
+    check(lib.spec_probe_mfma(int(shape), int(iters), _ptr(sink), ctypes.byref(flops), _stream()))
+    return flops.value
 
 
 def verify_noalloc(target_logits, draft_logits, draft_tokens, u_accept, u_sample,

@@ -23,7 +23,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspecverify.so")
 DIAG_LIB = os.path.join(HERE, "libspecverify_diag.so")
-SOURCES = ["api.cpp", "gemm_stream.hip", "gemm_skinny.hip", "gemm_mfma.hip", "sampler.hip", "attention.hip"]
+SOURCES = ["api.cpp", "gemm_stream.hip", "gemm_skinny.hip", "gemm_mfma.hip", "sampler.hip",
+           "attention.hip", "probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

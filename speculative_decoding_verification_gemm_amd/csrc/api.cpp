@@ -112,8 +112,9 @@ int check_gemm_args(const uint16_t* x, const uint16_t* w, const void* y, int y_d
   return SPEC_OK;
 }
 
-// FP8 weights: as check_gemm_args, plus the scale vector, d_in a multiple of
-// 16 (one 16-byte load holds 16 weights) and M within the streaming kernel.
+// FP8 weights: as check_gemm_args, plus the scale vector and d_in a multiple
+// of 16 (one 16-byte load holds 16 weights); above the streaming kernel's
+// positions (M > 16) the tile kernel needs d_in a multiple of 64.
 int check_gemm_w8_args(const uint16_t* x, const uint8_t* w, const float* w_scale, const void* y,
                        int y_dtype, int M, int d_in, int d_out) {
   if (!w_scale) return fail(SPEC_ERR_INVALID_ARGUMENT, "null w_scale");
@@ -123,9 +124,10 @@ int check_gemm_w8_args(const uint16_t* x, const uint8_t* w, const float* w_scale
     return fail(SPEC_ERR_INVALID_ARGUMENT, "d_in=%d must be a multiple of 16 for FP8 weights",
                 d_in);
   if (!aligned(w_scale, 4)) return fail(SPEC_ERR_ALIGNMENT, "w_scale is not 4-byte aligned");
-  if (M > specv::kMaxStreamM)
-    return fail(SPEC_ERR_UNSUPPORTED, "FP8 weights are implemented for M <= %d (got %d)",
-                specv::kMaxStreamM, M);
+  if (M > specv::kMaxStreamM && d_in % 64 != 0)
+    return fail(SPEC_ERR_UNSUPPORTED,
+                "FP8 weights with M > %d need d_in a multiple of 64 (got M=%d, d_in=%d)",
+                specv::kMaxStreamM, M, d_in);
   return SPEC_OK;
 }
 
@@ -417,10 +419,54 @@ int spec_verify_gemm_w8(const uint16_t* x, const uint8_t* w, const float* w_scal
   if (rc != SPEC_OK) return rc;
   int cus = 0;
   if ((rc = check_device(&cus)) != SPEC_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M > specv::kMaxStreamM)  // a dense contraction: the MFMA tile kernel
+    return launched(specv::launch_gemm_tile_w8(x, w, w_scale, y, y_dtype == SPEC_BF16, M, d_in,
+                                               d_out, s),
+                    "spec_verify_gemm_w8");
   return launched(specv::launch_gemm_stream(x, w, w_scale, y, y_dtype == SPEC_BF16, true, M, d_in,
-                                            d_out, cus * stream_wgs_per_cu(M, true),
-                                            static_cast<hipStream_t>(stream)),
+                                            d_out, cus * stream_wgs_per_cu(M, true), s),
                   "spec_verify_gemm_w8");
+}
+
+int spec_probe_read(const void* buf, size_t bytes, int loads_per_lane, int wgs_per_cu,
+                    void* sink, void* stream) {
+  clear_error();
+  if (!buf || !sink) return fail(SPEC_ERR_INVALID_ARGUMENT, "null buf or sink");
+  if (loads_per_lane != 1 && loads_per_lane != 2 && loads_per_lane != 4 && loads_per_lane != 8)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "loads_per_lane=%d (1, 2, 4 or 8)", loads_per_lane);
+  if (wgs_per_cu < 1 || wgs_per_cu > 4)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "wgs_per_cu=%d outside [1, 4]", wgs_per_cu);
+  if (bytes < 16 || bytes % 16 != 0)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "bytes=%zu must be a positive multiple of 16", bytes);
+  if (!aligned(buf, 16) || !aligned(sink, 4))
+    return fail(SPEC_ERR_ALIGNMENT, "buf must be 16-byte and sink 4-byte aligned");
+  int cus = 0;
+  int rc = check_device(&cus);
+  if (rc != SPEC_OK) return rc;
+  return launched(specv::launch_probe_read(buf, bytes, loads_per_lane,
+                                           static_cast<unsigned*>(sink), wgs_per_cu * cus,
+                                           static_cast<hipStream_t>(stream)),
+                  "spec_probe_read");
+}
+
+int spec_probe_mfma(int shape, int iters, void* sink, double* flops, void* stream) {
+  clear_error();
+  if (shape != 16 && shape != 32)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "shape=%d (16 or 32)", shape);
+  if (iters < 1 || iters > (1 << 24))
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "iters=%d outside [1, 2^24]", iters);
+  if (!sink || !flops) return fail(SPEC_ERR_INVALID_ARGUMENT, "null sink or flops");
+  if (!aligned(sink, 4)) return fail(SPEC_ERR_ALIGNMENT, "sink must be 4-byte aligned");
+  int cus = 0;
+  int rc = check_device(&cus);
+  if (rc != SPEC_OK) return rc;
+  const int grid = 2 * cus;  // two workgroups of four waves: two waves per SIMD
+  // per wave and iteration: 8 x 16x16x32 or 4 x 32x32x16, 131072 FLOPs either way
+  *flops = (double)grid * 4 * iters * 131072.0;
+  return launched(specv::launch_probe_mfma(shape, iters, static_cast<unsigned*>(sink), grid,
+                                           static_cast<hipStream_t>(stream)),
+                  "spec_probe_mfma");
 }
 
 int spec_chain_reset(void* workspace, unsigned generation) {

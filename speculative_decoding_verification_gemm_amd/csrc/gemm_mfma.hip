@@ -1,5 +1,6 @@
 // Verify-pass linears for many verify positions: y[M][N] = x[M][K] . w[N][K]^T
-// with bf16 MFMA (v_mfma_f32_16x16x32_bf16) and fp32 accumulators.
+// with bf16 MFMA (v_mfma_f32_32x32x16_bf16 and v_mfma_f32_16x16x32_bf16) and
+// fp32 accumulators; w bf16, or FP8 E4M3 codes with a scale per row.
 //
 // Once B*(K+1) positions make the product a real dense contraction (the
 // batch crossover of "Speculative Decoding: Guess Several Tokens, Check Them
@@ -158,48 +159,87 @@ constexpr int kTileKAlign = 64;  // the kernel needs K to be a multiple of this
 // its own, and the KS partial tiles are added through LDS in group order at
 // the end (deterministic). A small tile then still has NW waves' loads in
 // flight.
-template <int BM, int BN, int WM, int S, int BK, int NW, int KS = 1>
+//
+// MF is the MFMA block: 16 (v_mfma_f32_16x16x32_bf16, a k-step of 32) or 32
+// (v_mfma_f32_32x32x16_bf16, a k-step of 16). Both read one 16-byte operand
+// unit per lane per k-step, so a wave tile reads the same LDS bytes per
+// reduction element either way; the 32x32 form issues half as many MFMAs
+// for the same products, and measured on MI355X a stream of independent
+// 32x32x16 MFMAs reaches about 1.9 PFLOP/s where 16x16x32 reaches about 1.2.
+// W8: the weights are FP8 E4M3 codes (one byte each) with one fp32 scale
+// per output row (weight-only 8-bit storage, "Speculative Decoding: The
+// Algebra and the Proof", Where it breaks). A weight row then takes BK
+// bytes of LDS per stage instead of 2 BK; fragment reads fetch 8 codes (8
+// bytes) per lane and widen them exactly to bf16 before the same MFMA, and
+// the row's scale multiplies the fp32 sum in the epilogue.
+template <int BM, int BN, int WM, int S, int BK, int NW, int KS = 1, int MF = 16, bool W8 = false>
 struct TileCfg {
   static constexpr int NWG = NW / KS;            // waves per k-group
   static constexpr int WN = NWG / WM;            // a group's waves: WM along M, WN along N
-  static constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
-  static constexpr int ROWS = BM + BN;           // LDS rows per stage (x rows, then w rows)
-  static constexpr int UPR = BK / 8;             // 16-byte units per row
-  static constexpr int RPI = 64 / UPR;           // rows per load instruction
-  static constexpr int RPL = 128 / (2 * BK);     // rows per 128-byte bank line
-  static constexpr int ROW_BYTES = 2 * BK;
-  static constexpr int L = ROWS / (NWG * RPI);   // load instructions per wave per stage
-  static constexpr int STAGE_BYTES = ROWS * ROW_BYTES;
+  static constexpr int TM = BM / WM / MF, TN = BN / WN / MF;
+  static constexpr int MFB = MF;
+  static constexpr int KSTEP = MF == 16 ? 32 : 16;  // reduction elements per MFMA
+  static constexpr int NACC = MF == 16 ? 4 : 16;    // accumulator floats per lane per block
+  // A stage holds BM x rows (bf16), then BN w rows (bf16, or FP8 codes).
+  static constexpr int ROW_A = 2 * BK;
+  static constexpr int ROW_B = (W8 ? 1 : 2) * BK;
+  static constexpr int UPR_A = ROW_A / 16, UPR_B = ROW_B / 16;  // 16-byte units per row
+  static constexpr int RPI_A = 64 / UPR_A, RPI_B = 64 / UPR_B;  // rows per 1 KB load instruction
+  static constexpr int IA = BM / RPI_A, IB = BN / RPI_B;        // load instructions per stage
+  static constexpr int L = (IA + IB) / NWG;      // load instructions per wave per stage
+  static constexpr int B_OFF = BM * ROW_A;       // w rows' offset in a stage
+  static constexpr int STAGE_BYTES = B_OFF + BN * ROW_B;
   static constexpr int RING_BYTES = KS * S * STAGE_BYTES;
   static constexpr int RED_BYTES = KS > 1 ? KS * BM * BN * 4 : 0;  // partial tiles, over the drained ring
   static constexpr int LDS_BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
   static_assert(BK == 32 || BK == 64, "stage depth");
-  static_assert(TM >= 1 && TN >= 1 && BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
-  static_assert(NWG * KS == NW && WM * WN == NWG && ROWS % (NWG * RPI) == 0,
+  static_assert(!W8 || BK == 64, "FP8 rows are 64 bytes: a stage of 64 reduction elements");
+  static_assert(MF == 16 || MF == 32, "MFMA block");
+  static_assert(TM >= 1 && TN >= 1 && BM % (MF * WM) == 0 && BN % (MF * WN) == 0, "wave tile");
+  static_assert(NWG * KS == NW && WM * WN == NWG && BM % RPI_A == 0 && BN % RPI_B == 0 &&
+                    (IA + IB) % NWG == 0,
                 "whole load instructions per wave");
   static_assert(S >= 2 && LDS_BYTES <= 160 * 1024 && NW * 64 <= 1024, "LDS ring, workgroup");
 };
-// Stored position of unit u of LDS row r, XOR-swizzled so that a fragment
-// read (16 consecutive rows at one unit) is free of bank conflicts whether
-// the banks serve 128 bytes (eight lanes) or 256 bytes (sixteen lanes) at a
-// time: eight consecutive rows map to distinct 16-byte slots of a 128-byte
-// bank line, and the second eight rows of the 16 to the opposite slots.
-template <class C>
+// Stored position of unit u of LDS row r in a region of UPR 16-byte units
+// per row, XOR-swizzled so that fragment reads are free of bank conflicts.
+// Measured on MI355X (SQ_LDS_BANK_CONFLICT of a probe kernel): a
+// 16-byte-per-lane LDS read is served for lanes 0-7 together with lanes
+// 32-39 (and 8-15 with 40-47, ...), over 256 bytes of banks, so those 16
+// lanes must hit 16 distinct 16-byte slots of a 256-byte window.
+//  * 32x32 fragments (lane l: row l % 32, unit l / 32 of the k-step): rows
+//    r and r of the next unit meet, so the rows of one parity need distinct
+//    positions that stay distinct after flipping the unit's low bit: the
+//    row index itself, u ^ (r mod 8) ^ (bit 3 of r).
+//  * 16x16 fragments (row l % 16, unit l / 16): rows r at units u and
+//    u + 2 meet, so positions must stay distinct after flipping bit 1:
+//    u ^ g(r) with g taking 0, 0, 1, 1, 4, 4, 5, 5 over r mod 8 (rows of one
+//    parity take 0, 1, 4, 5), and bit 1 set for rows 8-15.
+// The former (row index) swizzle costs four conflict cycles per 16x16
+// fragment read; both forms here measure zero. 64-byte rows (BK = 32, or
+// FP8 weight rows) keep the row-index form over two rows per 128 bytes.
+template <int UPR, int MF>
 __device__ __forceinline__ int tile_unit_pos(int r, int u) {
-  return u ^ ((r / C::RPL) % C::UPR) ^ ((r / (C::RPL * C::UPR)) & 1);
+  if constexpr (MF == 16 && UPR == 8)
+    return u ^ ((((r >> 1) & 1) | (((r >> 2) & 1) << 2)) ^ (((r >> 3) & 1) << 1));
+  constexpr int RPL = 8 / UPR;  // rows per 128-byte line
+  return u ^ ((r / RPL) % UPR) ^ ((r / (RPL * UPR)) & 1);
 }
 
 __device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Address-space casts live in device helpers: the kernel body is also
 // checked by the host pass, where they are not valid.
-__device__ __forceinline__ void tile_load_lds(const uint16_t* src, char* lds_dst) {
+__device__ __forceinline__ void tile_load_lds(const char* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds((const SPECV_TILE_GLOBAL void*)src,
                                    (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 template <class T>
 __device__ __forceinline__ void tile_store(void* y, size_t i, T v) {
   ((SPECV_TILE_GLOBAL T*)y)[i] = v;
+}
+__device__ __forceinline__ float tile_scale(const float* ws, int col) {
+  return ((const SPECV_TILE_GLOBAL float*)ws)[col];
 }
 
 template <int N>
@@ -210,11 +250,28 @@ __device__ __forceinline__ void tile_wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int S, int BK, int NW, int KS, bool OUT_BF16>
+// Two FP8 E4M3 codes (the low or high 16 bits of v) widened to a bf16 pair;
+// every E4M3 value is exact in bf16.
+template <bool HI>
+__device__ __forceinline__ uint32_t tile_widen_fp8x2(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, HI));
+}
+
+// One MFMA on a pair of 16-byte operand fragments.
+template <int MF, class Acc>
+__device__ __forceinline__ Acc tile_mfma(bf16x8 a, bf16x8 b, Acc c) {
+  if constexpr (MF == 16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int BM, int BN, int WM, int S, int BK, int NW, int KS, int MF, bool W8, bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y, int M,
-    int N, int K, int n_tiles, int per_xcd) {
-  using C = TileCfg<BM, BN, WM, S, BK, NW, KS>;
+    const uint16_t* __restrict__ X, const void* __restrict__ W, const float* __restrict__ WS,
+    void* __restrict__ Y, int M, int N, int K, int n_tiles, int per_xcd) {
+  using C = TileCfg<BM, BN, WM, S, BK, NW, KS, MF, W8>;
+  typedef float facc __attribute__((ext_vector_type(C::NACC)));
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // XCD-grouped tile order: workgroup bid runs on XCD bid % 8
@@ -228,39 +285,56 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
   const int n_k = K / BK;
   const int n_j = (n_k + KS - 1) / KS;  // ring steps; group kg's step st is k-tile st * KS + kg
 
-  // This lane's source row and unit for each of its L load instructions: the
-  // instruction covers LDS rows RPI*g .. RPI*g + RPI-1 (g = wr + NWG*q); lane
-  // l writes LDS row RPI*g + l/UPR at stored unit l%UPR, which holds the
-  // row's global unit tile_unit_pos(row, l%UPR) (the swizzle is its own
-  // inverse).
-  const uint16_t* src[C::L];
+  // This lane's source address for each of its L load instructions. Load
+  // instruction g = wr + NWG q fills bytes [1 KB g, 1 KB (g + 1)) of a stage:
+  // x rows RPI_A g .. while g < IA, then w rows RPI_B (g - IA) ... Lane l
+  // writes row RPI g' + l / UPR of its region at stored unit l % UPR, which
+  // holds the row's global unit tile_unit_pos(row, l % UPR) (the swizzle is
+  // its own inverse). kstride: bytes of one k-tile along the row.
+  const char* src[C::L];
+  int kstride[C::L];
 #pragma unroll
   for (int q = 0; q < C::L; ++q) {
-    const int r = C::RPI * (wr + C::NWG * q) + lane / C::UPR;
-    const int u = tile_unit_pos<C>(r, lane % C::UPR);
-    const uint16_t* p;
-    if (r < BM)
-      p = X + (size_t)min(m0 + r, M - 1) * K + u * 8;
-    else
-      p = W + (size_t)min(n0 + (r - BM), N - 1) * K + u * 8;
-    src[q] = p;
+    const int g = wr + C::NWG * q;
+    if (g < C::IA) {
+      const int r = C::RPI_A * g + lane / C::UPR_A;
+      const int u = tile_unit_pos<C::UPR_A, MF>(r, lane % C::UPR_A);
+      src[q] = reinterpret_cast<const char*>(X + (size_t)min(m0 + r, M - 1) * K) + u * 16;
+      kstride[q] = C::ROW_A;
+    } else {
+      const int r = C::RPI_B * (g - C::IA) + lane / C::UPR_B;
+      const int u = tile_unit_pos<C::UPR_B, MF>(r, lane % C::UPR_B);
+      src[q] = static_cast<const char*>(W) + (size_t)min(n0 + r, N - 1) * K * (W8 ? 1 : 2) + u * 16;
+      kstride[q] = C::ROW_B;
+    }
   }
   auto issue = [&](int st) __attribute__((always_inline)) {
     // k-tiles past the end reload the last one into a slot nobody reads
     const int kc = min(st * KS + kg, n_k - 1);
     const int slot = kg * S + st % S;
 #pragma unroll
-    for (int q = 0; q < C::L; ++q) {
-      tile_load_lds(src[q] + (size_t)kc * BK, reinterpret_cast<char*>(lds) + slot * C::STAGE_BYTES +
-                                                  C::RPI * (wr + C::NWG * q) * C::ROW_BYTES);
-    }
+    for (int q = 0; q < C::L; ++q)
+      tile_load_lds(src[q] + (size_t)kc * kstride[q],
+                    reinterpret_cast<char*>(lds) + slot * C::STAGE_BYTES + (wr + C::NWG * q) * 1024);
   };
 
-  f32x4 acc[C::TM][C::TN];
+  facc acc[C::TM][C::TN];
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int e = 0; e < C::NACC; ++e) acc[i][j][e] = 0.f;
+  // Output position of accumulator float e of block (i, j) held by this
+  // lane: 16x16 blocks hold rows 4 (lane / 16) + e of column lane % 16;
+  // 32x32 blocks rows 8 (e / 4) + 4 (lane / 32) + e % 4 of column lane % 32.
+  auto out_row = [&](int i, int e) __attribute__((always_inline)) {
+    return MF == 16 ? wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + e
+                    : wm * (BM / WM) + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+  };
+  auto out_col = [&](int j) __attribute__((always_inline)) {
+    return wn * (BN / C::WN) + j * MF + (lane & (MF - 1));
+  };
 
 #pragma unroll
   for (int s = 0; s < S - 1; ++s) issue(s);
@@ -272,30 +346,47 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
     if (KS > 1 && st * KS + kg >= n_k) continue;  // this group has no k-tile left
     const char* base = reinterpret_cast<const char*>(lds) + (kg * S + st % S) * C::STAGE_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      const int unit = kk * 4 + (lane >> 4);
+    for (int kk = 0; kk < BK / C::KSTEP; ++kk) {
+      // lane l supplies row l % MF of its block and the 8 reduction
+      // elements starting at 8 (l / MF) of the k-step
+      const int k8 = kk * C::KSTEP + 8 * (lane / MF);
       bf16x8 a[C::TM], b[C::TN];
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
-        const int r = wm * (BM / WM) + i * 16 + (lane & 15);
-        a[i] = *reinterpret_cast<const bf16x8*>(base + r * C::ROW_BYTES +
-                                                 (tile_unit_pos<C>(r, unit) << 4));
+        const int r = wm * (BM / WM) + i * MF + (lane & (MF - 1));
+        a[i] = *reinterpret_cast<const bf16x8*>(
+            base + r * C::ROW_A + (tile_unit_pos<C::UPR_A, MF>(r, k8 >> 3) << 4));
       }
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
-        const int r = BM + wn * (BN / C::WN) + j * 16 + (lane & 15);
-        b[j] = *reinterpret_cast<const bf16x8*>(base + r * C::ROW_BYTES +
-                                                 (tile_unit_pos<C>(r, unit) << 4));
+        const int r = wn * (BN / C::WN) + j * MF + (lane & (MF - 1));
+        const char* row = base + C::B_OFF + r * C::ROW_B;
+        if constexpr (W8) {
+          // 8 codes: half (k8 / 8) % 2 of unit k8 / 16, widened to 8 bf16
+          const uint2 v = *reinterpret_cast<const uint2*>(
+              row + (tile_unit_pos<C::UPR_B, MF>(r, k8 >> 4) << 4) + ((k8 >> 3) & 1) * 8);
+          const u32x4 wv{tile_widen_fp8x2<false>(v.x), tile_widen_fp8x2<true>(v.x),
+                         tile_widen_fp8x2<false>(v.y), tile_widen_fp8x2<true>(v.y)};
+          b[j] = __builtin_bit_cast(bf16x8, wv);
+        } else {
+          b[j] = *reinterpret_cast<const bf16x8*>(
+              row + (tile_unit_pos<C::UPR_B, MF>(r, k8 >> 3) << 4));
+        }
       }
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = tile_mfma<MF>(a[i], b[j], acc[i][j]);
     }
   }
   tile_wait_vmcnt<0>();  // the reloads past the end land before the workgroup leaves
 
+  auto store = [&](int row, int col, float v) __attribute__((always_inline)) {
+    if (OUT_BF16)
+      tile_store<uint16_t>(Y, (size_t)row * N + col, f32_to_bf16_bits(v));
+    else
+      tile_store<float>(Y, (size_t)row * N + col, v);
+  };
   if constexpr (KS > 1) {
     // partial tiles of the k-groups into LDS (over the ring, once every wave
     // is done with it), then each output is the sum over groups in order
@@ -305,12 +396,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
       for (int jj = 0; jj < C::TN; ++jj) {
-        const int col = wn * (BN / C::WN) + jj * 16 + (lane & 15);
+        const int col = out_col(jj);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + r;
-          red[(kg * BM + row) * BN + col] = acc[i][jj][r];
-        }
+        for (int e = 0; e < C::NACC; ++e) red[(kg * BM + out_row(i, e)) * BN + col] = acc[i][jj][e];
       }
     __syncthreads();
     for (int e = tid; e < BM * BN; e += NW * 64) {
@@ -318,56 +406,47 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
       float v = red[e];
 #pragma unroll
       for (int g = 1; g < KS; ++g) v += red[g * BM * BN + e];
-      if (row < M && col < N) {
-        if (OUT_BF16)
-          tile_store<uint16_t>(Y, (size_t)row * N + col, f32_to_bf16_bits(v));
-        else
-          tile_store<float>(Y, (size_t)row * N + col, v);
-      }
+      if (row < M && col < N) store(row, col, W8 ? v * tile_scale(WS, col) : v);
     }
     return;
   }
 
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i)
+  for (int j = 0; j < C::TN; ++j) {
+    const int col = n0 + out_col(j);
+    const float sc = W8 && col < N ? tile_scale(WS, col) : 1.0f;
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int col = n0 + wn * (BN / C::WN) + j * 16 + (lane & 15);
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + r;
-        if (row < M && col < N) {
-          const float v = acc[i][j][r];
-          if (OUT_BF16)
-            tile_store<uint16_t>(Y, (size_t)row * N + col, f32_to_bf16_bits(v));
-          else
-            tile_store<float>(Y, (size_t)row * N + col, v);
-        }
+      for (int e = 0; e < C::NACC; ++e) {
+        const int row = m0 + out_row(i, e);
+        if (row < M && col < N) store(row, col, W8 ? acc[i][j][e] * sc : acc[i][j][e]);
       }
-    }
+  }
 }
 
-template <int BM, int BN, int WM, int S, int BK, int NW = 8, int KS = 1>
-static hipError_t launch_tile_t(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16,
-                                int M, int K, int N, hipStream_t s) {
-  using C = TileCfg<BM, BN, WM, S, BK, NW, KS>;
+template <int BM, int BN, int WM, int S, int BK, int NW = 8, int KS = 1, int MF = 16,
+          bool W8 = false>
+static hipError_t launch_tile_t(const uint16_t* x, const void* w, const float* ws, void* y,
+                                bool out_bf16, int M, int K, int N, hipStream_t s) {
+  using C = TileCfg<BM, BN, WM, S, BK, NW, KS, MF, W8>;
   const int n_tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int per_xcd = (n_tiles + 7) / 8;
   const dim3 grid(8 * per_xcd);
   static const hipError_t a1 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, true>),
+      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, true>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   static const hipError_t a2 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, false>),
+      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, false>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
   if (out_bf16)
-    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, true>), grid, dim3(NW * 64),
-                       C::LDS_BYTES, s, x, w, y, M, N, K, n_tiles, per_xcd);
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, true>), grid,
+                       dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, y, M, N, K, n_tiles, per_xcd);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, false>), grid, dim3(NW * 64),
-                       C::LDS_BYTES, s, x, w, y, M, N, K, n_tiles, per_xcd);
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, false>), grid,
+                       dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, y, M, N, K, n_tiles, per_xcd);
   return hipGetLastError();
 }
 
@@ -380,28 +459,36 @@ static const int kTileShapes[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 1
                                      {32, 32},   {32, 16},   {32, 64}};
 
 // Time model of one launch, per reduction element: a tile costs
-// a * (BM + BN) (operand lines into LDS and out to the matrix cores) plus
-// b * BM * BN (the products), and the tiles run in ceil(tiles / CUs) rounds.
-// a and b were fitted to measured Llama-shaped linears at M = 320 and 1280
-// on MI355X. At M = 20 to 128 the shapes it picks for the Llama-3.1-8B
-// linears were checked against every small shape forced in turn: the pick
-// was the fastest, or within about 10 % of it.
-static int pick_tile(int M, int N, int cus) {
+// a * (BM + wb BN) (operand lines into LDS and out to the matrix cores; wb
+// is the bytes of a weight element relative to bf16, 1/2 for FP8) plus
+// b * BM * BN (the products), and the tiles run in ceil(tiles / CUs)
+// rounds. a and b were fitted to measured Llama-shaped linears at M = 320
+// and 1280 on MI355X. At M = 20 to 128 the shapes it picks for the
+// Llama-3.1-8B linears were checked against every small shape forced in
+// turn: the pick was the fastest, or within about 10 % of it.
+static int pick_tile(int M, int N, int cus, const int (*shapes)[2], int n, double wb = 1.0) {
   const double a = 3.6e-5, b = 8.1e-8;
-  const int n = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
   int best = 0;
   double best_t = 0.0;
   for (int i = 0; i < n; ++i) {
-    const int bm = kTileShapes[i][0], bn = kTileShapes[i][1];
+    const int bm = shapes[i][0], bn = shapes[i][1];
     const long tiles = (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     const long rounds = (tiles + cus - 1) / cus;
-    const double t = rounds * (a * (bm + bn) + b * (double)bm * bn);
+    const double t = rounds * (a * (bm + wb * bn) + b * (double)bm * bn);
     if (i == 0 || t < best_t) {
       best_t = t;
       best = i;
     }
   }
   return best;
+}
+
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  return cus;
 }
 
 template <int BM, int BN, int WM>
@@ -417,14 +504,39 @@ static hipError_t launch_mfma_t(const uint16_t* x, const uint16_t* w, void* y, b
   return hipGetLastError();
 }
 
+#if defined(SPECV_DIAGNOSTICS)
+#include <stdlib.h>
+// Diagnostic builds: SPECV_TILE_FORCE=<id> replaces the picked tile by one
+// of these (timing experiments only).
+static hipError_t launch_tile_forced(int id, const uint16_t* x, const uint16_t* w, void* y,
+                                     bool o, int M, int K, int N, hipStream_t s) {
+  switch (id) {
+    case 100: return launch_tile_t<256, 256, 4, 4, 32, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 101: return launch_tile_t<256, 256, 4, 5, 32, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 102: return launch_tile_t<128, 256, 2, 6, 32, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 103: return launch_tile_t<256, 128, 4, 6, 32, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 104: return launch_tile_t<128, 128, 2, 8, 32, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 105: return launch_tile_t<256, 256, 4, 2, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s);
+    case 106: return launch_tile_t<192, 256, 2, 2, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 108: return launch_tile_t<320, 128, 2, 2, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 110: return launch_tile_t<256, 256, 4, 2, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 111: return launch_tile_t<128, 256, 2, 3, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 112: return launch_tile_t<128, 128, 2, 4, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 113: return launch_tile_t<64, 128, 2, 4, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+#endif
+
 hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
                             int K, int N, hipStream_t s) {
+#if defined(SPECV_DIAGNOSTICS)
+  if (const char* f = getenv("SPECV_TILE_FORCE"))
+    if (K % kTileKAlign == 0) return launch_tile_forced(atoi(f), x, w, y, out_bf16, M, K, N, s);
+#endif
   if (K % kTileKAlign == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus = 256;
-    const int pick = pick_tile(M, N, cus);
+    const int cus = device_cus();
+    const int pick = pick_tile(M, N, cus, kTileShapes, sizeof(kTileShapes) / sizeof(kTileShapes[0]));
     const long tiles = (long)((M + kTileShapes[pick][0] - 1) / kTileShapes[pick][0]) *
                        ((N + kTileShapes[pick][1] - 1) / kTileShapes[pick][1]);
     if (tiles <= cus) {
@@ -433,30 +545,55 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
       // flight as a large tile's (measured on the Llama linears at M = 20 to
       // 128: O and down 15-30 % faster, QKV 5-20 %).
       switch (pick) {
-        case 6: return launch_tile_t<64, 64, 2, 4, 64, 8, 2>(x, w, y, out_bf16, M, K, N, s);
-        case 7: return launch_tile_t<64, 32, 2, 4, 64, 8, 2>(x, w, y, out_bf16, M, K, N, s);
-        case 8: return launch_tile_t<32, 32, 2, 4, 64, 8, 2>(x, w, y, out_bf16, M, K, N, s);
-        case 9: return launch_tile_t<32, 16, 2, 4, 64, 8, 4>(x, w, y, out_bf16, M, K, N, s);
+        case 6: return launch_tile_t<64, 64, 2, 4, 64, 8, 2, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
+        case 7: return launch_tile_t<64, 32, 2, 4, 64, 8, 2>(x, w, nullptr, y, out_bf16, M, K, N, s);
+        case 8: return launch_tile_t<32, 32, 2, 4, 64, 8, 2>(x, w, nullptr, y, out_bf16, M, K, N, s);
+        case 9: return launch_tile_t<32, 16, 2, 4, 64, 8, 4>(x, w, nullptr, y, out_bf16, M, K, N, s);
         default: break;
       }
     }
     switch (pick) {
-      case 0: return launch_tile_t<256, 256, 4, 2, 64>(x, w, y, out_bf16, M, K, N, s);
-      case 1: return launch_tile_t<256, 128, 4, 3, 64>(x, w, y, out_bf16, M, K, N, s);
-      case 2: return launch_tile_t<128, 256, 2, 3, 64>(x, w, y, out_bf16, M, K, N, s);
-      case 3: return launch_tile_t<128, 128, 2, 4, 64>(x, w, y, out_bf16, M, K, N, s);
-      case 4: return launch_tile_t<128, 64, 4, 4, 64>(x, w, y, out_bf16, M, K, N, s);
-      case 5: return launch_tile_t<64, 128, 2, 4, 64>(x, w, y, out_bf16, M, K, N, s);
-      case 6: return launch_tile_t<64, 64, 2, 4, 64>(x, w, y, out_bf16, M, K, N, s);
-      case 7: return launch_tile_t<64, 32, 2, 4, 64, 4>(x, w, y, out_bf16, M, K, N, s);
-      case 8: return launch_tile_t<32, 32, 2, 6, 64, 4>(x, w, y, out_bf16, M, K, N, s);
-      case 9: return launch_tile_t<32, 16, 2, 6, 64, 2>(x, w, y, out_bf16, M, K, N, s);
-      default: return launch_tile_t<32, 64, 1, 4, 64, 4>(x, w, y, out_bf16, M, K, N, s);
+      // wave tiles that are whole 32x32 blocks use the 32x32x16 MFMA
+      case 0: return launch_tile_t<256, 256, 4, 2, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 1: return launch_tile_t<256, 128, 4, 3, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 2: return launch_tile_t<128, 256, 2, 3, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 3: return launch_tile_t<128, 128, 2, 4, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 4: return launch_tile_t<128, 64, 4, 4, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 5: return launch_tile_t<64, 128, 2, 4, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 6: return launch_tile_t<64, 64, 2, 4, 64>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 7: return launch_tile_t<64, 32, 2, 4, 64, 4>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 8: return launch_tile_t<32, 32, 2, 6, 64, 4>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 9: return launch_tile_t<32, 16, 2, 6, 64, 2>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      default: return launch_tile_t<32, 64, 1, 4, 64, 4>(x, w, nullptr, y, out_bf16, M, K, N, s);
     }
   }
   if (M <= 32) return launch_mfma_t<32, 64, 1>(x, w, y, out_bf16, M, K, N, s);
   if (M <= 128) return launch_mfma_t<64, 64, 2>(x, w, y, out_bf16, M, K, N, s);
   return launch_mfma_t<128, 128, 2>(x, w, y, out_bf16, M, K, N, s);
+}
+
+// FP8 E4M3 weights with per-row scales. The tile shapes are those whose
+// load instructions divide evenly over the waves once a weight row takes
+// 64 bytes per stage (8 x rows or 16 w rows per instruction); an FP8 stage
+// is 3/4 the size of a bf16 one, so the largest tile keeps three stages.
+static const int kTileShapesW8[][2] = {{256, 256}, {128, 256}, {128, 128}, {64, 128},
+                                       {64, 64},   {32, 32},   {32, 16},   {32, 64}};
+
+hipError_t launch_gemm_tile_w8(const uint16_t* x, const uint8_t* w, const float* w_scale, void* y,
+                               bool out_bf16, int M, int K, int N, hipStream_t s) {
+  if (K % kTileKAlign != 0) return hipErrorInvalidValue;
+  const int pick = pick_tile(M, N, device_cus(), kTileShapesW8,
+                             sizeof(kTileShapesW8) / sizeof(kTileShapesW8[0]), 0.5);
+  switch (pick) {
+    case 0: return launch_tile_t<256, 256, 4, 3, 64, 8, 1, 32, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 1: return launch_tile_t<128, 256, 2, 4, 64, 8, 1, 32, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 2: return launch_tile_t<128, 128, 2, 4, 64, 8, 1, 32, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 3: return launch_tile_t<64, 128, 2, 4, 64, 8, 1, 32, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 4: return launch_tile_t<64, 64, 2, 4, 64, 8, 2, 32, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 5: return launch_tile_t<32, 32, 2, 4, 64, 4, 2, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 6: return launch_tile_t<32, 16, 1, 4, 64, 4, 4, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    default: return launch_tile_t<32, 64, 1, 4, 64, 4, 1, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+  }
 }
 
 }  // namespace specv

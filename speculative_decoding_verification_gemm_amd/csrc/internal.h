@@ -94,6 +94,10 @@ hipError_t launch_gemm_skinny(const uint16_t* x, const uint16_t* w, void* y, boo
                               int K, int N, hipStream_t s);
 hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
                             int K, int N, hipStream_t s);
+// FP8 E4M3 weights with per-row scales on the tile kernel (K a multiple of
+// 64; any M, used above kMaxStreamM).
+hipError_t launch_gemm_tile_w8(const uint16_t* x, const uint8_t* w, const float* w_scale, void* y,
+                               bool out_bf16, int M, int K, int N, hipStream_t s);
 
 // Verify attention (attention.hip): head dimension 128, (K+1) * H / Hkv <= 32
 // query rows per key/value head. The split count depends only on the shape;
@@ -112,6 +116,13 @@ hipError_t launch_accept_probs(const float* p, const float* q, const int32_t* to
 hipError_t launch_sample_probs(const float* p, const float* q, const int32_t* n_accepted,
                                const float* u_sample, int B, int K, int V, int32_t* token,
                                uint8_t* zero_residual, hipStream_t s);
+
+// Probe kernels (probe.hip): the achievable HBM read bandwidth and dense
+// bf16 MFMA rate. launch_probe_mfma's FLOPs per launch are
+// grid * 4 waves * iters * 131072 (8 chains of 16x16x32 or 4 of 32x32x16).
+hipError_t launch_probe_read(const void* buf, size_t bytes, int loads, unsigned* sink, int grid,
+                             hipStream_t s);
+hipError_t launch_probe_mfma(int shape, int iters, unsigned* sink, int grid, hipStream_t s);
 
 // Fused sampling stage of spec_verify (logits in, tokens out).
 size_t verify_workspace_bytes(int B, int K, int V);

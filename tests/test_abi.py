@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     for n in names:
         assert hasattr(sv.lib, n), n
 
@@ -120,6 +120,21 @@ def test_verify_rejects(sv):
     assert _verify(sv, ws=A + 16) == -4
 
 
+def test_probe_rejects(sv):
+    import ctypes
+    f = ctypes.c_double()
+    assert sv.lib.spec_probe_read(None, 1024, 4, 1, A, None) == -1
+    assert sv.lib.spec_probe_read(A, 0, 4, 1, A, None) == -1
+    assert sv.lib.spec_probe_read(A, 1000, 4, 1, A, None) == -1
+    assert sv.lib.spec_probe_read(A, 1024, 3, 1, A, None) == -1
+    assert sv.lib.spec_probe_read(A, 1024, 4, 0, A, None) == -1
+    assert sv.lib.spec_probe_read(A + 8, 1024, 4, 1, A, None) == -2
+    assert sv.lib.spec_probe_mfma(8, 10, A, ctypes.byref(f), None) == -1
+    assert sv.lib.spec_probe_mfma(16, 0, A, ctypes.byref(f), None) == -1
+    assert sv.lib.spec_probe_mfma(32, 10, None, ctypes.byref(f), None) == -1
+    assert sv.lib.spec_probe_mfma(32, 10, A + 2, ctypes.byref(f), None) == -2
+
+
 def test_verify_noalloc_rejects(sv):
     f = sv.lib.spec_verify_noalloc
 
@@ -163,7 +178,7 @@ def test_gemm_w8_rejects(sv):
         ((A, A, A, A, 0, 5, 4096, 0), -1),
         ((A, A, A + 2, A, 0, 5, 4096, 4096), -2),    # misaligned scales
         ((A, A + 8, A, A, 0, 5, 4096, 4096), -2),    # misaligned weights
-        ((A, A, A, A, 0, 17, 4096, 4096), -3),       # beyond the streaming kernel
+        ((A, A, A, A, 0, 17, 4112, 4096), -3),       # tile kernel: d_in not a multiple of 64
     ]
     for args, code in cases:
         assert f(*args, None) == code, args

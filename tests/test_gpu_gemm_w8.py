@@ -1,5 +1,6 @@
 """GPU parity of the weight-only FP8 verify linear (spec_verify_gemm_w8 and
-the FP8 chain) against the fp64 oracle (oracle.linear_w8).
+the FP8 chain) against the fp64 oracle (oracle.linear_w8): the streaming
+kernel up to 16 positions, the MFMA tile kernel above.
 
 Weights are FP8 E4M3 codes with one float32 scale per output row,
 activations bf16 ("Speculative Decoding: The Algebra and the Proof", Where it
@@ -95,6 +96,83 @@ def test_w8_special_codes_one_hot_exact(sv, dev):
 
 
 LLAMA8B = [(4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096), (4096, 128256)]
+
+
+# Above 16 positions the tile kernel: one case per FP8 tile shape the
+# dispatcher can pick (256x256, 128x256, 128x128, 64x128, 64x64 in two
+# k-groups, 32x32 in two, 32x16 in four, 32x64), with ragged M and N tails,
+# d_in of one stage (64: some k-groups get no k-tile) up to many.
+W8_TILE_CASES = [(513, 256, 16400), (200, 192, 16400), (513, 1024, 4104), (33, 128, 16400),
+                 (130, 64, 4095), (17, 1024, 4104), (20, 4096, 777), (17, 512, 16400),
+                 (1280, 320, 777)]
+
+
+@pytest.mark.parametrize("M,d_in,d_out", W8_TILE_CASES)
+def test_w8_tile_kernel(sv, dev, M, d_in, d_out):
+    import torch
+    x, w, s = host_inputs(M + 3 * d_in + d_out, M, d_in, d_out)
+    ref = oracle.linear_w8(x, w, s)
+    for od in (torch.float32, torch.bfloat16):
+        y = run(sv, dev, x, w, s, od)
+        check(y, ref, od == torch.float32, f"w8 tile M={M} {d_in}->{d_out} {od}")
+
+
+def test_w8_tile_special_codes_one_hot_exact(sv, dev):
+    """As the one-hot test below, through the tile kernel (M = 32): every
+    finite code times its row scale, bit-exact."""
+    import torch
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    d_in, d_out, M = 256, len(codes), 32
+    rng = np.random.default_rng(5)
+    w = np.zeros((d_out, d_in), dtype=np.uint8)
+    cols = rng.permutation(d_in)[:M]
+    for j, k in enumerate(cols):
+        w[:, k] = np.roll(codes, 11 * j)
+    s = synth.w8_row_scales(6, "w8.special.tile", d_out)
+    x = np.zeros((M, d_in), dtype=np.uint16)
+    x[np.arange(M), cols] = 0x3F80  # 1.0
+    y = run(sv, dev, x, w, s, torch.float32)
+    want = (oracle.e4m3_to_f64(w[:, cols].T) * s.astype(np.float64)[None, :]).astype(np.float32)
+    assert np.array_equal(y.astype(np.float32), want)
+
+
+@pytest.mark.parametrize("M", [20, 80, 320, 1280])
+@pytest.mark.parametrize("d_in,d_out", LLAMA8B)
+def test_w8_batch_sweep_shapes(sv, dev, M, d_in, d_out):
+    """The Llama-3.1-8B linears with FP8 weights at every swept batch (B = 4,
+    16, 64, 256 at K = 4), as the FP8 batch sweep runs them; the oracle
+    checks sampled output columns (first and last 8 plus random ones)."""
+    import torch
+    from synth import device as sd
+    seed = 41 * M + d_out
+    w = sd.e4m3_normal_codes((d_out, d_in), synth.W8_CODE_STD, seed, dev)
+    s = sd.w8_row_scales(d_out, synth.WEIGHT_STD / synth.W8_CODE_STD, seed + 1, dev)
+    x = sd.normal_bf16((M, d_in), 1.0, seed + 2, dev)
+    od = torch.float32 if d_out == 128256 else torch.bfloat16
+    y = sv.verify_gemm_w8(x, w, s, out_dtype=od)
+    rng = np.random.default_rng(seed)
+    cols = np.unique(np.concatenate([np.arange(8), np.arange(d_out - 8, d_out),
+                                     rng.integers(0, d_out, 48)]))
+    idx = torch.from_numpy(cols).to(dev)
+    ref = oracle.linear_w8(sd.to_bits(x), w.index_select(0, idx).cpu().numpy(),
+                           s.index_select(0, idx).cpu().numpy())
+    got = y.index_select(1, idx).float().cpu().numpy().astype(np.float64)
+    check(got, ref, od == torch.float32, f"w8 sweep M={M} {d_in}->{d_out}")
+    del w, y
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M", [20, 320])
+def test_w8_tile_deterministic(sv, dev, M):
+    import torch
+    from synth import device as sd
+    w = sd.e4m3_normal_codes((6144, 4096), synth.W8_CODE_STD, 5, dev)
+    s = sd.w8_row_scales(6144, synth.WEIGHT_STD / synth.W8_CODE_STD, 6, dev)
+    x = sd.normal_bf16((M, 4096), 1.0, 7, dev)
+    a = sv.verify_gemm_w8(x, w, s)
+    b = sv.verify_gemm_w8(x, w, s)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("d_in,d_out", LLAMA8B)
