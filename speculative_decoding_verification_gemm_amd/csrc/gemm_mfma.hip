@@ -8,6 +8,8 @@
 // in LDS and multiplied on the matrix cores. Few positions use the
 // weight-streaming kernel in gemm_stream.hip instead.
 
+#include <stdlib.h>
+
 #include "common.h"
 #include "internal.h"
 
@@ -192,8 +194,7 @@ struct TileCfg {
   static constexpr int RING_BYTES = KS * S * STAGE_BYTES;
   static constexpr int RED_BYTES = KS > 1 ? KS * BM * BN * 4 : 0;  // partial tiles, over the drained ring
   static constexpr int LDS_BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
-  static_assert(BK == 32 || BK == 64, "stage depth");
-  static_assert(!W8 || BK == 64, "FP8 rows are 64 bytes: a stage of 64 reduction elements");
+  static_assert(BK == 32 || BK == 64 || (W8 && BK == 128), "stage depth");
   static_assert(MF == 16 || MF == 32, "MFMA block");
   static_assert(TM >= 1 && TN >= 1 && BM % (MF * WM) == 0 && BN % (MF * WN) == 0, "wave tile");
   static_assert(NWG * KS == NW && WM * WN == NWG && BM % RPI_A == 0 && BN % RPI_B == 0 &&
@@ -220,6 +221,14 @@ struct TileCfg {
 // FP8 weight rows) keep the row-index form over two rows per 128 bytes.
 template <int UPR, int MF>
 __device__ __forceinline__ int tile_unit_pos(int r, int u) {
+  // 256-byte rows (activations of 128-element FP8 stages): one row fills
+  // the 256-byte window, so the 16 lanes that meet need distinct positions
+  // among 16: g(r) keeps g and g ^ 2 apart for 16x16 (0, 1, 4, 5, 8, 9, 12,
+  // 13 over r mod 8), g and g ^ 1 for 32x32 (0, 2, 4, ..., 14).
+  if constexpr (UPR == 16) {
+    if constexpr (MF == 16) return u ^ ((r & 1) | ((r & 6) << 1));
+    return u ^ ((r & 7) << 1);
+  }
   if constexpr (MF == 16 && UPR == 8)
     return u ^ ((((r >> 1) & 1) | (((r >> 2) & 1) << 2)) ^ (((r >> 3) & 1) << 1));
   constexpr int RPL = 8 / UPR;  // rows per 128-byte line
@@ -430,6 +439,7 @@ template <int BM, int BN, int WM, int S, int BK, int NW = 8, int KS = 1, int MF 
 static hipError_t launch_tile_t(const uint16_t* x, const void* w, const float* ws, void* y,
                                 bool out_bf16, int M, int K, int N, hipStream_t s) {
   using C = TileCfg<BM, BN, WM, S, BK, NW, KS, MF, W8>;
+  if (K % BK != 0) return hipErrorInvalidValue;  // whole stages only
   const int n_tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int per_xcd = (n_tiles + 7) / 8;
   const dim3 grid(8 * per_xcd);
@@ -456,18 +466,22 @@ static hipError_t launch_tile_t(const uint16_t* x, const void* w, const float* w
 // CU.
 static const int kTileShapes[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128},
                                      {128, 64},  {64, 128},  {64, 64},   {64, 32},
-                                     {32, 32},   {32, 16},   {32, 64}};
+                                     {32, 32},   {32, 16},   {32, 64},   {320, 128},
+                                     {320, 256}};
 
 // Time model of one launch, per reduction element: a tile costs
 // a * (BM + wb BN) (operand lines into LDS and out to the matrix cores; wb
 // is the bytes of a weight element relative to bf16, 1/2 for FP8) plus
 // b * BM * BN (the products), and the tiles run in ceil(tiles / CUs)
-// rounds. a and b were fitted to measured Llama-shaped linears at M = 320
-// and 1280 on MI355X. At M = 20 to 128 the shapes it picks for the
-// Llama-3.1-8B linears were checked against every small shape forced in
-// turn: the pick was the fastest, or within about 10 % of it.
+// rounds. a and b are a relative least-squares fit to the measured times of
+// eight tile shapes (256x256, 256x128, 128x256, 128x128, 128x64, 64x128,
+// 320x128, 320x256) on the five Llama-3.1-8B linears at M = 320 and 1280 on
+// MI355X: the model then picks the fastest measured shape for nine of the
+// ten linears and one within 2 % for the tenth. At M = 20 to 256 it picks
+// what the earlier fit picked there, which was checked against every small
+// shape forced in turn at M = 20 to 128 (the fastest, or within about 10 %).
 static int pick_tile(int M, int N, int cus, const int (*shapes)[2], int n, double wb = 1.0) {
-  const double a = 3.6e-5, b = 8.1e-8;
+  const double a = 2.5e-5, b = 1.88e-7;
   int best = 0;
   double best_t = 0.0;
   for (int i = 0; i < n; ++i) {
@@ -505,7 +519,6 @@ static hipError_t launch_mfma_t(const uint16_t* x, const uint16_t* w, void* y, b
 }
 
 #if defined(SPECV_DIAGNOSTICS)
-#include <stdlib.h>
 // Diagnostic builds: SPECV_TILE_FORCE=<id> replaces the picked tile by one
 // of these (timing experiments only).
 static hipError_t launch_tile_forced(int id, const uint16_t* x, const uint16_t* w, void* y,
@@ -523,6 +536,15 @@ static hipError_t launch_tile_forced(int id, const uint16_t* x, const uint16_t* 
     case 111: return launch_tile_t<128, 256, 2, 3, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
     case 112: return launch_tile_t<128, 128, 2, 4, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
     case 113: return launch_tile_t<64, 128, 2, 4, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 120: return launch_tile_t<128, 256, 2, 3, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s);
+    case 121: return launch_tile_t<128, 128, 2, 4, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s);
+    case 122: return launch_tile_t<64, 128, 2, 4, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s);
+    case 123: return launch_tile_t<128, 64, 4, 4, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s);
+    case 124: return launch_tile_t<256, 128, 4, 3, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s);
+    case 125: return launch_tile_t<320, 128, 2, 2, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s);
+    case 126: return launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 127: return launch_tile_t<128, 64, 4, 4, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 128: return launch_tile_t<256, 128, 4, 3, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -536,7 +558,11 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
 #endif
   if (K % kTileKAlign == 0) {
     const int cus = device_cus();
-    const int pick = pick_tile(M, N, cus, kTileShapes, sizeof(kTileShapes) / sizeof(kTileShapes[0]));
+    constexpr int n_shapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
+    int pick = pick_tile(M, N, cus, kTileShapes, n_shapes);
+#if defined(SPECV_DIAGNOSTICS)
+    if (const char* f = getenv("SPECV_TILE_PICK")) pick = max(0, min(atoi(f), n_shapes - 1));
+#endif
     const long tiles = (long)((M + kTileShapes[pick][0] - 1) / kTileShapes[pick][0]) *
                        ((N + kTileShapes[pick][1] - 1) / kTileShapes[pick][1]);
     if (tiles <= cus) {
@@ -545,7 +571,7 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
       // flight as a large tile's (measured on the Llama linears at M = 20 to
       // 128: O and down 15-30 % faster, QKV 5-20 %).
       switch (pick) {
-        case 6: return launch_tile_t<64, 64, 2, 4, 64, 8, 2, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
+        case 6: return launch_tile_t<64, 64, 2, 4, 64, 8, 2>(x, w, nullptr, y, out_bf16, M, K, N, s);
         case 7: return launch_tile_t<64, 32, 2, 4, 64, 8, 2>(x, w, nullptr, y, out_bf16, M, K, N, s);
         case 8: return launch_tile_t<32, 32, 2, 4, 64, 8, 2>(x, w, nullptr, y, out_bf16, M, K, N, s);
         case 9: return launch_tile_t<32, 16, 2, 4, 64, 8, 4>(x, w, nullptr, y, out_bf16, M, K, N, s);
@@ -553,18 +579,27 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
       }
     }
     switch (pick) {
-      // wave tiles that are whole 32x32 blocks use the 32x32x16 MFMA
-      case 0: return launch_tile_t<256, 256, 4, 2, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
-      case 1: return launch_tile_t<256, 128, 4, 3, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
-      case 2: return launch_tile_t<128, 256, 2, 3, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
-      case 3: return launch_tile_t<128, 128, 2, 4, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
-      case 4: return launch_tile_t<128, 64, 4, 4, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
-      case 5: return launch_tile_t<64, 128, 2, 4, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      // 16x16x32 blocks: measured faster than 32x32x16 on every shape both
+      // forms exist for (by 3-15 %, e.g. 256x128 at M = 1280: QKV 66 against
+      // 71 us, down 197 against 220; 256x256 lm-head 1193 against 1275)
+      case 0: return launch_tile_t<256, 256, 4, 2, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 1: return launch_tile_t<256, 128, 4, 3, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 2: return launch_tile_t<128, 256, 2, 3, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 3: return launch_tile_t<128, 128, 2, 4, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 4: return launch_tile_t<128, 64, 4, 4, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 5: return launch_tile_t<64, 128, 2, 4, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
       case 6: return launch_tile_t<64, 64, 2, 4, 64>(x, w, nullptr, y, out_bf16, M, K, N, s);
       case 7: return launch_tile_t<64, 32, 2, 4, 64, 4>(x, w, nullptr, y, out_bf16, M, K, N, s);
       case 8: return launch_tile_t<32, 32, 2, 6, 64, 4>(x, w, nullptr, y, out_bf16, M, K, N, s);
       case 9: return launch_tile_t<32, 16, 2, 6, 64, 2>(x, w, nullptr, y, out_bf16, M, K, N, s);
-      default: return launch_tile_t<32, 64, 1, 4, 64, 4>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 10: return launch_tile_t<32, 64, 1, 4, 64, 4>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      // 320 rows: B = 64 and B = 256 sequences of K + 1 = 5 positions fill
+      // one or four of them without padding (M = 320: gate/up 89 against
+      // 144 us with 256x256 tiles; lm-head with 320x256, 334 against 419 us;
+      // M = 1280 gate/up with 320x256, 282 against 316 us). The 320x256
+      // wave tile (160x64) uses 32x32x16 blocks, the only form measured.
+      case 11: return launch_tile_t<320, 128, 2, 2, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      default: return launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
     }
   }
   if (M <= 32) return launch_mfma_t<32, 64, 1>(x, w, y, out_bf16, M, K, N, s);
@@ -577,22 +612,96 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
 // 64 bytes per stage (8 x rows or 16 w rows per instruction); an FP8 stage
 // is 3/4 the size of a bf16 one, so the largest tile keeps three stages.
 static const int kTileShapesW8[][2] = {{256, 256}, {128, 256}, {128, 128}, {64, 128},
-                                       {64, 64},   {32, 32},   {32, 16},   {32, 64}};
+                                       {64, 64},   {32, 32},   {32, 16},   {32, 64},
+                                       {64, 32},   {320, 128}, {320, 256}};
+
+// Stages of 128 reduction elements (K a multiple of 128): a weight row is
+// then one whole 128-byte line per stage instead of half of one. Measured
+// on the Llama-3.1-8B linears at M = 20 to 1280 against the 64-element
+// form of the same shape, these are faster wherever they appear below
+// (e.g. 64x32 at M = 80 on the down projection 48 against 61 us, 32x16 at
+// M = 20 24 against 31 us, 128x256 at M = 1280 on QKV 85 against 96 us).
+// The others keep 64-element stages: 64x128, and 32x32 and 32x64 over
+// several rounds, hold more workgroups per CU that way (the doubled stage
+// would halve it) and measured slower with 128; 256x256 and the 320-row
+// tiles would not fit their stages in LDS.
+static bool w8_has_k128(int pick, bool one_round) {
+  return pick == 1 || pick == 2 || pick == 4 || pick == 6 || pick == 8 ||
+         ((pick == 5 || pick == 7) && one_round);
+}
+
+static hipError_t launch_w8_k128(int pick, const uint16_t* x, const uint8_t* w, const float* ws,
+                                 void* y, bool o, int M, int K, int N, hipStream_t s) {
+  switch (pick) {
+    case 1: return launch_tile_t<128, 256, 2, 2, 128, 8, 1, 16, true>(x, w, ws, y, o, M, K, N, s);
+    case 2: return launch_tile_t<128, 128, 2, 3, 128, 8, 1, 16, true>(x, w, ws, y, o, M, K, N, s);
+    case 4: return launch_tile_t<64, 64, 2, 3, 128, 8, 2, 16, true>(x, w, ws, y, o, M, K, N, s);
+    case 5: return launch_tile_t<32, 32, 2, 3, 128, 8, 4, 16, true>(x, w, ws, y, o, M, K, N, s);
+    case 6: return launch_tile_t<32, 16, 1, 2, 128, 8, 8, 16, true>(x, w, ws, y, o, M, K, N, s);
+    case 7: return launch_tile_t<32, 64, 1, 4, 128, 8, 2, 16, true>(x, w, ws, y, o, M, K, N, s);
+    case 8: return launch_tile_t<64, 32, 2, 2, 128, 8, 4, 16, true>(x, w, ws, y, o, M, K, N, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+#if defined(SPECV_DIAGNOSTICS)
+// Diagnostic builds: further 128-element FP8 forms (K a multiple of 128).
+static hipError_t launch_w8_forced(int id, const uint16_t* x, const uint8_t* w, const float* ws,
+                                   void* y, bool o, int M, int K, int N, hipStream_t s) {
+  if (K % 128 != 0) return hipErrorInvalidValue;
+  switch (id) {
+    case 105: return launch_tile_t<64, 128, 2, 4, 128, 8, 1, 16, true>(x, w, ws, y, o, M, K, N, s);
+    case 108: return launch_tile_t<32, 64, 1, 4, 128, 4, 1, 16, true>(x, w, ws, y, o, M, K, N, s);
+    case 109: return launch_tile_t<32, 32, 2, 4, 128, 4, 2, 16, true>(x, w, ws, y, o, M, K, N, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+#endif
 
 hipError_t launch_gemm_tile_w8(const uint16_t* x, const uint8_t* w, const float* w_scale, void* y,
                                bool out_bf16, int M, int K, int N, hipStream_t s) {
   if (K % kTileKAlign != 0) return hipErrorInvalidValue;
-  const int pick = pick_tile(M, N, device_cus(), kTileShapesW8,
-                             sizeof(kTileShapesW8) / sizeof(kTileShapesW8[0]), 0.5);
+  const int cus = device_cus();
+  constexpr int n_shapes = sizeof(kTileShapesW8) / sizeof(kTileShapesW8[0]);
+  int pick = pick_tile(M, N, cus, kTileShapesW8, n_shapes, 0.5);
+  bool allow_k128 = true;
+#if defined(SPECV_DIAGNOSTICS)
+  if (const char* f = getenv("SPECV_TILE_FORCE_W8")) {
+    const int id = atoi(f);
+    if (id >= 100) return launch_w8_forced(id, x, w, w_scale, y, out_bf16, M, K, N, s);
+    pick = max(0, min(id, n_shapes - 1));
+  }
+  if (getenv("SPECV_W8_NO_K128")) allow_k128 = false;
+#endif
+  const long tiles = (long)((M + kTileShapesW8[pick][0] - 1) / kTileShapesW8[pick][0]) *
+                     ((N + kTileShapesW8[pick][1] - 1) / kTileShapesW8[pick][1]);
+  const bool one_round = tiles <= cus;
+  if (allow_k128 && K % 128 == 0 && w8_has_k128(pick, one_round))
+    return launch_w8_k128(pick, x, w, w_scale, y, out_bf16, M, K, N, s);
+  if (one_round) {
+    // one round of small tiles: eight waves per tile in k-groups, so that
+    // each CU keeps eight waves' loads in flight (as for bf16 weights)
+    switch (pick) {
+      case 5: return launch_tile_t<32, 32, 2, 4, 64, 8, 4, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+      case 7: return launch_tile_t<32, 64, 1, 4, 64, 8, 2, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+      default: break;
+    }
+  }
   switch (pick) {
-    case 0: return launch_tile_t<256, 256, 4, 3, 64, 8, 1, 32, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
-    case 1: return launch_tile_t<128, 256, 2, 4, 64, 8, 1, 32, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
-    case 2: return launch_tile_t<128, 128, 2, 4, 64, 8, 1, 32, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
-    case 3: return launch_tile_t<64, 128, 2, 4, 64, 8, 1, 32, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
-    case 4: return launch_tile_t<64, 64, 2, 4, 64, 8, 2, 32, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 0: return launch_tile_t<256, 256, 4, 3, 64, 8, 1, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 1: return launch_tile_t<128, 256, 2, 4, 64, 8, 1, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 2: return launch_tile_t<128, 128, 2, 4, 64, 8, 1, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 3: return launch_tile_t<64, 128, 2, 4, 64, 8, 1, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 4: return launch_tile_t<64, 64, 2, 4, 64, 8, 2, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    // 64x32 needs four k-groups of two waves for whole load instructions
+    case 8: return launch_tile_t<64, 32, 2, 4, 64, 8, 4, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 9: return launch_tile_t<320, 128, 2, 3, 64, 8, 1, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 10: return launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
     case 5: return launch_tile_t<32, 32, 2, 4, 64, 4, 2, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
-    case 6: return launch_tile_t<32, 16, 1, 4, 64, 4, 4, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
-    default: return launch_tile_t<32, 64, 1, 4, 64, 4, 1, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    // (the model picks 32x16 only where its tiles fit one round)
+    case 6: return launch_tile_t<32, 16, 1, 3, 64, 8, 8, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    case 7: return launch_tile_t<32, 64, 1, 4, 64, 4, 1, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -98,12 +98,21 @@ def test_w8_special_codes_one_hot_exact(sv, dev):
 LLAMA8B = [(4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096), (4096, 128256)]
 
 
-# Above 16 positions the tile kernel: one case per FP8 tile shape the
-# dispatcher can pick (256x256, 128x256, 128x128, 64x128, 64x64 in two
-# k-groups, 32x32 in two, 32x16 in four, 32x64), with ragged M and N tails,
-# d_in of one stage (64: some k-groups get no k-tile) up to many.
-W8_TILE_CASES = [(513, 256, 16400), (200, 192, 16400), (513, 1024, 4104), (33, 128, 16400),
-                 (130, 64, 4095), (17, 1024, 4104), (20, 4096, 777), (17, 512, 16400),
+# Above 16 positions the tile kernel: one case per FP8 tile form the
+# dispatcher can pick -- 256x256, 128x256, 128x128, 64x128, 64x64 in two
+# k-groups, 64x32 in four; 32x32 in one round (eight waves, four k-groups)
+# and in several (four waves, two); 32x16 (eight waves, eight k-groups);
+# 32x64 in one round (eight waves, two k-groups) and in several (four
+# waves); 320x128 and 320x256 -- with ragged M and N tails, d_in of one
+# stage (64 or 128: some k-groups get no k-tile) up to many. Where d_in is
+# a multiple of 128, 128x256, 128x128, 64x64, 64x32, 32x16 and the
+# one-round 32x32 and 32x64 run with 128-element stages; each of those
+# shapes appears here with such a d_in and with one that is not.
+W8_TILE_CASES = [(513, 256, 16400), (200, 192, 16400), (130, 384, 24000), (513, 1024, 4104),
+                 (80, 320, 16400), (33, 128, 16400), (130, 64, 4095), (47, 640, 8200),
+                 (611, 128, 792), (611, 192, 792), (17, 1024, 4104), (20, 192, 6150),
+                 (193, 128, 2334), (20, 4096, 777), (17, 320, 1000), (20, 256, 12288),
+                 (20, 192, 12300), (17, 512, 16400), (301, 192, 24000), (301, 64, 60000),
                  (1280, 320, 777)]
 
 
