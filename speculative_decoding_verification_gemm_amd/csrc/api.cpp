@@ -378,7 +378,7 @@ size_t spec_verify_attention_workspace_bytes(int B, int K, int T, int n_heads, i
                                              int head_dim) {
   if (check_attention_shape(B, K, T, n_heads, n_kv_heads, head_dim) != SPEC_OK) return 0;
   const size_t n = specv::attention_workspace_bytes(
-      B, K + 1, n_heads, n_kv_heads, specv::attention_splits(B, n_kv_heads, T));
+      B, K + 1, n_heads, n_kv_heads, specv::attention_splits(B, K + 1, n_heads, n_kv_heads, T));
   return (n + 255) & ~(size_t)255;
 }
 

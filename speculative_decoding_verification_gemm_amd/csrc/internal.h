@@ -102,7 +102,7 @@ hipError_t launch_gemm_tile_w8(const uint16_t* x, const uint8_t* w, const float*
 // Verify attention (attention.hip): head dimension 128, (K+1) * H / Hkv <= 32
 // query rows per key/value head. The split count depends only on the shape;
 // the workspace holds the split partials (0 bytes when there is one split).
-int attention_splits(int B, int Hkv, int T);
+int attention_splits(int B, int K1, int H, int Hkv, int T);
 size_t attention_workspace_bytes(int B, int K1, int H, int Hkv, int n_split);
 hipError_t launch_verify_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    void* out, bool out_bf16, int B, int K1, int T, int H, int Hkv,
