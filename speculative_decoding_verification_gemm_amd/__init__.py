@@ -420,9 +420,22 @@ class Chain:
         prepare = lib.spec_chain_prepare_w8 if self.w8 else lib.spec_chain_prepare
         check(prepare(descs, self.n, self.M, _ptr(self.workspace), nbytes))
 
-    def run(self):
+    def run(self, check_error=False):
+        """One launch of the chain on the current stream (asynchronous). A
+        barrier that gives up, or a grid the device could not hold, is only
+        known on the device: with check_error=True the call waits for the
+        launch and raises RuntimeError if the error word is set (it is then
+        read and cleared)."""
         run = lib.spec_verify_gemm_chain_w8 if self.w8 else lib.spec_verify_gemm_chain
         check(run(self.n, self.M, _ptr(self.workspace), _stream()))
+        if check_error:
+            _torch().cuda.current_stream().synchronize()
+            e = self.error()
+            if e:
+                raise RuntimeError(
+                    f"chain launch failed on the device (error word {e}: bit 0, a barrier "
+                    "gave up waiting; bit 1, the grid differs from the prepared plan); "
+                    "its outputs are not valid")
 
     def error(self):
         """Read and clear the device-side error word (synchronous)."""

@@ -174,7 +174,8 @@ constexpr int kTileKAlign = 64;  // the kernel needs K to be a multiple of this
 // bytes of LDS per stage instead of 2 BK; fragment reads fetch 8 codes (8
 // bytes) per lane and widen them exactly to bf16 before the same MFMA, and
 // the row's scale multiplies the fp32 sum in the epilogue.
-template <int BM, int BN, int WM, int S, int BK, int NW, int KS = 1, int MF = 16, bool W8 = false>
+template <int BM, int BN, int WM, int S, int BK, int NW, int KS = 1, int MF = 16, bool W8 = false,
+          bool WL = false>
 struct TileCfg {
   static constexpr int NWG = NW / KS;            // waves per k-group
   static constexpr int WN = NWG / WM;            // a group's waves: WM along M, WN along N
@@ -193,7 +194,12 @@ struct TileCfg {
   static constexpr int STAGE_BYTES = B_OFF + BN * ROW_B;
   static constexpr int RING_BYTES = KS * S * STAGE_BYTES;
   static constexpr int RED_BYTES = KS > 1 ? KS * BM * BN * 4 : 0;  // partial tiles, over the drained ring
-  static constexpr int LDS_BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
+  // WL (FP8 weights): each stage's codes are widened once per workgroup
+  // into a bf16 region of BN rows of 2 BK bytes after the ring
+  static constexpr int ROW_W = 2 * BK, UPR_W = ROW_W / 16;
+  static constexpr int WIDE_BYTES = WL ? BN * ROW_W : 0;
+  static constexpr int LDS_BYTES = (RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES) + WIDE_BYTES;
+  static_assert(!WL || (W8 && KS == 1), "widening in LDS: FP8 weights, one k-group");
   static_assert(BK == 32 || BK == 64 || (W8 && BK == 128), "stage depth");
   static_assert(MF == 16 || MF == 32, "MFMA block");
   static_assert(TM >= 1 && TN >= 1 && BM % (MF * WM) == 0 && BN % (MF * WN) == 0, "wave tile");
@@ -275,11 +281,12 @@ __device__ __forceinline__ Acc tile_mfma(bf16x8 a, bf16x8 b, Acc c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int BM, int BN, int WM, int S, int BK, int NW, int KS, int MF, bool W8, bool OUT_BF16>
+template <int BM, int BN, int WM, int S, int BK, int NW, int KS, int MF, bool W8, bool WL,
+          bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
     const uint16_t* __restrict__ X, const void* __restrict__ W, const float* __restrict__ WS,
     void* __restrict__ Y, int M, int N, int K, int n_tiles, int per_xcd) {
-  using C = TileCfg<BM, BN, WM, S, BK, NW, KS, MF, W8>;
+  using C = TileCfg<BM, BN, WM, S, BK, NW, KS, MF, W8, WL>;
   typedef float facc __attribute__((ext_vector_type(C::NACC)));
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -354,6 +361,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
     issue(st + S - 1);
     if (KS > 1 && st * KS + kg >= n_k) continue;  // this group has no k-tile left
     const char* base = reinterpret_cast<const char*>(lds) + (kg * S + st % S) * C::STAGE_BYTES;
+    char* wide = reinterpret_cast<char*>(lds) + C::LDS_BYTES - C::WIDE_BYTES;
+    if constexpr (WL) {
+      // widen the stage's codes once for the workgroup: 16 codes (one
+      // 16-byte unit) per thread and pass into two bf16 units of the wide
+      // region (whose previous contents every wave finished with before the
+      // barrier above); then make them visible to every wave
+      constexpr int UPB = BK / 16;  // code units per weight row
+      for (int c = tid; c < BN * UPB; c += NW * 64) {
+        const int r = c / UPB, u = c - r * UPB;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(
+            base + C::B_OFF + r * C::ROW_B + (tile_unit_pos<C::UPR_B, MF>(r, u) << 4));
+        const u32x4 lo{tile_widen_fp8x2<false>(v.x), tile_widen_fp8x2<true>(v.x),
+                       tile_widen_fp8x2<false>(v.y), tile_widen_fp8x2<true>(v.y)};
+        const u32x4 hi{tile_widen_fp8x2<false>(v.z), tile_widen_fp8x2<true>(v.z),
+                       tile_widen_fp8x2<false>(v.w), tile_widen_fp8x2<true>(v.w)};
+        *reinterpret_cast<u32x4*>(wide + r * C::ROW_W + (tile_unit_pos<C::UPR_W, MF>(r, 2 * u) << 4)) = lo;
+        *reinterpret_cast<u32x4*>(wide + r * C::ROW_W +
+                                  (tile_unit_pos<C::UPR_W, MF>(r, 2 * u + 1) << 4)) = hi;
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+      tile_barrier();
+    }
 #pragma unroll
     for (int kk = 0; kk < BK / C::KSTEP; ++kk) {
       // lane l supplies row l % MF of its block and the 8 reduction
@@ -370,7 +399,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
       for (int j = 0; j < C::TN; ++j) {
         const int r = wn * (BN / C::WN) + j * MF + (lane & (MF - 1));
         const char* row = base + C::B_OFF + r * C::ROW_B;
-        if constexpr (W8) {
+        if constexpr (WL) {
+          b[j] = *reinterpret_cast<const bf16x8*>(
+              wide + r * C::ROW_W + (tile_unit_pos<C::UPR_W, MF>(r, k8 >> 3) << 4));
+        } else if constexpr (W8) {
           // 8 codes: half (k8 / 8) % 2 of unit k8 / 16, widened to 8 bf16
           const uint2 v = *reinterpret_cast<const uint2*>(
               row + (tile_unit_pos<C::UPR_B, MF>(r, k8 >> 4) << 4) + ((k8 >> 3) & 1) * 8);
@@ -435,27 +467,27 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
 }
 
 template <int BM, int BN, int WM, int S, int BK, int NW = 8, int KS = 1, int MF = 16,
-          bool W8 = false>
+          bool W8 = false, bool WL = false>
 static hipError_t launch_tile_t(const uint16_t* x, const void* w, const float* ws, void* y,
                                 bool out_bf16, int M, int K, int N, hipStream_t s) {
-  using C = TileCfg<BM, BN, WM, S, BK, NW, KS, MF, W8>;
+  using C = TileCfg<BM, BN, WM, S, BK, NW, KS, MF, W8, WL>;
   if (K % BK != 0) return hipErrorInvalidValue;  // whole stages only
   const int n_tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int per_xcd = (n_tiles + 7) / 8;
   const dim3 grid(8 * per_xcd);
   static const hipError_t a1 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, true>),
+      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, WL, true>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   static const hipError_t a2 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, false>),
+      reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, WL, false>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
   if (out_bf16)
-    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, true>), grid,
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, WL, true>), grid,
                        dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, y, M, N, K, n_tiles, per_xcd);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, false>), grid,
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, WL, false>), grid,
                        dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, y, M, N, K, n_tiles, per_xcd);
   return hipGetLastError();
 }
@@ -644,6 +676,32 @@ static hipError_t launch_w8_k128(int pick, const uint16_t* x, const uint8_t* w, 
   }
 }
 
+// Each stage's codes widened once per workgroup into a bf16 LDS region
+// (behind a second barrier per stage) instead of once per wave row at every
+// fragment read: 1 / WM of the conversions. v_cvt_scalef32_pk_bf16_fp8
+// costs about two plain VALU slots (measured), and the per-wave widening
+// spends 4 / TM of them per MFMA, enough to compete with the matrix cores
+// once the products dominate. Measured on the Llama-3.1-8B linears at
+// M = 320: QKV 46.5 -> 41.3 us, O 47.2 -> 40.3, gate/up 130 -> 98.5, down
+// 169 -> 123, lm-head 392 -> 359; at M = 1280 1-6 % on the 320-row tiles
+// and 64x128 / 128x128 down. Tiles whose per-wave widening costs little
+// (128x256 with 128-element stages, 256x256) measured slower with it, and
+// so did 64x128 at M = 80 on gate/up: the 320-row tiles always take it,
+// 64x128 and 128x128 from M = 256.
+static bool w8_wide(int pick, int M) {
+  return pick == 9 || pick == 10 || (M >= 256 && (pick == 2 || pick == 3));
+}
+static hipError_t launch_w8_wide(int pick, const uint16_t* x, const uint8_t* w, const float* ws,
+                                 void* y, bool o, int M, int K, int N, hipStream_t s) {
+  switch (pick) {
+    case 2: return launch_tile_t<128, 128, 2, 4, 64, 8, 1, 16, true, true>(x, w, ws, y, o, M, K, N, s);
+    case 3: return launch_tile_t<64, 128, 2, 4, 64, 8, 1, 16, true, true>(x, w, ws, y, o, M, K, N, s);
+    case 9: return launch_tile_t<320, 128, 2, 3, 64, 8, 1, 16, true, true>(x, w, ws, y, o, M, K, N, s);
+    case 10: return launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32, true, true>(x, w, ws, y, o, M, K, N, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 #if defined(SPECV_DIAGNOSTICS)
 // Diagnostic builds: further 128-element FP8 forms (K a multiple of 128).
 static hipError_t launch_w8_forced(int id, const uint16_t* x, const uint8_t* w, const float* ws,
@@ -676,6 +734,7 @@ hipError_t launch_gemm_tile_w8(const uint16_t* x, const uint8_t* w, const float*
   const long tiles = (long)((M + kTileShapesW8[pick][0] - 1) / kTileShapesW8[pick][0]) *
                      ((N + kTileShapesW8[pick][1] - 1) / kTileShapesW8[pick][1]);
   const bool one_round = tiles <= cus;
+  if (w8_wide(pick, M)) return launch_w8_wide(pick, x, w, w_scale, y, out_bf16, M, K, N, s);
   if (allow_k128 && K % 128 == 0 && w8_has_k128(pick, one_round))
     return launch_w8_k128(pick, x, w, w_scale, y, out_bf16, M, K, N, s);
   if (one_round) {
@@ -695,8 +754,6 @@ hipError_t launch_gemm_tile_w8(const uint16_t* x, const uint8_t* w, const float*
     case 4: return launch_tile_t<64, 64, 2, 4, 64, 8, 2, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
     // 64x32 needs four k-groups of two waves for whole load instructions
     case 8: return launch_tile_t<64, 32, 2, 4, 64, 8, 4, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
-    case 9: return launch_tile_t<320, 128, 2, 3, 64, 8, 1, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
-    case 10: return launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
     case 5: return launch_tile_t<32, 32, 2, 4, 64, 4, 2, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);
     // (the model picks 32x16 only where its tiles fit one round)
     case 6: return launch_tile_t<32, 16, 1, 3, 64, 8, 8, 16, true>(x, w, w_scale, y, out_bf16, M, K, N, s);

@@ -261,6 +261,14 @@ def test_chain_barrier_give_up_is_reported(sv, dev):
     ch.run()
     torch.cuda.synchronize()
     assert ch.error() & 1
+    # the same, reported by the binding's checked launch
+    ch.reset(5)
+    hdr[7] = 64
+    hdr[0] = 9
+    torch.cuda.synchronize()
+    with pytest.raises(RuntimeError, match="error word 1"):
+        ch.run(check_error=True)
     hdr[7] = default_limit
     ch.reset(5)
     _run_and_check(ch, lin, refs, "after reset")
+    ch.run(check_error=True)

@@ -107,13 +107,17 @@ LLAMA8B = [(4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096), (4096, 1282
 # stage (64 or 128: some k-groups get no k-tile) up to many. Where d_in is
 # a multiple of 128, 128x256, 128x128, 64x64, 64x32, 32x16 and the
 # one-round 32x32 and 32x64 run with 128-element stages; each of those
-# shapes appears here with such a d_in and with one that is not.
+# shapes appears here with such a d_in and with one that is not. The
+# 320-row tiles, and 64x128 and 128x128 from M = 256, widen each stage's
+# codes once per workgroup in LDS: each of those appears with d_in a
+# multiple of 128 and not.
 W8_TILE_CASES = [(513, 256, 16400), (200, 192, 16400), (130, 384, 24000), (513, 1024, 4104),
-                 (80, 320, 16400), (33, 128, 16400), (130, 64, 4095), (47, 640, 8200),
+                 (300, 192, 8200), (80, 320, 16400), (80, 256, 16400), (33, 128, 16400),
+                 (1280, 320, 777), (301, 256, 6150), (130, 64, 4095), (47, 640, 8200),
                  (611, 128, 792), (611, 192, 792), (17, 1024, 4104), (20, 192, 6150),
                  (193, 128, 2334), (20, 4096, 777), (17, 320, 1000), (20, 256, 12288),
-                 (20, 192, 12300), (17, 512, 16400), (301, 192, 24000), (301, 64, 60000),
-                 (1280, 320, 777)]
+                 (20, 192, 12300), (17, 512, 16400), (301, 192, 24000), (257, 128, 24000),
+                 (301, 64, 60000), (513, 128, 60000)]
 
 
 @pytest.mark.parametrize("M,d_in,d_out", W8_TILE_CASES)
@@ -126,12 +130,15 @@ def test_w8_tile_kernel(sv, dev, M, d_in, d_out):
         check(y, ref, od == torch.float32, f"w8 tile M={M} {d_in}->{d_out} {od}")
 
 
-def test_w8_tile_special_codes_one_hot_exact(sv, dev):
-    """As the one-hot test below, through the tile kernel (M = 32): every
-    finite code times its row scale, bit-exact."""
+@pytest.mark.parametrize("M,d_in", [(32, 256), (320, 512)])
+def test_w8_tile_special_codes_one_hot_exact(sv, dev, M, d_in):
+    """As the one-hot test below, through the tile kernel: every finite code
+    times its row scale, bit-exact -- with the codes widened per wave at
+    every fragment read (M = 32) and once per workgroup in LDS (M = 320, a
+    320-row tile)."""
     import torch
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
-    d_in, d_out, M = 256, len(codes), 32
+    d_out = len(codes)
     rng = np.random.default_rng(5)
     w = np.zeros((d_out, d_in), dtype=np.uint8)
     cols = rng.permutation(d_in)[:M]
