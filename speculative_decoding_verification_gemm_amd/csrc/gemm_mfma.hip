@@ -265,6 +265,15 @@ __device__ __forceinline__ void tile_wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
+// lgkmcnt(0): this wave's LDS accesses are complete. The builtin alone is
+// not ordered against LDS accesses by the compiler; the empty asm with a
+// memory clobber on both sides keeps them where they are written.
+__device__ __forceinline__ void tile_wait_lgkm0() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt and expcnt at their maxima, lgkmcnt 0
+  asm volatile("" ::: "memory");
+}
+
 // Two FP8 E4M3 codes (the low or high 16 bits of v) widened to a bf16 pair;
 // every E4M3 value is exact in bf16.
 template <bool HI>
@@ -380,7 +389,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
         *reinterpret_cast<u32x4*>(wide + r * C::ROW_W +
                                   (tile_unit_pos<C::UPR_W, MF>(r, 2 * u + 1) << 4)) = hi;
       }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+      tile_wait_lgkm0();  // this wave's LDS writes are done
       tile_barrier();
     }
 #pragma unroll
