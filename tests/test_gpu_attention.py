@@ -55,6 +55,10 @@ CASES = [  # B, K, T, H, Hkv
     (2, 3, 77, 16, 2),        # 8 query heads per kv head
     (1, 4, 5, 32, 8),         # no context: T = K+1
     (1, 4, 4096, 32, 8),      # the Llama-3.1-8B layer shape, context splits
+    (1, 3, 4096, 32, 8),      # 16 rows: eight waves in single-wave teams, 16 splits
+    (40, 4, 300, 32, 8),      # 320 (sequence, kv head) groups: four waves, two splits
+    (40, 3, 300, 32, 8),      # the same with 16 rows (single-wave teams)
+    (64, 3, 200, 32, 8),      # 512 groups of 16 rows: four waves, one split
 ]
 
 
