@@ -93,12 +93,6 @@ __device__ __forceinline__ float att_row_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// LDS transpose read (ds_read_b64_tr_b16): within each 16 lanes, lane j
-// receives element j % 4 of the 8-byte chunks addressed by lanes j / 4,
-// j / 4 + 4, j / 4 + 8 and j / 4 + 12 (measured on MI355X), i.e. a 4 x 4
-// transpose of 16-bit elements.
-typedef short att_v4s __attribute__((ext_vector_type(4)));
-
 // Stored position of 16-byte unit u of token t in an LDS tile: u ^ swz(t),
 // swz(t) = (t0, t0, t1, t1 ^ t3) as bits 0..3 (t0 = bit 0 of t, ...). With
 // the sixteen lanes that one 16-byte access serves together (lanes 0-7 with
@@ -111,6 +105,12 @@ __device__ __forceinline__ int att_swz(int t) {
   const int b0 = t & 1, b1 = (t >> 1) & 1, b3 = (t >> 3) & 1;
   return b0 | (b0 << 1) | (b1 << 2) | ((b1 ^ b3) << 3);
 }
+
+// LDS transpose read (ds_read_b64_tr_b16): within each 16 lanes, lane j
+// receives element j % 4 of the 8-byte chunks addressed by lanes j / 4,
+// j / 4 + 4, j / 4 + 8 and j / 4 + 12 (measured on MI355X), i.e. a 4 x 4
+// transpose of 16-bit elements.
+typedef short att_v4s __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint2 att_read_tr(const char* p) {
   const att_v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) att_v4s*)(p));
@@ -118,11 +118,12 @@ __device__ __forceinline__ uint2 att_read_tr(const char* p) {
 }
 
 // Waves and query rows: every wave computes one 16-row tile of the group's
-// query rows. With up to 16 rows (RT = 1) each of the four waves walks its
-// own token tiles; with 17..32 rows (RT = 2) two teams of two waves share
-// token tiles, each wave of a team loading half of a tile (keys or values)
-// into the team's double-buffered LDS tile, one barrier per tile step. Either
-// way the registers allow two workgroups per CU.
+// query rows. With up to 16 rows (RT = 1) each of the NW waves walks its own
+// token tiles; with 17..32 rows (RT = 2) teams of two waves share token
+// tiles, each wave of a team loading half of a tile (keys or values) into
+// the team's double-buffered LDS tile, one barrier per tile step. The
+// registers allow two waves per SIMD: two four-wave workgroups per CU, or
+// one of eight.
 template <int RT, int NW>
 __global__ __launch_bounds__(NW * kWave, 8 / NW) void verify_attention_kernel(AttnArgs a) {
   extern __shared__ u32x4 att_lds[];

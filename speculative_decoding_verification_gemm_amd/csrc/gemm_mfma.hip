@@ -140,10 +140,9 @@ __global__ __launch_bounds__(kMfmaThreads) void gemm_mfma_kernel(
 //
 // Both operands reach LDS as whole 128-byte lines: one load instruction of a
 // wave moves 8 rows x 128 bytes (64 reduction elements) straight into LDS
-// (global_load_lds, no registers). Inside a row the eight 16-byte units are
-// stored XOR-swizzled by the row index mod 8, so the fragment reads of
-// v_mfma_f32_16x16x32_bf16 (lane l: row l % 16, unit l / 16) hit eight
-// distinct bank groups in every eight lanes. S tile stages are in flight;
+// (global_load_lds, no registers). Inside a row the 16-byte units are
+// stored XOR-swizzled (tile_unit_pos below), so that the MFMA fragment reads
+// are free of LDS bank conflicts. S tile stages are in flight;
 // each wave waits (vmcnt) for its own loads of the stage it computes on and
 // a workgroup barrier makes every wave's loads visible. The barrier is a
 // bare s_barrier: a memory fence there would make the compiler wait for all
@@ -155,7 +154,8 @@ constexpr int kTileKAlign = 64;  // the kernel needs K to be a multiple of this
 
 // BK reduction elements per stage: 64 (a whole 128-byte line of each row) or
 // 32 (half a line; the other half follows in the next stage, from L2), which
-// halves a stage so that more of them fit in LDS.
+// halves a stage so that more of them fit in LDS; with FP8 weights also 128
+// (a whole 128-byte line of each weight row).
 // KS > 1 splits the reduction inside the workgroup: the waves form KS
 // groups of NW / KS, group g takes k-tiles g, g + KS, ... through a ring of
 // its own, and the KS partial tiles are added through LDS in group order at
@@ -502,9 +502,10 @@ static hipError_t launch_tile_t(const uint16_t* x, const void* w, const float* w
 }
 
 // Tile shapes (BM, BN), indexed as in the launch switch of
-// launch_gemm_mfma; the first seven use eight waves, the last four (for
-// linears with few positions) two or four, so that several of them share a
-// CU.
+// launch_gemm_mfma: the first seven and the two 320-row tiles use eight
+// waves; the four small ones (for linears with few positions) two or four,
+// so that several of them share a CU, or eight in k-groups when their tiles
+// fit one round.
 static const int kTileShapes[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128},
                                      {128, 64},  {64, 128},  {64, 64},   {64, 32},
                                      {32, 32},   {32, 16},   {32, 64},   {320, 128},
