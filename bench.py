@@ -4,8 +4,10 @@ One step is the whole hot path of a speculative-decoding verify pass over
 synthetic Llama-shaped inputs already resident in HBM:
 
   1. the target's linear stack over M = B*(K+1) positions: per layer QKV,
-     O, gate/up and down, each a spec_verify_gemm that reads its bf16
-     weights once (bf16 outputs);
+     O, gate/up and down, each reading its bf16 weights once (bf16
+     outputs): one spec_verify_gemm_chain launch for all of them up to
+     M = 8, above that one spec_verify_gemm_ws per linear (the reduction
+     split over workgroups where that is faster);
   2. the lm-head (spec_verify_gemm, fp32 logits over the vocabulary);
   3. the sampling stage (spec_verify on those logits): softmax statistics,
      accept test and first rejection, residual or bonus draw, emit.
@@ -20,7 +22,8 @@ measured time, against the 8 TB/s HBM peak; MFMA peak where the FLOPs
 dominate) and the fp64 oracle's rate on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--workload llama8b|llama70b]
-                    [--batch B] [--no-graph] [--no-chain] [--no-cpu-baseline] [--w8]
+                    [--batch B] [--no-graph] [--no-chain] [--no-split]
+                    [--no-cpu-baseline] [--w8]
     python bench.py --attention [--batch B] [--context C]
                                          # the verify attention alone
     python bench.py --stress [--rounds R]  # the sampling-stress workload
@@ -60,6 +63,9 @@ def parse():
     ap.add_argument("--workload", choices=["llama8b", "llama70b"], default="llama8b")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-split", action="store_true",
+                    help="per-linear launches: spec_verify_gemm (no split reduction) "
+                         "instead of spec_verify_gemm_ws")
     ap.add_argument("--no-chain", action="store_true",
                     help="one spec_verify_gemm launch per linear instead of one chain launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -141,6 +147,7 @@ class Workload:
 
         self.stack, self.B, self.K, self.dev, self.w8 = stack, B, K, dev, w8
         self.fused_lm_head = fused_lm_head  # lm-head runs inside spec_verify
+        self.split = True  # bf16 per-linear launches: spec_verify_gemm_ws
         self.t_target, self.t_draft = 1.0, 1.0  # sampling temperatures (0: greedy)
         self.M = B * (K + 1)
         self.linears = []  # (name, x, w, y)
@@ -205,13 +212,28 @@ class Workload:
                 lin.append((self.hidden, self.lm_head, self.target_logits.view(self.M, self.V)))
         self.chain = sv.Chain(lin, self.dev)
 
+    def split_linears(self, sv):
+        """Stack linears that spec_verify_gemm_ws runs with a split reduction."""
+        if self.w8 or not self.split:
+            return 0
+        return sum(sv.gemm_workspace_bytes(self.M, w.shape[1], w.shape[0]) > 0
+                   for _, _, w, _ in self.linears)
+
     def gemm_phase(self, sv):
+        import torch
         if getattr(self, "chain", None) is not None:
             self.chain.run()
             return
+        if not self.w8 and self.split and getattr(self, "gemm_ws", None) is None:
+            # one workspace for every linear: the calls run in stream order
+            need = max(sv.gemm_workspace_bytes(self.M, w.shape[1], w.shape[0])
+                       for _, _, w, _ in self.linears)
+            self.gemm_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.dev)
         for (_, x, w, y), sc in zip(self.linears, self.scales):
             if self.w8:
                 sv.verify_gemm_w8(x, w, sc, out=y)
+            elif self.split:
+                sv.verify_gemm_ws(x, w, out=y, workspace=self.gemm_ws)
             else:
                 sv.verify_gemm(x, w, out=y)
         if not self.fused_lm_head:
@@ -648,6 +670,7 @@ def sweep_bench(args):
     rows = []
     for B in [int(b) for b in args.sweep_batches.split(",")]:
         wl = Workload(stack, B, K, args.seed, dev, w8=args.w8)
+        wl.split = not args.no_split
         wl.make_drafts(sv, synth.draft_noise_sigma(key, 0.8), args.seed)
         use_chain = wl.M <= (16 if args.w8 else 8)
         if use_chain:
@@ -658,6 +681,7 @@ def sweep_bench(args):
         by, fl = wl.gemm_bytes(), wl.gemm_flops()
         rows.append({"B": B, "M": wl.M, "steps": steps,
                      "gemm_launch": "chain" if use_chain else "per-linear",
+                     "split_linears": 0 if use_chain else wl.split_linears(sv),
                      "ms_gemm_phase": ms_gemm, "ms_sampling_phase": ms_samp,
                      "positions_per_s": wl.M / ((ms_gemm + ms_samp) * 1e-3),
                      "gemm_bytes": by, "gemm_flops": fl,
@@ -828,6 +852,7 @@ def main():
         sys.exit(2)
     wl = Workload(stack, B, K, args.seed, dev, w8=args.w8, fused_lm_head=fused)
     wl.t_target, wl.t_draft = args.t_target, args.t_draft
+    wl.split = not args.no_split
     wl.make_drafts(sv, synth.draft_noise_sigma(key, 0.8), args.seed)
     # the chain runs the streaming kernel: bf16 up to 8 positions (above, the
     # per-linear tile kernel is faster), FP8 weights up to 16 (its only kernel)
@@ -899,6 +924,7 @@ def main():
             "vocab": wl.V,
             "graph": not args.no_graph,
             "gemm_launch": "chain" if use_chain else "per-linear",
+            "split_linears": 0 if use_chain else wl.split_linears(sv),
             "lm_head": ("in spec_verify, softmax statistics fused into its epilogue" if fused
                         else "last linear of the GEMM phase"),
             "weights": "fp8_e4m3 + fp32 row scale" if args.w8 else "bf16",
@@ -922,8 +948,11 @@ def main():
             "kernel": (("gemm_stream FP8-weight chain" if args.w8 else "gemm_stream chain")
                        + (" (all stack linears in one launch)" if fused else
                           " (all stack linears + lm-head in one launch)") if use_chain
-                       else "per-linear spec_verify_gemm launches (stack linears"
-                       + ("" if fused else " + lm-head") + ")"),
+                       else "per-linear " + ("spec_verify_gemm_w8" if args.w8 else
+                                             "spec_verify_gemm_ws" if wl.split else
+                                             "spec_verify_gemm")
+                       + " calls (stack linears" + ("" if fused else " + lm-head")
+                       + "; a call with a split reduction runs two kernels)"),
             "traffic": traffic,
             "hbm_gbs": achieved,
             "hbm_frac": achieved / HBM_PEAK_GBS,

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 6
+#define SPEC_ABI_VERSION 7
 
 /* Status codes. */
 #define SPEC_OK 0
@@ -94,6 +94,44 @@ const char* spec_last_error(void);
  */
 int spec_verify_gemm(const uint16_t* x, const uint16_t* w, void* y, int y_dtype,
                      int M, int d_in, int d_out, void* stream);
+
+/*
+ * spec_verify_gemm_workspace_bytes -- device workspace spec_verify_gemm_ws
+ * needs for this shape, or 0 when it does not split the reduction there (or
+ * the sizes are out of range). Depends on the shape only, not on the device;
+ * no device call.
+ */
+size_t spec_verify_gemm_workspace_bytes(int M, int d_in, int d_out);
+
+/*
+ * spec_verify_gemm_ws -- spec_verify_gemm with the reduction over d_in
+ * split across workgroups where a time model fitted on MI355X predicts
+ * that to be faster: the same product y = x . w^T as spec_verify_gemm
+ * ("What Actually Happens During Speculative Decoding in LLMs": the
+ * weights are read once for all M positions), for shapes whose tiles alone
+ * would leave compute units idle over a long reduction (a down projection,
+ * d_in = 14336 into 4096, at M = 5 to 1280; measured 0.64 to 1.00 of the
+ * unsplit time on the Llama-3.1-8B and 70B linears where it splits).
+ *
+ *   x, w, y, y_dtype, M, d_in, d_out  as for spec_verify_gemm.
+ *   workspace        device memory of at least
+ *                    spec_verify_gemm_workspace_bytes(M, d_in, d_out) bytes,
+ *                    16-byte aligned, owned by the caller; may be NULL when
+ *                    that size is 0. Overwritten: S fp32 partial outputs
+ *                    [S][M][d_out], S the number of splits.
+ *   workspace_bytes  its size in bytes.
+ * When the size is 0 the call is exactly spec_verify_gemm. Otherwise two
+ * kernels run on `stream`: the tile kernel writes each split's fp32 partial
+ * sums, and a second kernel adds them in split order and rounds once, so
+ * the result is deterministic (bitwise equal across launches), though its
+ * fp32 rounding differs from spec_verify_gemm's single accumulator. Calls
+ * sharing one workspace must be ordered on one stream.
+ * Errors: as spec_verify_gemm; SPEC_ERR_WORKSPACE (before any device call)
+ * if the workspace is NULL, smaller than needed or misaligned.
+ */
+int spec_verify_gemm_ws(const uint16_t* x, const uint16_t* w, void* y, int y_dtype,
+                        int M, int d_in, int d_out, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /*
  * spec_linear -- one linear of a chain (see spec_chain_prepare).

@@ -48,6 +48,8 @@ SIGNATURES = {
     "spec_status_string": (ctypes.c_char_p, [_i]),
     "spec_last_error": (ctypes.c_char_p, []),
     "spec_verify_gemm": (_i, [_p, _p, _p, _i, _i, _i, _i, _p]),
+    "spec_verify_gemm_workspace_bytes": (_z, [_i, _i, _i]),
+    "spec_verify_gemm_ws": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _z, _p]),
     "spec_softmax": (_i, [_p, _i, _i, _p, _p, _p, _p]),
     "spec_accept_scan": (_i, [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p]),
     "spec_residual_sample": (_i, [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p]),
@@ -136,10 +138,7 @@ def _need(t, dtype, name, ndim=None):
     return t
 
 
-def verify_gemm(x, w, out=None, out_dtype=None):
-    """y[M][d_out] = x[M][d_in] . w[d_out][d_in]^T (bf16 in, fp32 accumulate).
-
-    out_dtype: torch.float32 (default) or torch.bfloat16."""
+def _gemm_out(x, w, out, out_dtype):
     torch = _torch()
     _need(x, torch.bfloat16, "x", 2)
     _need(w, torch.bfloat16, "w", 2)
@@ -155,7 +154,39 @@ def verify_gemm(x, w, out=None, out_dtype=None):
     code = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16}.get(out.dtype)
     if code is None:
         raise TypeError("out must be float32 or bfloat16")
+    return out, code, M, d_in, d_out
+
+
+def verify_gemm(x, w, out=None, out_dtype=None):
+    """y[M][d_out] = x[M][d_in] . w[d_out][d_in]^T (bf16 in, fp32 accumulate).
+
+    out_dtype: torch.float32 (default) or torch.bfloat16."""
+    out, code, M, d_in, d_out = _gemm_out(x, w, out, out_dtype)
     check(lib.spec_verify_gemm(_ptr(x), _ptr(w), _ptr(out), code, M, d_in, d_out, _stream()))
+    return out
+
+
+def gemm_workspace_bytes(M, d_in, d_out):
+    """Workspace bytes verify_gemm_ws needs for this shape (0: none)."""
+    return lib.spec_verify_gemm_workspace_bytes(M, d_in, d_out)
+
+
+def verify_gemm_ws(x, w, out=None, out_dtype=None, workspace=None):
+    """verify_gemm with the reduction split over workgroups where that is
+    faster; `workspace` is a device tensor of at least
+    gemm_workspace_bytes(M, d_in, d_out) bytes (allocated here if None)."""
+    torch = _torch()
+    out, code, M, d_in, d_out = _gemm_out(x, w, out, out_dtype)
+    if workspace is None:
+        need = gemm_workspace_bytes(M, d_in, d_out)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    n = 0
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+            raise TypeError("workspace must be a device tensor")
+        n = workspace.numel() * workspace.element_size()
+    check(lib.spec_verify_gemm_ws(_ptr(x), _ptr(w), _ptr(out), code, M, d_in, d_out,
+                                  _ptr(workspace), n, _stream()))
     return out
 
 

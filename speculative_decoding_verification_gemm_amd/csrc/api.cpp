@@ -304,6 +304,44 @@ int spec_verify_gemm(const uint16_t* x, const uint16_t* w, void* y, int y_dtype,
                   static_cast<hipStream_t>(stream));
 }
 
+// The tile path's reduction split applies where the per-linear call would
+// run the pipelined tile kernel (d_in a multiple of 64, no streaming).
+size_t split_bytes(int M, int d_in, int d_out) {
+  if (M < 1 || M > kMaxM || d_in < 64 || d_in > kMaxDin || d_out < 1 || d_out > kMaxDout)
+    return 0;
+  if (d_in % 64 != 0 || use_stream(M, d_in, d_out)) return 0;
+  return specv::gemm_split_workspace_bytes(M, d_in, d_out);
+}
+
+size_t spec_verify_gemm_workspace_bytes(int M, int d_in, int d_out) {
+  return split_bytes(M, d_in, d_out);
+}
+
+int spec_verify_gemm_ws(const uint16_t* x, const uint16_t* w, void* y, int y_dtype, int M,
+                        int d_in, int d_out, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  clear_error();
+  int rc = check_gemm_args(x, w, y, y_dtype, M, d_in, d_out);
+  if (rc != SPEC_OK) return rc;
+  const size_t need = split_bytes(M, d_in, d_out);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SPEC_ERR_WORKSPACE,
+                "workspace of %zu bytes (%s) is smaller than the %zu bytes M=%d, d_in=%d, "
+                "d_out=%d needs",
+                workspace_bytes, workspace ? "non-null" : "null", need, M, d_in, d_out);
+  if (need > 0 && !aligned(workspace, 16))
+    return fail(SPEC_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+  int cus = 0;
+  if ((rc = check_device(&cus)) != SPEC_OK) return rc;
+  if (need == 0)
+    return run_gemm(x, w, y, y_dtype == SPEC_BF16, M, d_in, d_out, cus,
+                    static_cast<hipStream_t>(stream));
+  return launched(specv::launch_gemm_split(x, w, y, y_dtype == SPEC_BF16, M, d_in, d_out,
+                                           workspace, workspace_bytes,
+                                           static_cast<hipStream_t>(stream)),
+                  "spec_verify_gemm_ws");
+}
+
 size_t spec_chain_workspace_bytes(int n) {
   if (n < 1 || n > kMaxChain) return 0;
   return chain_bytes(n);

@@ -9,6 +9,7 @@
 // weight-streaming kernel in gemm_stream.hip instead.
 
 #include <stdlib.h>
+#include <string.h>
 
 #include "common.h"
 #include "internal.h"
@@ -294,20 +295,26 @@ template <int BM, int BN, int WM, int S, int BK, int NW, int KS, int MF, bool W8
           bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
     const uint16_t* __restrict__ X, const void* __restrict__ W, const float* __restrict__ WS,
-    void* __restrict__ Y, int M, int N, int K, int n_tiles, int per_xcd) {
+    void* __restrict__ Y, int M, int N, int K, int n_tiles, int per_xcd, int sk) {
   using C = TileCfg<BM, BN, WM, S, BK, NW, KS, MF, W8, WL>;
   typedef float facc __attribute__((ext_vector_type(C::NACC)));
   extern __shared__ u32x4 lds[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // XCD-grouped tile order: workgroup bid runs on XCD bid % 8
-  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (t >= n_tiles) return;
+  // Work item (tile t, reduction split s): with sk > 1 the K stages of a
+  // tile are split over sk workgroups, each storing an fp32 partial tile
+  // (to Y, then a workspace of sk x M x N floats) that the split-sum kernel
+  // adds up in split order.
+  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (item >= n_tiles * sk) return;
+  const int t = item / sk, split = item - t * sk;
   const int MT = (M + BM - 1) / BM;
   const int tm = t % MT, tn = t / MT;
   const int m0 = tm * BM, n0 = tn * BN;
   const int kg = wave / C::NWG, wr = wave % C::NWG;  // k-group, wave inside it
   const int wm = wr / C::WN, wn = wr % C::WN;
-  const int n_k = K / BK;
+  const int k_begin = split * (K / BK) / sk, k_end = (split + 1) * (K / BK) / sk;
+  const int n_k = k_end - k_begin;      // this work item's k-tiles, from k_begin
   const int n_j = (n_k + KS - 1) / KS;  // ring steps; group kg's step st is k-tile st * KS + kg
 
   // This lane's source address for each of its L load instructions. Load
@@ -335,7 +342,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
   }
   auto issue = [&](int st) __attribute__((always_inline)) {
     // k-tiles past the end reload the last one into a slot nobody reads
-    const int kc = min(st * KS + kg, n_k - 1);
+    const int kc = k_begin + min(st * KS + kg, n_k - 1);
     const int slot = kg * S + st % S;
 #pragma unroll
     for (int q = 0; q < C::L; ++q)
@@ -431,6 +438,22 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
   }
   tile_wait_vmcnt<0>();  // the reloads past the end land before the workgroup leaves
 
+  if (sk > 1) {
+    // a partial tile: fp32, unscaled, to split `split` of the workspace
+    float* part = static_cast<float*>(Y) + (size_t)split * M * N;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int col = n0 + out_col(j);
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int e = 0; e < C::NACC; ++e) {
+          const int row = m0 + out_row(i, e);
+          if (row < M && col < N) tile_store<float>(part, (size_t)row * N + col, acc[i][j][e]);
+        }
+    }
+    return;
+  }
   auto store = [&](int row, int col, float v) __attribute__((always_inline)) {
     if (OUT_BF16)
       tile_store<uint16_t>(Y, (size_t)row * N + col, f32_to_bf16_bits(v));
@@ -475,14 +498,40 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
   }
 }
 
+// The sk partial tiles of a split reduction added in split order (fixed, so
+// the result is deterministic), scaled by the row scale for FP8 weights and
+// stored as the output.
+template <bool OUT_BF16, bool W8>
+__global__ __launch_bounds__(256) void gemm_split_sum_kernel(const float* __restrict__ P,
+                                                             const float* __restrict__ WS,
+                                                             void* __restrict__ Y, int M, int N,
+                                                             int sk) {
+  const size_t mn = (size_t)M * N;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= mn) return;
+  float v = P[i];
+  for (int p = 1; p < sk; ++p) v += P[(size_t)p * mn + i];
+  if (W8) v *= tile_scale(WS, (int)(i % N));
+  if (OUT_BF16)
+    tile_store<uint16_t>(Y, i, f32_to_bf16_bits(v));
+  else
+    tile_store<float>(Y, i, v);
+}
+
+// sk > 1: the reduction is split over sk workgroups per tile (whole k-tiles,
+// at least one each) whose fp32 partial tiles go to `partials` (sk x M x N
+// floats), then added up by the split-sum kernel; one k-group per workgroup.
 template <int BM, int BN, int WM, int S, int BK, int NW = 8, int KS = 1, int MF = 16,
           bool W8 = false, bool WL = false>
 static hipError_t launch_tile_t(const uint16_t* x, const void* w, const float* ws, void* y,
-                                bool out_bf16, int M, int K, int N, hipStream_t s) {
+                                bool out_bf16, int M, int K, int N, hipStream_t s,
+                                float* partials = nullptr, int sk = 1) {
   using C = TileCfg<BM, BN, WM, S, BK, NW, KS, MF, W8, WL>;
   if (K % BK != 0) return hipErrorInvalidValue;  // whole stages only
+  if (sk < 1 || (sk > 1 && (KS != 1 || partials == nullptr || K / BK < sk)))
+    return hipErrorInvalidValue;
   const int n_tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int per_xcd = (n_tiles + 7) / 8;
+  const int per_xcd = (n_tiles * sk + 7) / 8;
   const dim3 grid(8 * per_xcd);
   static const hipError_t a1 = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, WL, true>),
@@ -492,12 +541,27 @@ static hipError_t launch_tile_t(const uint16_t* x, const void* w, const float* w
       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
+  if (sk > 1) {
+    hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, WL, false>), grid,
+                       dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, partials, M, N, K, n_tiles,
+                       per_xcd, sk);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 sgrid((unsigned)(((size_t)M * N + 255) / 256));
+    if (out_bf16)
+      hipLaunchKernelGGL((gemm_split_sum_kernel<true, W8>), sgrid, dim3(256), 0, s, partials, ws, y,
+                         M, N, sk);
+    else
+      hipLaunchKernelGGL((gemm_split_sum_kernel<false, W8>), sgrid, dim3(256), 0, s, partials, ws,
+                         y, M, N, sk);
+    return hipGetLastError();
+  }
   if (out_bf16)
     hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, WL, true>), grid,
-                       dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, y, M, N, K, n_tiles, per_xcd);
+                       dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, y, M, N, K, n_tiles, per_xcd, 1);
   else
     hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, WL, false>), grid,
-                       dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, y, M, N, K, n_tiles, per_xcd);
+                       dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, y, M, N, K, n_tiles, per_xcd, 1);
   return hipGetLastError();
 }
 
@@ -647,6 +711,111 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
   if (M <= 32) return launch_mfma_t<32, 64, 1>(x, w, y, out_bf16, M, K, N, s);
   if (M <= 128) return launch_mfma_t<64, 64, 2>(x, w, y, out_bf16, M, K, N, s);
   return launch_mfma_t<128, 128, 2>(x, w, y, out_bf16, M, K, N, s);
+}
+
+// Reduction split over workgroups (spec_verify_gemm_ws). When few tiles of
+// a large shape would leave CUs idle (the down projection at M = 320 has
+// 192 tiles of 128x64 for 256 CUs and K = 14336), each tile's K stages are
+// split over sk workgroups writing fp32 partial tiles to a caller
+// workspace, and a second kernel adds them in split order.
+static const int kSplitShapes[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128},
+                                      {64, 128},  {320, 128}, {320, 256}, {128, 64},
+                                      {64, 64},   {32, 64}};
+constexpr int kSplitShapeCount = sizeof(kSplitShapes) / sizeof(kSplitShapes[0]);
+constexpr int kPlanCUs = 256;  // plans depend on the shape only, not the device
+
+static hipError_t launch_split_shape(int shape, const uint16_t* x, const uint16_t* w, void* y,
+                                     bool o, int M, int K, int N, float* part, int sk,
+                                     hipStream_t s) {
+  switch (shape) {
+    case 0: return launch_tile_t<256, 256, 4, 2, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s, part, sk);
+    case 1: return launch_tile_t<256, 128, 4, 3, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s, part, sk);
+    case 2: return launch_tile_t<128, 256, 2, 3, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s, part, sk);
+    case 3: return launch_tile_t<128, 128, 2, 4, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s, part, sk);
+    case 4: return launch_tile_t<64, 128, 2, 4, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s, part, sk);
+    case 5: return launch_tile_t<320, 128, 2, 2, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s, part, sk);
+    case 6: return launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s, part, sk);
+    case 7: return launch_tile_t<128, 64, 4, 4, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s, part, sk);
+    case 8: return launch_tile_t<64, 64, 2, 4, 64>(x, w, nullptr, y, o, M, K, N, s, part, sk);
+    case 9: return launch_tile_t<32, 64, 1, 4, 64, 4>(x, w, nullptr, y, o, M, K, N, s, part, sk);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+struct SplitPlan {
+  int shape, sk;  // sk == 1: no split (the per-linear kernel's own pick)
+};
+
+// Time of one launch in microseconds: the tile model's term (scaled by a
+// fit to measured launches) plus, for a split, a fixed cost and the fp32
+// partial tiles written and read back by the split-sum kernel. The fit is to
+// 250 launches on MI355X (the Llama-3.1-8B linears except the lm-head at
+// M = 20, 80, 320, 1280, every split of the shapes below from 2 to 16):
+// rms error 12 %; on each of the 16 linears the plan it picks is the fastest
+// measured or within 5.2 % of it. Checked on the Llama-3.1-8B and 70B
+// linears at M = 5 to 1280: where it splits, the split runs 0.64 to 1.00 of
+// the unsplit time.
+static double tile_us(int M, int N, int K, int bm, int bn, int sk, int cus) {
+  const double a = 2.5e-5, b = 1.88e-7;
+  const long tiles = (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  const long rounds = (tiles * sk + cus - 1) / cus;
+  const double t = 0.962 * rounds * (a * (bm + bn) + b * (double)bm * bn) * K / sk + 4.15;
+  if (sk == 1) return t;
+  return t + 2.65 + 0.19e-6 * ((double)sk * M * N * 8 + (double)M * N * 2);
+}
+
+static SplitPlan split_plan(int M, int N, int K) {
+  SplitPlan p{0, 1};
+#if defined(SPECV_DIAGNOSTICS)
+  if (const char* f = getenv("SPECV_SPLITK")) {  // "shape,sk"
+    p.shape = max(0, min(atoi(f), kSplitShapeCount - 1));
+    if (const char* c = strchr(f, ',')) p.sk = max(1, atoi(c + 1));
+    return p;
+  }
+#endif
+  constexpr int n_shapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
+  const int base = pick_tile(M, N, kPlanCUs, kTileShapes, n_shapes);
+  const long base_tiles = (long)((M + kTileShapes[base][0] - 1) / kTileShapes[base][0]) *
+                          ((N + kTileShapes[base][1] - 1) / kTileShapes[base][1]);
+  // A split must beat the unsplit pick by 5 % of the model's time, or by
+  // 20 % where that pick runs in k-groups (one round of the small 64x64 to
+  // 32x16 tiles), which the model does not credit: measured, such picks
+  // beat the splits the model put 10 to 18 % ahead of them (the 8192x8192
+  // and 28672x8192 linears at M = 10 to 80).
+  const bool k_groups = base_tiles <= kPlanCUs && base >= 6 && base <= 9;
+  double best = (k_groups ? 0.80 : 0.95) *
+                tile_us(M, N, K, kTileShapes[base][0], kTileShapes[base][1], 1, kPlanCUs);
+  for (int i = 0; i < kSplitShapeCount; ++i) {
+    const long tiles =
+        (long)((M + kSplitShapes[i][0] - 1) / kSplitShapes[i][0]) *
+        ((N + kSplitShapes[i][1] - 1) / kSplitShapes[i][1]);
+    // at least two k-tiles per split, at most four rounds of work items
+    for (int sk = 2; sk <= 16 && 2 * sk <= K / 64 && tiles * sk <= 4 * kPlanCUs; ++sk) {
+      const double t = tile_us(M, N, K, kSplitShapes[i][0], kSplitShapes[i][1], sk, kPlanCUs);
+      if (t < best) {
+        best = t;
+        p = SplitPlan{i, sk};
+      }
+    }
+  }
+  return p;
+}
+
+size_t gemm_split_workspace_bytes(int M, int K, int N) {
+  if (K % kTileKAlign != 0) return 0;
+  const SplitPlan p = split_plan(M, N, K);
+  return p.sk > 1 ? (size_t)p.sk * M * N * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_split(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
+                             int K, int N, void* workspace, size_t workspace_bytes, hipStream_t s) {
+  const SplitPlan p = split_plan(M, N, K);
+  if (K % kTileKAlign != 0 || p.sk <= 1) return launch_gemm_mfma(x, w, y, out_bf16, M, K, N, s);
+  if (workspace == nullptr || workspace_bytes < (size_t)p.sk * M * N * sizeof(float) ||
+      K / 64 < p.sk)
+    return hipErrorInvalidValue;
+  return launch_split_shape(p.shape, x, w, y, out_bf16, M, K, N, static_cast<float*>(workspace),
+                            p.sk, s);
 }
 
 // FP8 E4M3 weights with per-row scales. The tile shapes are those whose

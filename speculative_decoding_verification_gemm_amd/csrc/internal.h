@@ -96,6 +96,12 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
                             int K, int N, hipStream_t s);
 // FP8 E4M3 weights with per-row scales on the tile kernel (K a multiple of
 // 64; any M, used above kMaxStreamM).
+// The per-linear tile kernel with its reduction split over workgroups into a
+// caller workspace of gemm_split_workspace_bytes(M, K, N) bytes (0: the
+// plan does not split, and launch_gemm_split runs launch_gemm_mfma).
+size_t gemm_split_workspace_bytes(int M, int K, int N);
+hipError_t launch_gemm_split(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
+                             int K, int N, void* workspace, size_t workspace_bytes, hipStream_t s);
 hipError_t launch_gemm_tile_w8(const uint16_t* x, const uint8_t* w, const float* w_scale, void* y,
                                bool out_bf16, int M, int K, int N, hipStream_t s);
 

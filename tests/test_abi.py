@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 25
     for n in names:
         assert hasattr(sv.lib, n), n
 
@@ -33,7 +33,7 @@ def test_binding_covers_exactly_the_header(sv):
 
 
 def test_version_and_status_strings(sv):
-    assert sv.abi_version() == 6
+    assert sv.abi_version() == 7
     for code, name in [(0, b"SPEC_OK"), (-1, b"SPEC_ERR_INVALID_ARGUMENT"),
                        (-2, b"SPEC_ERR_ALIGNMENT"), (-3, b"SPEC_ERR_UNSUPPORTED"),
                        (-4, b"SPEC_ERR_WORKSPACE"), (-5, b"SPEC_ERR_HIP")]:
@@ -63,6 +63,41 @@ GEMM_BAD = [
 def test_gemm_rejects(sv, args, code):
     assert sv.lib.spec_verify_gemm(*args, None) == code
     assert sv.lib.spec_last_error()
+
+
+@pytest.mark.parametrize("args,code", GEMM_BAD)
+def test_gemm_ws_rejects_as_gemm(sv, args, code):
+    assert sv.lib.spec_verify_gemm_ws(*args, A, 1 << 30, None) == code
+    assert sv.lib.spec_last_error()
+
+
+def test_gemm_workspace_bytes(sv):
+    f = sv.lib.spec_verify_gemm_workspace_bytes
+    # out of range, or d_in not a multiple of 64: no split
+    assert f(0, 14336, 4096) == 0 and f(65537, 14336, 4096) == 0
+    assert f(320, 14336 + 8, 4096) == 0 and f(320, 14336, 0) == 0
+    # the streaming kernel's shapes (M <= 8 on 2^26 weights or more): no split
+    assert f(5, 8192, 57344) == 0
+    # the 14336 -> 4096 down projection splits at every batch of the sweep,
+    # into whole fp32 copies of the output, at most 16
+    for M in (20, 80, 320, 1280):
+        n = f(M, 14336, 4096)
+        assert n > 0 and n % (M * 4096 * 4) == 0 and 2 <= n // (M * 4096 * 4) <= 16
+    # the gate/up projection (d_in 4096 into 28672) never does
+    for M in (20, 80, 320, 1280):
+        assert f(M, 4096, 28672) == 0
+
+
+def test_gemm_ws_rejects_workspace(sv):
+    f = sv.lib.spec_verify_gemm_ws
+    need = sv.lib.spec_verify_gemm_workspace_bytes(320, 14336, 4096)
+    assert need > 0
+    # checked before any device call
+    assert f(A, A, A, 1, 320, 14336, 4096, None, need, None) == -4
+    assert f(A, A, A, 1, 320, 14336, 4096, A, need - 1, None) == -4
+    assert b"smaller" in sv.lib.spec_last_error()
+    assert f(A, A, A, 1, 320, 14336, 4096, A + 8, need, None) == -4
+    assert b"aligned" in sv.lib.spec_last_error()
 
 
 def test_softmax_rejects(sv):

@@ -1,0 +1,147 @@
+"""GPU parity of spec_verify_gemm_ws (the tile kernel with its reduction
+split over workgroups, fp32 partial outputs added by a second kernel)
+against the fp64 oracle.
+
+Tolerances as for spec_verify_gemm: max |y - y_ref| / max(|y_ref|, rms of
+the reference row) <= 2e-2 for bf16 outputs and 1e-3 for fp32 outputs (fp32
+accumulation in every split, then a sum of at most 16 fp32 partials); a
+split that skipped or repeated its k-tiles would miss 1e-3 by far.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+TOL_F32 = 1e-3
+
+
+def rel_err(y, ref):
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    return float(np.max(np.abs(y - ref) / np.maximum(np.abs(ref), rms)))
+
+
+def check(y, ref, out_dtype, what):
+    import torch
+    e = rel_err(y, ref)
+    print(f"{what}: rel err {e:.3e}", flush=True)
+    assert e <= TOL, what
+    if out_dtype == torch.float32:
+        assert e <= TOL_F32, what
+
+
+def splits(sv, M, d_in, d_out):
+    """Number of splits the plan takes (0: none)."""
+    return sv.gemm_workspace_bytes(M, d_in, d_out) // (M * d_out * 4)
+
+
+# Shapes the plan splits, one per split tile shape reachable at sizes the
+# oracle finishes in seconds: ragged M and d_out tails, and k-tile counts
+# (d_in / 64) that the splits do not divide evenly (94 over 16, 128 over 15,
+# 94 over 10, 128 over 10) as well as ones they do (80 over 16).
+SMALL = [
+    (9, 5120, 300),      # 32x64 tiles, 16 splits
+    (9, 6016, 300),      # 32x64, 16 splits of 94 k-tiles
+    (37, 6016, 777),     # 64x64, 16 splits
+    (37, 8192, 2050),    # 64x128, 15 splits
+    (77, 6016, 3000),    # 128x128, 10 splits
+    (517, 8192, 300),    # 128x64, 10 splits
+]
+
+
+@pytest.mark.parametrize("M,d_in,d_out", SMALL)
+def test_split_parity(sv, dev, M, d_in, d_out):
+    import torch
+    from synth import device as sd
+    assert splits(sv, M, d_in, d_out) >= 2, (M, d_in, d_out)
+    xb, wb = synth.linear_inputs(500 + M, f"split{d_in}.{d_out}", M, d_in, d_out)
+    ref = oracle.linear(xb, wb)
+    x, w = sd.from_bits(xb, dev), sd.from_bits(wb, dev)
+    for od in (torch.float32, torch.bfloat16):
+        y = sv.verify_gemm_ws(x, w, out_dtype=od)
+        torch.cuda.synchronize()
+        check(y.float().cpu().numpy().astype(np.float64), ref, od,
+              f"split M={M} {d_in}->{d_out} {od}")
+
+
+def test_split_workspace_reuse_and_determinism(sv, dev):
+    """One workspace serves calls of different shapes in stream order; a
+    repeated call gives bitwise equal outputs (the partials are added in
+    split order)."""
+    import torch
+    from synth import device as sd
+    shapes = [(77, 6016, 3000), (37, 8192, 2050), (77, 6016, 3000)]
+    need = max(sv.gemm_workspace_bytes(*s) for s in shapes)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    outs = []
+    for i, (M, d_in, d_out) in enumerate(shapes):
+        x = sd.normal_bf16((M, d_in), 1.0, 10 + M, dev)
+        w = sd.normal_bf16((d_out, d_in), synth.WEIGHT_STD, 20 + d_in, dev)
+        outs.append(sv.verify_gemm_ws(x, w, out_dtype=torch.float32, workspace=ws))
+        if i == 1:
+            xb, wb = sd.to_bits(x), sd.to_bits(w)
+            torch.cuda.synchronize()
+            check(outs[1].cpu().numpy().astype(np.float64), oracle.linear(xb, wb),
+                  torch.float32, "reused workspace 37x8192->2050")
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("M,d_in,d_out", [(5, 4096, 4096), (320, 4096, 28672),
+                                           (5, 8192, 57344), (40, 1032, 777)])
+def test_no_split_is_spec_verify_gemm(sv, dev, M, d_in, d_out):
+    """Where the plan does not split (workspace size 0) the call is
+    spec_verify_gemm: bitwise equal outputs, no workspace needed (the tile
+    kernel, the streaming kernel, and d_in not a multiple of 64)."""
+    import torch
+    from synth import device as sd
+    assert sv.gemm_workspace_bytes(M, d_in, d_out) == 0
+    x = sd.normal_bf16((M, d_in), 1.0, 30 + M, dev)
+    w = sd.normal_bf16((d_out, d_in), synth.WEIGHT_STD, 40 + d_in, dev)
+    a = sv.verify_gemm(x, w, out_dtype=torch.bfloat16)
+    b = sv.verify_gemm_ws(x, w, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def sampled_full_size(sv, dev, M, d_in, d_out, seed, out_dtype, n_cols=48):
+    """Full-size linear through spec_verify_gemm_ws; the oracle checks a
+    sample of output columns (first and last 8 plus random ones)."""
+    import torch
+    from synth import device as sd
+    w = sd.normal_bf16((d_out, d_in), synth.WEIGHT_STD, seed, dev)
+    x = sd.normal_bf16((M, d_in), 1.0, seed + 1, dev)
+    y = sv.verify_gemm_ws(x, w, out_dtype=out_dtype)
+    rng = np.random.default_rng(seed)
+    cols = np.unique(np.concatenate([np.arange(8), np.arange(d_out - 8, d_out),
+                                     rng.integers(0, d_out, n_cols)]))
+    idx = torch.from_numpy(cols).to(dev)
+    w_rows = sd.to_bits(w.index_select(0, idx))
+    x_bits = sd.to_bits(x)
+    y_s = y.index_select(1, idx).float().cpu().numpy().astype(np.float64)
+    del w, y
+    torch.cuda.empty_cache()
+    return y_s, oracle.linear(x_bits, w_rows)
+
+
+# Full-size linears the plan splits: the Llama-3.1-8B down projection at
+# every swept M (32x64, 128x128, 256x128, 320x128 and 320x256 tiles), a
+# ragged 320-row tile (M = 301) and 256x256 tiles (M = 1000), the O
+# projection at M = 1280 (two splits), and the Llama-3.1-70B down
+# projection (128x256 and 256x256 tiles).
+FULL = [(5, 14336, 4096), (20, 14336, 4096), (80, 14336, 4096), (160, 14336, 4096),
+        (301, 14336, 4096), (320, 14336, 4096), (1000, 14336, 4096), (1280, 14336, 4096),
+        (1280, 4096, 4096), (80, 28672, 8192), (160, 28672, 8192), (640, 8192, 10240)]
+
+
+@pytest.mark.parametrize("M,d_in,d_out", FULL)
+def test_split_full_size(sv, dev, M, d_in, d_out):
+    import torch
+    assert splits(sv, M, d_in, d_out) >= 2, (M, d_in, d_out)
+    for od in (torch.bfloat16, torch.float32):
+        y, ref = sampled_full_size(sv, dev, M, d_in, d_out, 7 * M + d_in, od)
+        check(y, ref, od, f"split full M={M} {d_in}->{d_out} {od}")
