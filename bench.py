@@ -16,7 +16,8 @@ Each phase is captured once in a HIP graph; a timed step replays the two
 graphs back to back with HIP events between them on the same stream.
 With --w8 every linear (stack and lm-head) holds FP8 E4M3 weights with a
 per-row scale (weight-only 8-bit storage, bf16 activations and products):
-one chain launch up to M = 16, per-linear MFMA tile launches above. Prints one JSON line: the throughput in verified positions per second, the
+one chain launch up to M = 16, per-linear MFMA tile launches
+(spec_verify_gemm_w8_ws) above. Prints one JSON line: the throughput in verified positions per second, the
 per-phase times, the roofline of the GEMM phase (algorithmic bytes over its
 measured time, against the 8 TB/s HBM peak; MFMA peak where the FLOPs
 dominate) and the fp64 oracle's rate on the host cores.
@@ -64,8 +65,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-split", action="store_true",
-                    help="per-linear launches: spec_verify_gemm (no split reduction) "
-                         "instead of spec_verify_gemm_ws")
+                    help="per-linear launches: spec_verify_gemm / _w8 (no split "
+                         "reduction) instead of spec_verify_gemm_ws / _w8_ws")
     ap.add_argument("--no-chain", action="store_true",
                     help="one spec_verify_gemm launch per linear instead of one chain launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -212,25 +213,30 @@ class Workload:
                 lin.append((self.hidden, self.lm_head, self.target_logits.view(self.M, self.V)))
         self.chain = sv.Chain(lin, self.dev)
 
+    def ws_bytes(self, sv, w):
+        f = sv.gemm_w8_workspace_bytes if self.w8 else sv.gemm_workspace_bytes
+        return f(self.M, w.shape[1], w.shape[0])
+
     def split_linears(self, sv):
-        """Stack linears that spec_verify_gemm_ws runs with a split reduction."""
-        if self.w8 or not self.split:
+        """Stack linears that spec_verify_gemm_ws (_w8_ws) runs with a split
+        reduction."""
+        if not self.split:
             return 0
-        return sum(sv.gemm_workspace_bytes(self.M, w.shape[1], w.shape[0]) > 0
-                   for _, _, w, _ in self.linears)
+        return sum(self.ws_bytes(sv, w) > 0 for _, _, w, _ in self.linears)
 
     def gemm_phase(self, sv):
         import torch
         if getattr(self, "chain", None) is not None:
             self.chain.run()
             return
-        if not self.w8 and self.split and getattr(self, "gemm_ws", None) is None:
+        if self.split and getattr(self, "gemm_ws", None) is None:
             # one workspace for every linear: the calls run in stream order
-            need = max(sv.gemm_workspace_bytes(self.M, w.shape[1], w.shape[0])
-                       for _, _, w, _ in self.linears)
+            need = max(self.ws_bytes(sv, w) for _, _, w, _ in self.linears)
             self.gemm_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.dev)
         for (_, x, w, y), sc in zip(self.linears, self.scales):
-            if self.w8:
+            if self.w8 and self.split:
+                sv.verify_gemm_w8_ws(x, w, sc, out=y, workspace=self.gemm_ws)
+            elif self.w8:
                 sv.verify_gemm_w8(x, w, sc, out=y)
             elif self.split:
                 sv.verify_gemm_ws(x, w, out=y, workspace=self.gemm_ws)
@@ -949,8 +955,8 @@ def main():
                        + (" (all stack linears in one launch)" if fused else
                           " (all stack linears + lm-head in one launch)") if use_chain
                        else "per-linear " + ("spec_verify_gemm_w8" if args.w8 else
-                                             "spec_verify_gemm_ws" if wl.split else
                                              "spec_verify_gemm")
+                       + ("_ws" if wl.split else "")
                        + " calls (stack linears" + ("" if fused else " + lm-head")
                        + "; a call with a split reduction runs two kernels)"),
             "traffic": traffic,

@@ -233,6 +233,27 @@ int spec_verify_gemm_chain(int n, int M, void* workspace, void* stream);
 int spec_verify_gemm_w8(const uint16_t* x, const uint8_t* w, const float* w_scale, void* y,
                         int y_dtype, int M, int d_in, int d_out, void* stream);
 
+/*
+ * spec_verify_gemm_w8_workspace_bytes -- as spec_verify_gemm_workspace_bytes
+ * for spec_verify_gemm_w8_ws (0: no split; always 0 at M <= 16).
+ */
+size_t spec_verify_gemm_w8_workspace_bytes(int M, int d_in, int d_out);
+
+/*
+ * spec_verify_gemm_w8_ws -- spec_verify_gemm_w8 with the reduction split
+ * over workgroups where a time model fitted on MI355X predicts that to be
+ * faster (M above 16; measured 0.42 to 0.99 of the unsplit time on the
+ * Llama-3.1-8B and 70B linears where it splits, the down projections most).
+ * Arguments as spec_verify_gemm_w8, plus `workspace` / `workspace_bytes`
+ * as for spec_verify_gemm_ws. The fp32 partial sums are unscaled; the
+ * second kernel adds them in split order, multiplies by w_scale[n] and
+ * rounds once. Deterministic; errors as spec_verify_gemm_w8, and
+ * SPEC_ERR_WORKSPACE as spec_verify_gemm_ws.
+ */
+int spec_verify_gemm_w8_ws(const uint16_t* x, const uint8_t* w, const float* w_scale, void* y,
+                           int y_dtype, int M, int d_in, int d_out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* One linear of an FP8-weight chain: spec_linear with w_scale. */
 typedef struct spec_linear_w8 {
   const uint16_t* x;

@@ -58,6 +58,8 @@ SIGNATURES = {
     "spec_chain_prepare": (_i, [_p, _i, _i, _p, _z]),
     "spec_verify_gemm_chain": (_i, [_i, _i, _p, _p]),
     "spec_verify_gemm_w8": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _p]),
+    "spec_verify_gemm_w8_workspace_bytes": (_z, [_i, _i, _i]),
+    "spec_verify_gemm_w8_ws": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _p, _z, _p]),
     "spec_chain_prepare_w8": (_i, [_p, _i, _i, _p, _z]),
     "spec_verify_gemm_chain_w8": (_i, [_i, _i, _p, _p]),
     "spec_verify_attention_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i]),
@@ -175,26 +177,14 @@ def verify_gemm_ws(x, w, out=None, out_dtype=None, workspace=None):
     """verify_gemm with the reduction split over workgroups where that is
     faster; `workspace` is a device tensor of at least
     gemm_workspace_bytes(M, d_in, d_out) bytes (allocated here if None)."""
-    torch = _torch()
     out, code, M, d_in, d_out = _gemm_out(x, w, out, out_dtype)
-    if workspace is None:
-        need = gemm_workspace_bytes(M, d_in, d_out)
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
-    n = 0
-    if workspace is not None:
-        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
-            raise TypeError("workspace must be a device tensor")
-        n = workspace.numel() * workspace.element_size()
+    workspace, n = _workspace(workspace, gemm_workspace_bytes(M, d_in, d_out), x.device)
     check(lib.spec_verify_gemm_ws(_ptr(x), _ptr(w), _ptr(out), code, M, d_in, d_out,
                                   _ptr(workspace), n, _stream()))
     return out
 
 
-def verify_gemm_w8(x, w, w_scale, out=None, out_dtype=None):
-    """y[m][n] = w_scale[n] * sum_k x[m][k] * e4m3(w[n][k]) (weight-only FP8).
-
-    x bf16 [M][d_in]; w uint8 FP8 E4M3 codes [d_out][d_in]; w_scale float32
-    [d_out]; out_dtype torch.float32 (default) or torch.bfloat16."""
+def _gemm_w8_out(x, w, w_scale, out, out_dtype):
     torch = _torch()
     _need(x, torch.bfloat16, "x", 2)
     _need(w, torch.uint8, "w", 2)
@@ -212,8 +202,42 @@ def verify_gemm_w8(x, w, w_scale, out=None, out_dtype=None):
     code = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16}.get(out.dtype)
     if code is None:
         raise TypeError("out must be float32 or bfloat16")
+    return out, code, M, d_in, d_out
+
+
+def verify_gemm_w8(x, w, w_scale, out=None, out_dtype=None):
+    """y[m][n] = w_scale[n] * sum_k x[m][k] * e4m3(w[n][k]) (weight-only FP8).
+
+    x bf16 [M][d_in]; w uint8 FP8 E4M3 codes [d_out][d_in]; w_scale float32
+    [d_out]; out_dtype torch.float32 (default) or torch.bfloat16."""
+    out, code, M, d_in, d_out = _gemm_w8_out(x, w, w_scale, out, out_dtype)
     check(lib.spec_verify_gemm_w8(_ptr(x), _ptr(w), _ptr(w_scale), _ptr(out), code, M, d_in,
                                   d_out, _stream()))
+    return out
+
+
+def gemm_w8_workspace_bytes(M, d_in, d_out):
+    """Workspace bytes verify_gemm_w8_ws needs for this shape (0: none)."""
+    return lib.spec_verify_gemm_w8_workspace_bytes(M, d_in, d_out)
+
+
+def _workspace(workspace, need, dev):
+    torch = _torch()
+    if workspace is None:
+        return (torch.empty(need, dtype=torch.uint8, device=dev) if need else None), need
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise TypeError("workspace must be a device tensor")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def verify_gemm_w8_ws(x, w, w_scale, out=None, out_dtype=None, workspace=None):
+    """verify_gemm_w8 with the reduction split over workgroups where that is
+    faster; `workspace` is a device tensor of at least
+    gemm_w8_workspace_bytes(M, d_in, d_out) bytes (allocated here if None)."""
+    out, code, M, d_in, d_out = _gemm_w8_out(x, w, w_scale, out, out_dtype)
+    workspace, n = _workspace(workspace, gemm_w8_workspace_bytes(M, d_in, d_out), x.device)
+    check(lib.spec_verify_gemm_w8_ws(_ptr(x), _ptr(w), _ptr(w_scale), _ptr(out), code, M, d_in,
+                                     d_out, _ptr(workspace), n, _stream()))
     return out
 
 

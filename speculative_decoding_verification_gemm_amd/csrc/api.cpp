@@ -467,6 +467,42 @@ int spec_verify_gemm_w8(const uint16_t* x, const uint8_t* w, const float* w_scal
                   "spec_verify_gemm_w8");
 }
 
+// FP8 weights: the split applies to the tile kernel (M above the streaming
+// kernel's positions; d_in a multiple of 64 is then required anyway).
+size_t split_bytes_w8(int M, int d_in, int d_out) {
+  if (M <= specv::kMaxStreamM || M > kMaxM || d_in < 64 || d_in > kMaxDin || d_in % 64 != 0 ||
+      d_out < 1 || d_out > kMaxDout)
+    return 0;
+  return specv::gemm_split_workspace_bytes_w8(M, d_in, d_out);
+}
+
+size_t spec_verify_gemm_w8_workspace_bytes(int M, int d_in, int d_out) {
+  return split_bytes_w8(M, d_in, d_out);
+}
+
+int spec_verify_gemm_w8_ws(const uint16_t* x, const uint8_t* w, const float* w_scale, void* y,
+                           int y_dtype, int M, int d_in, int d_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  clear_error();
+  int rc = check_gemm_w8_args(x, w, w_scale, y, y_dtype, M, d_in, d_out);
+  if (rc != SPEC_OK) return rc;
+  const size_t need = split_bytes_w8(M, d_in, d_out);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SPEC_ERR_WORKSPACE,
+                "workspace of %zu bytes (%s) is smaller than the %zu bytes M=%d, d_in=%d, "
+                "d_out=%d needs",
+                workspace_bytes, workspace ? "non-null" : "null", need, M, d_in, d_out);
+  if (need > 0 && !aligned(workspace, 16))
+    return fail(SPEC_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+  if (need == 0) return spec_verify_gemm_w8(x, w, w_scale, y, y_dtype, M, d_in, d_out, stream);
+  int cus = 0;
+  if ((rc = check_device(&cus)) != SPEC_OK) return rc;
+  return launched(specv::launch_gemm_split_w8(x, w, w_scale, y, y_dtype == SPEC_BF16, M, d_in,
+                                              d_out, workspace, workspace_bytes,
+                                              static_cast<hipStream_t>(stream)),
+                  "spec_verify_gemm_w8_ws");
+}
+
 int spec_probe_read(const void* buf, size_t bytes, int loads_per_lane, int wgs_per_cu,
                     void* sink, void* stream) {
   clear_error();

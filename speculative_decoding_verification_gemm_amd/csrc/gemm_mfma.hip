@@ -941,4 +941,99 @@ hipError_t launch_gemm_tile_w8(const uint16_t* x, const uint8_t* w, const float*
   }
 }
 
+// FP8 weights with a split reduction: the KS = 1 forms of the FP8 tile
+// table (the widen-once 64x128, 128x128 and 320-row tiles, 128-element
+// stages for 128x256 where d_in allows).
+static const int kSplitShapesW8[][2] = {{256, 256}, {128, 256}, {128, 128},
+                                        {64, 128},  {320, 128}, {320, 256}};
+constexpr int kSplitShapeCountW8 = sizeof(kSplitShapesW8) / sizeof(kSplitShapesW8[0]);
+
+static hipError_t launch_split_shape_w8(int shape, const uint16_t* x, const uint8_t* w,
+                                        const float* ws, void* y, bool o, int M, int K, int N,
+                                        float* part, int sk, hipStream_t s) {
+  const bool k128 = K % 128 == 0;
+  switch (shape) {
+    case 0: return launch_tile_t<256, 256, 4, 3, 64, 8, 1, 16, true>(x, w, ws, y, o, M, K, N, s, part, sk);
+    case 1:
+      if (k128) return launch_tile_t<128, 256, 2, 2, 128, 8, 1, 16, true>(x, w, ws, y, o, M, K, N, s, part, sk);
+      return launch_tile_t<128, 256, 2, 4, 64, 8, 1, 16, true>(x, w, ws, y, o, M, K, N, s, part, sk);
+    case 2: return launch_tile_t<128, 128, 2, 4, 64, 8, 1, 16, true, true>(x, w, ws, y, o, M, K, N, s, part, sk);
+    case 3: return launch_tile_t<64, 128, 2, 4, 64, 8, 1, 16, true, true>(x, w, ws, y, o, M, K, N, s, part, sk);
+    case 4: return launch_tile_t<320, 128, 2, 3, 64, 8, 1, 16, true, true>(x, w, ws, y, o, M, K, N, s, part, sk);
+    case 5: return launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32, true, true>(x, w, ws, y, o, M, K, N, s, part, sk);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// k-tiles of a split form: 128-element stages for the 128x256 form when
+// d_in allows, 64 elsewhere
+static int split_k_tiles_w8(int shape, int K) {
+  return (shape == 1 && K % 128 == 0) ? K / 128 : K / 64;
+}
+
+// The FP8 tile model's term (weights at half the bytes of bf16) for `sk`
+// splits of one tile shape.
+static double tile_term_w8(int M, int N, int K, int bm, int bn, int sk, int cus) {
+  const double a = 2.5e-5, b = 1.88e-7;
+  const long tiles = (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  const long rounds = (tiles * sk + cus - 1) / cus;
+  return rounds * (a * (bm + 0.5 * bn) + b * (double)bm * bn) * K / sk;
+}
+
+// Two fits (microseconds) to 277 launches on MI355X (six Llama-3.1-8B and
+// 70B linears at M = 20, 80, 320, 1280, unsplit and every split of the
+// shapes above from 2 to 16): the unsplit kernels, whose several FP8 forms
+// the tile model prices alike (rms error 15 %), and the split ones with the
+// cost of their fp32 partials (rms 8 %). A split must beat the unsplit
+// estimate by 5 %; on those 24 linears the plans sum to 1.01 of the fastest
+// measured choice, and none is slower than the unsplit kernel.
+static SplitPlan split_plan_w8(int M, int N, int K) {
+  SplitPlan p{0, 1};
+#if defined(SPECV_DIAGNOSTICS)
+  if (const char* f = getenv("SPECV_SPLITK_W8")) {  // "shape,sk"
+    p.shape = max(0, min(atoi(f), kSplitShapeCountW8 - 1));
+    if (const char* c = strchr(f, ',')) p.sk = max(1, atoi(c + 1));
+    return p;
+  }
+#endif
+  constexpr int n_shapes = sizeof(kTileShapesW8) / sizeof(kTileShapesW8[0]);
+  const int base = pick_tile(M, N, kPlanCUs, kTileShapesW8, n_shapes, 0.5);
+  double best =
+      0.95 * (1.595 * tile_term_w8(M, N, K, kTileShapesW8[base][0], kTileShapesW8[base][1], 1,
+                                   kPlanCUs) + 2.59);
+  for (int i = 0; i < kSplitShapeCountW8; ++i) {
+    const int bm = kSplitShapesW8[i][0], bn = kSplitShapesW8[i][1];
+    const long tiles = (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    for (int sk = 2; sk <= 16 && 2 * sk <= split_k_tiles_w8(i, K) && tiles * sk <= 4 * kPlanCUs;
+         ++sk) {
+      const double t = 1.365 * tile_term_w8(M, N, K, bm, bn, sk, kPlanCUs) +
+                       0.182e-6 * ((double)sk * M * N * 8 + (double)M * N * 2) + 7.79;
+      if (t < best) {
+        best = t;
+        p = SplitPlan{i, sk};
+      }
+    }
+  }
+  return p;
+}
+
+size_t gemm_split_workspace_bytes_w8(int M, int K, int N) {
+  if (K % kTileKAlign != 0) return 0;
+  const SplitPlan p = split_plan_w8(M, N, K);
+  return p.sk > 1 ? (size_t)p.sk * M * N * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_split_w8(const uint16_t* x, const uint8_t* w, const float* w_scale, void* y,
+                                bool out_bf16, int M, int K, int N, void* workspace,
+                                size_t workspace_bytes, hipStream_t s) {
+  const SplitPlan p = split_plan_w8(M, N, K);
+  if (K % kTileKAlign != 0 || p.sk <= 1)
+    return launch_gemm_tile_w8(x, w, w_scale, y, out_bf16, M, K, N, s);
+  if (workspace == nullptr || workspace_bytes < (size_t)p.sk * M * N * sizeof(float) ||
+      split_k_tiles_w8(p.shape, K) < p.sk)
+    return hipErrorInvalidValue;
+  return launch_split_shape_w8(p.shape, x, w, w_scale, y, out_bf16, M, K, N,
+                               static_cast<float*>(workspace), p.sk, s);
+}
+
 }  // namespace specv

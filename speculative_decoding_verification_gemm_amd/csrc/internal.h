@@ -102,6 +102,11 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
 size_t gemm_split_workspace_bytes(int M, int K, int N);
 hipError_t launch_gemm_split(const uint16_t* x, const uint16_t* w, void* y, bool out_bf16, int M,
                              int K, int N, void* workspace, size_t workspace_bytes, hipStream_t s);
+// The FP8 tile kernel with a split reduction (as launch_gemm_split).
+size_t gemm_split_workspace_bytes_w8(int M, int K, int N);
+hipError_t launch_gemm_split_w8(const uint16_t* x, const uint8_t* w, const float* w_scale, void* y,
+                                bool out_bf16, int M, int K, int N, void* workspace,
+                                size_t workspace_bytes, hipStream_t s);
 hipError_t launch_gemm_tile_w8(const uint16_t* x, const uint8_t* w, const float* w_scale, void* y,
                                bool out_bf16, int M, int K, int N, hipStream_t s);
 

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 25
+    assert len(names) == 27
     for n in names:
         assert hasattr(sv.lib, n), n
 
@@ -218,6 +218,23 @@ def test_gemm_w8_rejects(sv):
     for args, code in cases:
         assert f(*args, None) == code, args
         assert sv.lib.spec_last_error()
+
+
+def test_gemm_w8_workspace_bytes_and_rejects(sv):
+    f = sv.lib.spec_verify_gemm_w8_workspace_bytes
+    # the streaming kernel's positions, d_in not a multiple of 64, out of range
+    assert f(16, 14336, 4096) == 0 and f(320, 14336 + 16, 4096) == 0 and f(0, 4096, 4096) == 0
+    for M in (20, 80, 320, 1280):
+        n = f(M, 14336, 4096)
+        assert n > 0 and n % (M * 4096 * 4) == 0 and 2 <= n // (M * 4096 * 4) <= 16
+    g = sv.lib.spec_verify_gemm_w8_ws
+    need = f(320, 14336, 4096)
+    assert g(A, A, A, A, 1, 320, 14336, 4096, None, need, None) == -4
+    assert g(A, A, A, A, 1, 320, 14336, 4096, A, need - 1, None) == -4
+    assert g(A, A, A, A, 1, 320, 14336, 4096, A + 8, need, None) == -4
+    # argument checks as spec_verify_gemm_w8
+    assert g(A, A, None, A, 0, 320, 14336, 4096, A, need, None) == -1
+    assert g(A, A, A, A, 0, 17, 4112, 4096, A, 1 << 30, None) == -3
 
 
 def test_attention_rejects(sv):

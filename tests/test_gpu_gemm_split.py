@@ -145,3 +145,112 @@ def test_split_full_size(sv, dev, M, d_in, d_out):
     for od in (torch.bfloat16, torch.float32):
         y, ref = sampled_full_size(sv, dev, M, d_in, d_out, 7 * M + d_in, od)
         check(y, ref, od, f"split full M={M} {d_in}->{d_out} {od}")
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 weights with per-row scales (spec_verify_gemm_w8_ws): the partials
+# are unscaled sums, the split-sum kernel applies the row scale once.
+# ---------------------------------------------------------------------------
+
+def w8_splits(sv, M, d_in, d_out):
+    return sv.gemm_w8_workspace_bytes(M, d_in, d_out) // (M * d_out * 4)
+
+
+@pytest.mark.parametrize("M,d_in,d_out", [(17, 6016, 300), (100, 4160, 4100)])
+def test_w8_split_parity(sv, dev, M, d_in, d_out):
+    """64x128 tiles in 16 splits of 94 k-tiles, 128x128 in 7 splits of 65
+    (both widened once per workgroup), ragged M and d_out."""
+    import torch
+    from synth import device as sd
+    assert w8_splits(sv, M, d_in, d_out) >= 2
+    xb = synth.bf16_normal_bits(M, "w8split.x", (M, d_in))
+    codes = synth.e4m3_normal_codes(M, "w8split.w", (d_out, d_in))
+    scale = synth.w8_row_scales(M, "w8split.s", d_out)
+    ref = oracle.linear_w8(xb, codes, scale)
+    x = sd.from_bits(xb, dev)
+    w = torch.from_numpy(np.ascontiguousarray(codes)).to(dev)
+    s = torch.from_numpy(np.ascontiguousarray(scale)).to(dev)
+    for od in (torch.float32, torch.bfloat16):
+        y = sv.verify_gemm_w8_ws(x, w, s, out_dtype=od)
+        torch.cuda.synchronize()
+        check(y.float().cpu().numpy().astype(np.float64), ref, od,
+              f"w8 split M={M} {d_in}->{d_out} {od}")
+
+
+def test_w8_split_one_hot_exact(sv, dev):
+    """One-hot activations through a split plan: each output is a single
+    product in one split and exact zeros in the others, so y equals
+    fp32(scale * e4m3(code)) bit for bit for every finite code."""
+    import torch
+    from synth import device as sd
+    M, d_in = 17, 6016
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    d_out = 300
+    assert w8_splits(sv, M, d_in, d_out) >= 2
+    rng = np.random.default_rng(8)
+    cols = rng.permutation(d_in)[:M]
+    w = np.zeros((d_out, d_in), dtype=np.uint8)
+    for j, k in enumerate(cols):
+        w[:, k] = np.resize(np.roll(codes, 13 * j), d_out)
+    s = synth.w8_row_scales(9, "w8.special.split", d_out)
+    x = np.zeros((M, d_in), dtype=np.uint16)
+    x[np.arange(M), cols] = 0x3F80  # 1.0
+    y = sv.verify_gemm_w8_ws(sd.from_bits(x, dev), torch.from_numpy(w).to(dev),
+                             torch.from_numpy(s).to(dev), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = (oracle.e4m3_to_f64(w[:, cols].T) * s.astype(np.float64)[None, :]).astype(np.float32)
+    assert np.array_equal(y.cpu().numpy(), want)
+
+
+# Full-size FP8 linears the plan splits: the Llama-3.1-8B down projection at
+# M = 20 to 1280 (64x128, 128x256 with 128-element stages, 320x128,
+# 320x256, 256x256 tiles, a ragged 320-row tile at M = 301), d_in = 14400 (a
+# multiple of 64 but not 128: the 64-element 128x256 form), the O
+# projection at M = 320, gate/up at M = 80, and the Llama-3.1-70B down
+# projection at M = 160.
+W8_FULL = [(20, 14336, 4096), (80, 14336, 4096), (160, 14336, 4096), (301, 14336, 4096),
+           (320, 14336, 4096), (1000, 14336, 4096), (1280, 14336, 4096), (80, 14400, 4096),
+           (333, 14400, 4096), (320, 4096, 4096), (80, 4096, 28672), (160, 28672, 8192)]
+
+
+@pytest.mark.parametrize("M,d_in,d_out", W8_FULL)
+def test_w8_split_full_size(sv, dev, M, d_in, d_out):
+    import torch
+    from synth import device as sd
+    assert w8_splits(sv, M, d_in, d_out) >= 2, (M, d_in, d_out)
+    seed = 43 * M + d_in
+    w = sd.e4m3_normal_codes((d_out, d_in), synth.W8_CODE_STD, seed, dev)
+    s = sd.w8_row_scales(d_out, synth.WEIGHT_STD / synth.W8_CODE_STD, seed + 1, dev)
+    x = sd.normal_bf16((M, d_in), 1.0, seed + 2, dev)
+    rng = np.random.default_rng(seed)
+    cols = np.unique(np.concatenate([np.arange(8), np.arange(d_out - 8, d_out),
+                                     rng.integers(0, d_out, 48)]))
+    idx = torch.from_numpy(cols).to(dev)
+    ref = oracle.linear_w8(sd.to_bits(x), w.index_select(0, idx).cpu().numpy(),
+                           s.index_select(0, idx).cpu().numpy())
+    for od in (torch.bfloat16, torch.float32):
+        y = sv.verify_gemm_w8_ws(x, w, s, out_dtype=od)
+        got = y.index_select(1, idx).float().cpu().numpy().astype(np.float64)
+        check(got, ref, od, f"w8 split full M={M} {d_in}->{d_out} {od}")
+    a = sv.verify_gemm_w8_ws(x, w, s, out_dtype=torch.float32)
+    b = sv.verify_gemm_w8_ws(x, w, s, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "split FP8 launches differ"
+    del w, a, b
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M,d_in,d_out", [(16, 14336, 4096), (320, 4096, 28672), (20, 4096, 4096)])
+def test_w8_no_split_is_spec_verify_gemm_w8(sv, dev, M, d_in, d_out):
+    """No split planned (the streaming kernel at M <= 16; the tile kernel for
+    gate/up at M = 320 and O at M = 20): bitwise spec_verify_gemm_w8."""
+    import torch
+    from synth import device as sd
+    assert sv.gemm_w8_workspace_bytes(M, d_in, d_out) == 0
+    w = sd.e4m3_normal_codes((d_out, d_in), synth.W8_CODE_STD, 3, dev)
+    s = sd.w8_row_scales(d_out, synth.WEIGHT_STD / synth.W8_CODE_STD, 4, dev)
+    x = sd.normal_bf16((M, d_in), 1.0, 5, dev)
+    a = sv.verify_gemm_w8(x, w, s, out_dtype=torch.bfloat16)
+    b = sv.verify_gemm_w8_ws(x, w, s, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
