@@ -113,7 +113,7 @@ def kernel_source_sha():
     """Hash of the streaming-GEMM sources; stored traffic counters are used
     only while this matches the hash recorded with them."""
     h = hashlib.sha256()
-    for f in ("gemm_stream.hip", "common.h", "internal.h"):
+    for f in ("gemm_stream.hip", "common.h", "internal.h", "chain_sync.h"):
         with open(os.path.join(ROOT, "speculative_decoding_verification_gemm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
