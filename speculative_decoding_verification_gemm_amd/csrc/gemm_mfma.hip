@@ -295,7 +295,7 @@ template <int BM, int BN, int WM, int S, int BK, int NW, int KS, int MF, bool W8
           bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
     const uint16_t* __restrict__ X, const void* __restrict__ W, const float* __restrict__ WS,
-    void* __restrict__ Y, int M, int N, int K, int n_tiles, int per_xcd, int sk) {
+    void* __restrict__ Y, int M, int N, int K, int n_tiles, int per_xcd, int sk, int ldy) {
   using C = TileCfg<BM, BN, WM, S, BK, NW, KS, MF, W8, WL>;
   typedef float facc __attribute__((ext_vector_type(C::NACC)));
   extern __shared__ u32x4 lds[];
@@ -456,9 +456,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
   }
   auto store = [&](int row, int col, float v) __attribute__((always_inline)) {
     if (OUT_BF16)
-      tile_store<uint16_t>(Y, (size_t)row * N + col, f32_to_bf16_bits(v));
+      tile_store<uint16_t>(Y, (size_t)row * ldy + col, f32_to_bf16_bits(v));
     else
-      tile_store<float>(Y, (size_t)row * N + col, v);
+      tile_store<float>(Y, (size_t)row * ldy + col, v);
   };
   if constexpr (KS > 1) {
     // partial tiles of the k-groups into LDS (over the ring, once every wave
@@ -525,10 +525,11 @@ template <int BM, int BN, int WM, int S, int BK, int NW = 8, int KS = 1, int MF 
           bool W8 = false, bool WL = false>
 static hipError_t launch_tile_t(const uint16_t* x, const void* w, const float* ws, void* y,
                                 bool out_bf16, int M, int K, int N, hipStream_t s,
-                                float* partials = nullptr, int sk = 1) {
+                                float* partials = nullptr, int sk = 1, int ldy = 0) {
   using C = TileCfg<BM, BN, WM, S, BK, NW, KS, MF, W8, WL>;
-  if (K % BK != 0) return hipErrorInvalidValue;  // whole stages only
-  if (sk < 1 || (sk > 1 && (KS != 1 || partials == nullptr || K / BK < sk)))
+  if (ldy == 0) ldy = N;  // output rows of N elements unless a wider stride is given
+  if (K % BK != 0 || ldy < N) return hipErrorInvalidValue;  // whole stages only
+  if (sk < 1 || (sk > 1 && (KS != 1 || partials == nullptr || K / BK < sk || ldy != N)))
     return hipErrorInvalidValue;
   const int n_tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int per_xcd = (n_tiles * sk + 7) / 8;
@@ -544,7 +545,7 @@ static hipError_t launch_tile_t(const uint16_t* x, const void* w, const float* w
   if (sk > 1) {
     hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, WL, false>), grid,
                        dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, partials, M, N, K, n_tiles,
-                       per_xcd, sk);
+                       per_xcd, sk, N);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 sgrid((unsigned)(((size_t)M * N + 255) / 256));
@@ -558,10 +559,12 @@ static hipError_t launch_tile_t(const uint16_t* x, const void* w, const float* w
   }
   if (out_bf16)
     hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, WL, true>), grid,
-                       dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, y, M, N, K, n_tiles, per_xcd, 1);
+                       dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, y, M, N, K, n_tiles, per_xcd, 1,
+                       ldy);
   else
     hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, S, BK, NW, KS, MF, W8, WL, false>), grid,
-                       dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, y, M, N, K, n_tiles, per_xcd, 1);
+                       dim3(NW * 64), C::LDS_BYTES, s, x, w, ws, y, M, N, K, n_tiles, per_xcd, 1,
+                       ldy);
   return hipGetLastError();
 }
 
@@ -682,6 +685,30 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
         case 8: return launch_tile_t<32, 32, 2, 4, 64, 8, 2>(x, w, nullptr, y, out_bf16, M, K, N, s);
         case 9: return launch_tile_t<32, 16, 2, 4, 64, 8, 4>(x, w, nullptr, y, out_bf16, M, K, N, s);
         default: break;
+      }
+    }
+    if (pick == 12) {
+      // 320x256 tiles over two or more rounds with a partial last one (the
+      // gate/up projection, 4096 -> 28672, at M = 1280 has 448 tiles for 256
+      // CUs): the columns of the whole rounds keep 320x256 tiles, and the
+      // rest run as a second launch of 320x192 tiles when those fit one
+      // round, so the last round costs a 320x192 tile's time instead of a
+      // 320x256 one's. Measured at M = 1280 on that linear: 306 against
+      // 369 us (the whole linear on 320x256 tiles) and 327 (on 256x256).
+      const int mt = (M + 319) / 320;
+      const long tiles = (long)mt * ((N + 255) / 256);
+      const long rounds = (tiles + cus - 1) / cus;
+      if (rounds >= 2 && tiles % cus != 0) {
+        const int n1 = (int)((rounds - 1) * cus / mt) * 256;
+        const int n2 = N - n1;
+        if (n2 > 0 && (long)mt * ((n2 + 191) / 192) <= cus) {
+          const hipError_t e = launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32>(
+              x, w, nullptr, y, out_bf16, M, K, n1, s, nullptr, 1, N);
+          if (e != hipSuccess) return e;
+          void* y2 = static_cast<char*>(y) + (size_t)n1 * (out_bf16 ? 2 : 4);
+          return launch_tile_t<320, 192, 2, 2, 64, 8, 1, 16>(
+              x, w + (size_t)n1 * K, nullptr, y2, out_bf16, M, K, n2, s, nullptr, 1, N);
+        }
       }
     }
     switch (pick) {

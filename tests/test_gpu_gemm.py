@@ -102,13 +102,17 @@ def test_mfma_kernel(sv, dev, M):
                                            (65, 512, 4097), (129, 64, 777), (200, 1024, 777),
                                            (256, 512, 4112), (320, 1024, 300), (513, 128, 1000),
                                            (1280, 1024, 777), (301, 256, 24000),
-                                           (640, 192, 28672)])
+                                           (640, 192, 28672), (1250, 64, 28000),
+                                           (1900, 128, 28600), (1100, 64, 57344)])
 def test_tile_kernel(sv, dev, M, d_in, d_out):
     """The pipelined tile kernel (d_in a multiple of 64, M above 8): ragged
     M and N tails, one or many stages (d_in 64 leaves k-groups without a
     k-tile), the two-, four- and eight-wave tile shapes the dispatcher picks
     (32x16, 32x32, 32x64, 64x32, 64x64, 128x64), with and without k-groups,
-    and the 320x128 tile (M = 301: a ragged 320-row tile; M = 640: two)."""
+    the 320x128 tile (M = 301: a ragged 320-row tile; M = 640: two), and
+    320x256 tiles split over two launches by columns, the rest on 320x192
+    tiles (M = 1250, 1900, 1100: ragged rows, a ragged last column tile of
+    either launch, two to four rounds)."""
     import torch
     x, w = synth.linear_inputs(300 + M, f"tile{d_in}.{d_out}", M, d_in, d_out)
     ref = oracle.linear(x, w)
