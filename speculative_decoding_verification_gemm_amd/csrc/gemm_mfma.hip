@@ -190,7 +190,11 @@ struct TileCfg {
   static constexpr int UPR_A = ROW_A / 16, UPR_B = ROW_B / 16;  // 16-byte units per row
   static constexpr int RPI_A = 64 / UPR_A, RPI_B = 64 / UPR_B;  // rows per 1 KB load instruction
   static constexpr int IA = BM / RPI_A, IB = BN / RPI_B;        // load instructions per stage
-  static constexpr int L = (IA + IB) / NWG;      // load instructions per wave per stage
+  // load instructions per wave per stage; when the stage's IA + IB do not
+  // divide among the NWG waves, the spare ones reload one line of x into a
+  // dummy kilobyte that nothing reads, so every wave's vmcnt waits are equal
+  static constexpr int L = (IA + IB + NWG - 1) / NWG;
+  static constexpr int DUMMY_BYTES = L * NWG > IA + IB ? 1024 : 0;
   static constexpr int B_OFF = BM * ROW_A;       // w rows' offset in a stage
   static constexpr int STAGE_BYTES = B_OFF + BN * ROW_B;
   static constexpr int RING_BYTES = KS * S * STAGE_BYTES;
@@ -199,14 +203,15 @@ struct TileCfg {
   // into a bf16 region of BN rows of 2 BK bytes after the ring
   static constexpr int ROW_W = 2 * BK, UPR_W = ROW_W / 16;
   static constexpr int WIDE_BYTES = WL ? BN * ROW_W : 0;
-  static constexpr int LDS_BYTES = (RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES) + WIDE_BYTES;
+  static constexpr int LDS_BYTES =
+      (RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES) + DUMMY_BYTES + WIDE_BYTES;
+  static constexpr int DUMMY_OFF = LDS_BYTES - WIDE_BYTES - DUMMY_BYTES;
   static_assert(!WL || (W8 && KS == 1), "widening in LDS: FP8 weights, one k-group");
   static_assert(BK == 32 || BK == 64 || (W8 && BK == 128), "stage depth");
   static_assert(MF == 16 || MF == 32, "MFMA block");
   static_assert(TM >= 1 && TN >= 1 && BM % (MF * WM) == 0 && BN % (MF * WN) == 0, "wave tile");
-  static_assert(NWG * KS == NW && WM * WN == NWG && BM % RPI_A == 0 && BN % RPI_B == 0 &&
-                    (IA + IB) % NWG == 0,
-                "whole load instructions per wave");
+  static_assert(NWG * KS == NW && WM * WN == NWG && BM % RPI_A == 0 && BN % RPI_B == 0,
+                "whole load instructions");
   static_assert(S >= 2 && LDS_BYTES <= 160 * 1024 && NW * 64 <= 1024, "LDS ring, workgroup");
 };
 // Stored position of unit u of LDS row r in a region of UPR 16-byte units
@@ -328,7 +333,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
 #pragma unroll
   for (int q = 0; q < C::L; ++q) {
     const int g = wr + C::NWG * q;
-    if (g < C::IA) {
+    if (C::DUMMY_BYTES > 0 && g >= C::IA + C::IB) {
+      // a spare instruction: the same valid line at every stage
+      src[q] = reinterpret_cast<const char*>(X);
+      kstride[q] = 0;
+    } else if (g < C::IA) {
       const int r = C::RPI_A * g + lane / C::UPR_A;
       const int u = tile_unit_pos<C::UPR_A, MF>(r, lane % C::UPR_A);
       src[q] = reinterpret_cast<const char*>(X + (size_t)min(m0 + r, M - 1) * K) + u * 16;
@@ -345,9 +354,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
     const int kc = k_begin + min(st * KS + kg, n_k - 1);
     const int slot = kg * S + st % S;
 #pragma unroll
-    for (int q = 0; q < C::L; ++q)
-      tile_load_lds(src[q] + (size_t)kc * kstride[q],
-                    reinterpret_cast<char*>(lds) + slot * C::STAGE_BYTES + (wr + C::NWG * q) * 1024);
+    for (int q = 0; q < C::L; ++q) {
+      const int g = wr + C::NWG * q;
+      char* dst = reinterpret_cast<char*>(lds) + slot * C::STAGE_BYTES + g * 1024;
+      if constexpr (C::DUMMY_BYTES > 0)
+        if (g >= C::IA + C::IB) dst = reinterpret_cast<char*>(lds) + C::DUMMY_OFF;
+      tile_load_lds(src[q] + (size_t)kc * kstride[q], dst);
+    }
   };
 
   facc acc[C::TM][C::TN];
@@ -940,6 +953,27 @@ hipError_t launch_gemm_tile_w8(const uint16_t* x, const uint8_t* w, const float*
   const long tiles = (long)((M + kTileShapesW8[pick][0] - 1) / kTileShapesW8[pick][0]) *
                      ((N + kTileShapesW8[pick][1] - 1) / kTileShapesW8[pick][1]);
   const bool one_round = tiles <= cus;
+  if (pick == 10 && w8_wide(pick, M)) {
+    // as for bf16 weights: 320x256 tiles over two or more rounds with a
+    // partial last one run the columns of the whole rounds on 320x256 and
+    // the rest on 320x192 (both widened once per workgroup) when those fit
+    // one round
+    const int mt = (M + 319) / 320;
+    const long tiles = (long)mt * ((N + 255) / 256);
+    const long rounds = (tiles + cus - 1) / cus;
+    if (rounds >= 2 && tiles % cus != 0) {
+      const int n1 = (int)((rounds - 1) * cus / mt) * 256;
+      const int n2 = N - n1;
+      if (n2 > 0 && (long)mt * ((n2 + 191) / 192) <= cus) {
+        const hipError_t e = launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32, true, true>(
+            x, w, w_scale, y, out_bf16, M, K, n1, s, nullptr, 1, N);
+        if (e != hipSuccess) return e;
+        void* y2 = static_cast<char*>(y) + (size_t)n1 * (out_bf16 ? 2 : 4);
+        return launch_tile_t<320, 192, 2, 2, 64, 8, 1, 16, true, true>(
+            x, w + (size_t)n1 * K, w_scale + n1, y2, out_bf16, M, K, n2, s, nullptr, 1, N);
+      }
+    }
+  }
   if (w8_wide(pick, M)) return launch_w8_wide(pick, x, w, w_scale, y, out_bf16, M, K, N, s);
   if (allow_k128 && K % 128 == 0 && w8_has_k128(pick, one_round))
     return launch_w8_k128(pick, x, w, w_scale, y, out_bf16, M, K, N, s);

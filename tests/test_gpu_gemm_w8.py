@@ -117,7 +117,11 @@ W8_TILE_CASES = [(513, 256, 16400), (200, 192, 16400), (130, 384, 24000), (513, 
                  (611, 128, 792), (611, 192, 792), (17, 1024, 4104), (20, 192, 6150),
                  (193, 128, 2334), (20, 4096, 777), (17, 320, 1000), (20, 256, 12288),
                  (20, 192, 12300), (17, 512, 16400), (301, 192, 24000), (257, 128, 24000),
-                 (301, 64, 60000), (513, 128, 60000)]
+                 (301, 64, 60000), (513, 128, 60000),
+                 # 320x256 over two to four rounds, split by columns: the
+                 # rest on 320x192 tiles (whose 52 load instructions per
+                 # stage leave four spare ones for the eight waves)
+                 (1250, 64, 28000), (1900, 128, 28000), (1280, 64, 57344)]
 
 
 @pytest.mark.parametrize("M,d_in,d_out", W8_TILE_CASES)
