@@ -513,22 +513,44 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
 
 // The sk partial tiles of a split reduction added in split order (fixed, so
 // the result is deterministic), scaled by the row scale for FP8 weights and
-// stored as the output.
+// stored as the output. Each thread takes four consecutive outputs with
+// 16-byte loads when M * N is a multiple of four (every partial slice is
+// then 16-byte aligned), else one at a time.
 template <bool OUT_BF16, bool W8>
 __global__ __launch_bounds__(256) void gemm_split_sum_kernel(const float* __restrict__ P,
                                                              const float* __restrict__ WS,
                                                              void* __restrict__ Y, int M, int N,
                                                              int sk) {
   const size_t mn = (size_t)M * N;
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= mn) return;
-  float v = P[i];
-  for (int p = 1; p < sk; ++p) v += P[(size_t)p * mn + i];
-  if (W8) v *= tile_scale(WS, (int)(i % N));
-  if (OUT_BF16)
-    tile_store<uint16_t>(Y, i, f32_to_bf16_bits(v));
-  else
-    tile_store<float>(Y, i, v);
+  const size_t i0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i0 >= mn) return;
+  float v[4];
+  int cnt = 4;
+  if ((mn & 3) == 0) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const SPECV_TILE_GLOBAL f32x4* p4 = (const SPECV_TILE_GLOBAL f32x4*)(P + i0);
+    f32x4 a = p4[0];
+    for (int p = 1; p < sk; ++p) a += p4[(size_t)p * (mn / 4)];
+    v[0] = a.x;
+    v[1] = a.y;
+    v[2] = a.z;
+    v[3] = a.w;
+  } else {
+    cnt = (int)min((size_t)4, mn - i0);
+    for (int e = 0; e < cnt; ++e) {
+      float a = P[i0 + e];
+      for (int p = 1; p < sk; ++p) a += P[(size_t)p * mn + i0 + e];
+      v[e] = a;
+    }
+  }
+  for (int e = 0; e < cnt; ++e) {
+    const size_t i = i0 + e;
+    const float x = W8 ? v[e] * tile_scale(WS, (int)(i % N)) : v[e];
+    if (OUT_BF16)
+      tile_store<uint16_t>(Y, i, f32_to_bf16_bits(x));
+    else
+      tile_store<float>(Y, i, x);
+  }
 }
 
 // sk > 1: the reduction is split over sk workgroups per tile (whole k-tiles,
@@ -561,7 +583,7 @@ static hipError_t launch_tile_t(const uint16_t* x, const void* w, const float* w
                        per_xcd, sk, N);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 sgrid((unsigned)(((size_t)M * N + 255) / 256));
+    const dim3 sgrid((unsigned)(((size_t)M * N + 1023) / 1024));  // four outputs per thread
     if (out_bf16)
       hipLaunchKernelGGL((gemm_split_sum_kernel<true, W8>), sgrid, dim3(256), 0, s, partials, ws, y,
                          M, N, sk);
