@@ -254,3 +254,38 @@ def test_w8_no_split_is_spec_verify_gemm_w8(sv, dev, M, d_in, d_out):
     b = sv.verify_gemm_w8_ws(x, w, s, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_split_in_graph_replays(sv, dev):
+    """The split path (tile kernel, then the split-sum kernel) captured in a
+    HIP graph, as the step benchmark runs it: every replay, with eager work
+    and synchronizations between them, equals the eager call bit for bit."""
+    import torch
+    from synth import device as sd
+    M, d_in, d_out = 320, 14336, 4096
+    assert splits(sv, M, d_in, d_out) >= 2
+    x = sd.normal_bf16((M, d_in), 1.0, 61, dev)
+    w = sd.normal_bf16((d_out, d_in), synth.WEIGHT_STD, 62, dev)
+    ws = torch.empty(sv.gemm_workspace_bytes(M, d_in, d_out), dtype=torch.uint8, device=dev)
+    eager = sv.verify_gemm_ws(x, w, out_dtype=torch.bfloat16, workspace=ws)
+    torch.cuda.synchronize()
+    y = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sv.verify_gemm_ws(x, w, out=y, workspace=ws)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        sv.verify_gemm_ws(x, w, out=y, workspace=ws)
+    for r in range(4):
+        y.fill_(0.0)
+        ws.fill_(0xFF)  # the partials must be rewritten by every replay
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"replay {r}"
+        # eager work between replays, on the same workspace
+        sv.verify_gemm_ws(x[:80].contiguous(), w, out_dtype=torch.bfloat16, workspace=ws)
+        torch.cuda.synchronize()
