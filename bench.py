@@ -99,8 +99,9 @@ def parse():
                     help="batch sweep on the workload's shapes: B in --sweep-batches")
     ap.add_argument("--sweep-batches", default="1,4,16,64,256")
     ap.add_argument("--linear", default=None,
-                    help="DINxDOUT: time spec_verify_gemm (or _w8) on one linear at M = 5 B, "
-                         "rotating over weight copies that together exceed the 256 MB cache")
+                    help="DINxDOUT: time spec_verify_gemm_ws (or _w8_ws; with --no-split the "
+                         "calls without a split reduction) on one linear at M = 5 B, rotating "
+                         "over weight copies that together exceed the 256 MB cache")
     ap.add_argument("--probe", action="store_true",
                     help="measure the achievable HBM read bandwidth and dense bf16 MFMA rate")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -725,10 +726,11 @@ def sweep_bench(args):
 
 
 def linear_bench(args):
-    """spec_verify_gemm (spec_verify_gemm_w8 with --w8) on one linear, one
-    launch per step, rotating over weight copies that together exceed the
-    256 MB Infinity Cache (so every launch reads its weights from HBM).
-    Output bf16, or fp32 for a linear as wide as the vocabulary."""
+    """spec_verify_gemm_ws (spec_verify_gemm_w8_ws with --w8; the calls
+    without a split reduction with --no-split) on one linear, one call per
+    step, rotating over weight copies that together exceed the 256 MB
+    Infinity Cache (so every launch reads its weights from HBM). Output
+    bf16, or fp32 for a linear as wide as the vocabulary."""
     import torch
     import synth
     import speculative_decoding_verification_gemm_amd as sv
@@ -750,10 +752,17 @@ def linear_bench(args):
     x = sd.normal_bf16((M, d_in), 1.0, args.seed + 999, dev)
     od = torch.float32 if d_out >= 100000 else torch.bfloat16
     y = torch.empty((M, d_out), dtype=od, device=dev)
+    need = (sv.gemm_w8_workspace_bytes if args.w8 else sv.gemm_workspace_bytes)(M, d_in, d_out)
+    wsp = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    split = not args.no_split
 
     def call(i):
-        if args.w8:
+        if args.w8 and split:
+            sv.verify_gemm_w8_ws(x, ws[i % copies], scs[i % copies], out=y, workspace=wsp)
+        elif args.w8:
             sv.verify_gemm_w8(x, ws[i % copies], scs[i % copies], out=y)
+        elif split:
+            sv.verify_gemm_ws(x, ws[i % copies], out=y, workspace=wsp)
         else:
             sv.verify_gemm(x, ws[i % copies], out=y)
     for i in range(max(args.warmup, copies)):
@@ -775,7 +784,8 @@ def linear_bench(args):
         "unit": "us per launch", "n_gpus": 1, "steps": n, "warmup": args.warmup,
         "higher_is_better": False, "vs_baseline": None,
         "dtype": "bf16 (fp8 e4m3 weights)" if args.w8 else "bf16", "data": "synthetic",
-        "config": {"workload": f"linear {d_in}->{d_out}, M={M}, {copies} weight copies"},
+        "config": {"workload": f"linear {d_in}->{d_out}, M={M}, {copies} weight copies",
+                   "split_reduction": need > 0 and split},
         "gbs": by / (ms * 1e-3) / 1e9, "tflops": fl / (ms * 1e-3) / 1e12,
         "hbm_frac": by / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "mfma_frac": fl / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)}), flush=True)
