@@ -812,9 +812,9 @@ struct SplitPlan {
 // fit to measured launches) plus, for a split, a fixed cost and the fp32
 // partial tiles written and read back by the split-sum kernel. The fit is to
 // 250 launches on MI355X (the Llama-3.1-8B linears except the lm-head at
-// M = 20, 80, 320, 1280, every split of the shapes below from 2 to 16):
-// rms error 12 %; on each of the 16 linears the plan it picks is the fastest
-// measured or within 5.2 % of it. Checked on the Llama-3.1-8B and 70B
+// M = 20, 80, 320, 1280, every split of the split shapes above from 2 to
+// 16): rms error 12 %; on each of the 16 linears the plan it picks is the
+// fastest measured or within 5.2 % of it. Checked on the Llama-3.1-8B and 70B
 // linears at M = 5 to 1280: where it splits, the split runs 0.64 to 1.00 of
 // the unsplit time.
 static double tile_us(int M, int N, int K, int bm, int bn, int sk, int cus) {
