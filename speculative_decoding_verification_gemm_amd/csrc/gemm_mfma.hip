@@ -262,6 +262,54 @@ __device__ __forceinline__ void tile_store(void* y, size_t i, T v) {
 __device__ __forceinline__ float tile_scale(const float* ws, int col) {
   return ((const SPECV_TILE_GLOBAL float*)ws)[col];
 }
+__device__ __forceinline__ void tile_store16(void* base, size_t byte_off, u32x4 v) {
+  *(SPECV_TILE_GLOBAL u32x4*)(static_cast<char*>(base) + byte_off) = v;
+}
+
+// One staged block of the epilogue (R rows of WTN fp32 values, LDW floats
+// apart in LDS) to rows row0.. and columns col0.. of an output of ld
+// elements per row: each lane takes 16 bytes of a row per store (8 bf16 or
+// 4 fp32 outputs), so a wave's store covers whole runs of a row instead of
+// one 16- or 32-column piece per row. Element by element at the right edge
+// and where the output is not 16-byte aligned.
+template <int R, int WTN, int LDW, bool BF>
+__device__ __forceinline__ void tile_emit_block(const float* stg, void* base, int ld, bool vec_ok,
+                                                int row0, int col0, int M, int N, int lane) {
+  constexpr int VEC = BF ? 8 : 4, CPR = WTN / VEC;
+  static_assert(WTN % VEC == 0, "whole stores per row");
+#pragma unroll
+  for (int it = 0; it < (R * CPR + 63) / 64; ++it) {
+    const int c = lane + 64 * it;
+    if (R * CPR % 64 != 0 && c >= R * CPR) break;
+    const int rr = c / CPR, cc = (c - rr * CPR) * VEC;
+    const int row = row0 + rr, col = col0 + cc;
+    if (row >= M) continue;
+    const float* sp = stg + rr * LDW + cc;
+    const size_t off = (size_t)row * ld + col;
+    if (vec_ok && col + VEC <= N) {
+      if constexpr (BF) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(sp);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(sp + 4);
+        auto pk = [](uint32_t a, uint32_t b) {
+          return (uint32_t)f32_to_bf16_bits(__builtin_bit_cast(float, a)) |
+                 ((uint32_t)f32_to_bf16_bits(__builtin_bit_cast(float, b)) << 16);
+        };
+        tile_store16(base, off * 2, u32x4{pk(lo.x, lo.y), pk(lo.z, lo.w), pk(hi.x, hi.y), pk(hi.z, hi.w)});
+      } else {
+        tile_store16(base, off * 4, *reinterpret_cast<const u32x4*>(sp));
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v)
+        if (col + v < N) {
+          if constexpr (BF)
+            tile_store<uint16_t>(base, off + v, f32_to_bf16_bits(sp[v]));
+          else
+            tile_store<float>(base, off + v, sp[v]);
+        }
+    }
+  }
+}
 
 template <int N>
 __device__ __forceinline__ void tile_wait_vmcnt() {
@@ -450,6 +498,57 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
     }
   }
   tile_wait_vmcnt<0>();  // the reloads past the end land before the workgroup leaves
+
+  // Epilogue through LDS (one k-group, and 64 or more outputs per lane):
+  // each wave writes one row of its blocks (MF rows of its wave tile) into a
+  // padded staging block of its own over the drained ring, then stores it
+  // along the rows, 16 bytes a lane (tile_emit_block). Stored directly, the
+  // blocks' own layout (4 rows of 16 columns, or 2 of 32, per store) takes
+  // one store instruction per output of a lane, each writing 32- to 128-byte
+  // pieces of rows. Measured on the Llama-3.1-8B linears: 2-5 % faster with
+  // 320x256, 256x256 and 320x128 tiles (up to 14 % with FP8 weights); 1-2 %
+  // slower with 32 or fewer outputs per lane, which keep the direct stores.
+  constexpr int WTN = BN / C::WN;           // wave tile columns
+  constexpr int LDW = WTN + 4;              // staged row, floats (padded against bank conflicts)
+  constexpr int STG_BYTES = MF * LDW * 4;   // one wave's staging block
+  if constexpr (KS == 1 && C::TM * C::TN * C::NACC >= 64 && NW * STG_BYTES <= C::LDS_BYTES &&
+                WTN % 8 == 0) {
+    __syncthreads();  // every wave's loads have landed and its ring reads are done
+    float* stg = reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + wave * STG_BYTES);
+    const int r0 = wm * (BM / WM), c0 = wn * WTN;  // wave tile origin in the tile
+    const bool partial = sk > 1;
+    // a partial tile goes to split `split` of the workspace (fp32, unscaled)
+    void* dst = partial ? static_cast<void*>(static_cast<float*>(Y) + (size_t)split * M * N) : Y;
+    const int ld = partial ? N : ldy;
+    float sc[C::TN];
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int col = n0 + out_col(j);
+      sc[j] = W8 && !partial && col < N ? tile_scale(WS, col) : 1.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int col = out_col(j) - c0;
+#pragma unroll
+        for (int e = 0; e < C::NACC; ++e)
+          stg[(out_row(i, e) - r0 - i * MF) * LDW + col] = W8 ? acc[i][j][e] * sc[j] : acc[i][j][e];
+      }
+      tile_wait_lgkm0();  // the block is in LDS (one wave writes and reads it)
+      if (!partial && OUT_BF16) {
+        const bool vec_ok = (reinterpret_cast<uintptr_t>(dst) & 15) == 0 && ld % 8 == 0;
+        tile_emit_block<MF, WTN, LDW, true>(stg, dst, ld, vec_ok, m0 + r0 + i * MF, n0 + c0, M, N,
+                                            lane);
+      } else {
+        const bool vec_ok = (reinterpret_cast<uintptr_t>(dst) & 15) == 0 && ld % 4 == 0;
+        tile_emit_block<MF, WTN, LDW, false>(stg, dst, ld, vec_ok, m0 + r0 + i * MF, n0 + c0, M,
+                                             N, lane);
+      }
+      tile_wait_lgkm0();  // its reads are done before the next block overwrites it
+    }
+    return;
+  }
 
   if (sk > 1) {
     // a partial tile: fp32, unscaled, to split `split` of the workspace
@@ -689,6 +788,9 @@ static hipError_t launch_tile_forced(int id, const uint16_t* x, const uint16_t* 
     case 126: return launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
     case 127: return launch_tile_t<128, 64, 4, 4, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
     case 128: return launch_tile_t<256, 128, 4, 3, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s);
+    case 133: return launch_tile_t<320, 128, 4, 2, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s);
+    case 134: return launch_tile_t<320, 256, 4, 2, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s);
+    case 135: return launch_tile_t<320, 192, 4, 2, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -737,11 +839,11 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
         const int n1 = (int)((rounds - 1) * cus / mt) * 256;
         const int n2 = N - n1;
         if (n2 > 0 && (long)mt * ((n2 + 191) / 192) <= cus) {
-          const hipError_t e = launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32>(
+          const hipError_t e = launch_tile_t<320, 256, 4, 2, 64, 8, 1, 16>(
               x, w, nullptr, y, out_bf16, M, K, n1, s, nullptr, 1, N);
           if (e != hipSuccess) return e;
           void* y2 = static_cast<char*>(y) + (size_t)n1 * (out_bf16 ? 2 : 4);
-          return launch_tile_t<320, 192, 2, 2, 64, 8, 1, 16>(
+          return launch_tile_t<320, 192, 4, 2, 64, 8, 1, 16>(
               x, w + (size_t)n1 * K, nullptr, y2, out_bf16, M, K, n2, s, nullptr, 1, N);
         }
       }
@@ -764,10 +866,14 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
       // 320 rows: B = 64 and B = 256 sequences of K + 1 = 5 positions fill
       // one or four of them without padding (M = 320: gate/up 89 against
       // 144 us with 256x256 tiles; lm-head with 320x256, 334 against 419 us;
-      // M = 1280 gate/up with 320x256, 282 against 316 us). The 320x256
-      // wave tile (160x64) uses 32x32x16 blocks, the only form measured.
+      // M = 1280 gate/up with 320x256, 282 against 316 us). 320x256 tiles
+      // lay the eight waves out 4x2 (80x128 wave tiles of 16x16x32 blocks):
+      // measured faster than 2x2 with 160x64 wave tiles of 32x32x16 blocks
+      // (lm-head at M = 1280: 1174 against 1240 us; gate/up 267-284 against
+      // 284-307), and so are the split forms below (down projection at
+      // M = 1280 with sk = 4: 165-177 against 176-202 us).
       case 11: return launch_tile_t<320, 128, 2, 2, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
-      default: return launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      default: return launch_tile_t<320, 256, 4, 2, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
     }
   }
   if (M <= 32) return launch_mfma_t<32, 64, 1>(x, w, y, out_bf16, M, K, N, s);
@@ -796,7 +902,7 @@ static hipError_t launch_split_shape(int shape, const uint16_t* x, const uint16_
     case 3: return launch_tile_t<128, 128, 2, 4, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s, part, sk);
     case 4: return launch_tile_t<64, 128, 2, 4, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s, part, sk);
     case 5: return launch_tile_t<320, 128, 2, 2, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s, part, sk);
-    case 6: return launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32>(x, w, nullptr, y, o, M, K, N, s, part, sk);
+    case 6: return launch_tile_t<320, 256, 4, 2, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s, part, sk);
     case 7: return launch_tile_t<128, 64, 4, 4, 64, 8, 1, 16>(x, w, nullptr, y, o, M, K, N, s, part, sk);
     case 8: return launch_tile_t<64, 64, 2, 4, 64>(x, w, nullptr, y, o, M, K, N, s, part, sk);
     case 9: return launch_tile_t<32, 64, 1, 4, 64, 4>(x, w, nullptr, y, o, M, K, N, s, part, sk);
@@ -952,6 +1058,10 @@ static hipError_t launch_w8_forced(int id, const uint16_t* x, const uint8_t* w, 
     case 105: return launch_tile_t<64, 128, 2, 4, 128, 8, 1, 16, true>(x, w, ws, y, o, M, K, N, s);
     case 108: return launch_tile_t<32, 64, 1, 4, 128, 4, 1, 16, true>(x, w, ws, y, o, M, K, N, s);
     case 109: return launch_tile_t<32, 32, 2, 4, 128, 4, 2, 16, true>(x, w, ws, y, o, M, K, N, s);
+    case 110: return launch_tile_t<320, 256, 4, 2, 64, 8, 1, 16, true, true>(x, w, ws, y, o, M, K, N, s);
+    case 111: return launch_tile_t<320, 256, 2, 2, 64, 8, 1, 32, true, true>(x, w, ws, y, o, M, K, N, s);
+    case 112: return launch_tile_t<320, 128, 4, 2, 64, 8, 1, 16, true, true>(x, w, ws, y, o, M, K, N, s);
+    case 113: return launch_tile_t<320, 128, 2, 3, 64, 8, 1, 16, true, true>(x, w, ws, y, o, M, K, N, s);
     default: return hipErrorInvalidValue;
   }
 }
