@@ -103,7 +103,10 @@ def test_mfma_kernel(sv, dev, M):
                                            (256, 512, 4112), (320, 1024, 300), (513, 128, 1000),
                                            (1280, 1024, 777), (301, 256, 24000),
                                            (640, 192, 28672), (1250, 64, 28000),
-                                           (1900, 128, 28600), (1100, 64, 57344)])
+                                           (1900, 128, 28600), (1100, 64, 57344),
+                                           (480, 64, 28675), (1280, 64, 6147), (80, 64, 50001),
+                                           (301, 64, 24001), (640, 64, 28675), (1250, 64, 28003),
+                                           (1250, 64, 28004)])
 def test_tile_kernel(sv, dev, M, d_in, d_out):
     """The pipelined tile kernel (d_in a multiple of 64, M above 8): ragged
     M and N tails, one or many stages (d_in 64 leaves k-groups without a
@@ -112,7 +115,12 @@ def test_tile_kernel(sv, dev, M, d_in, d_out):
     the 320x128 tile (M = 301: a ragged 320-row tile; M = 640: two), and
     320x256 tiles split over two launches by columns, the rest on 320x192
     tiles (M = 1250, 1900, 1100: ragged rows, a ragged last column tile of
-    either launch, two to four rounds)."""
+    either launch, two to four rounds). The tiles that store through the
+    LDS staging block (256x256, 256x128, 128x256, 320x128, 320x256 and the
+    column split: M = 480, 1280, 80, 301, 640, 1250 with d_out not a
+    multiple of 8) also meet output rows whose 16-byte stores do not line
+    up, stored element by element (d_out = 28004: bf16 rows element by
+    element, fp32 rows in 16-byte stores)."""
     import torch
     x, w = synth.linear_inputs(300 + M, f"tile{d_in}.{d_out}", M, d_in, d_out)
     ref = oracle.linear(x, w)

@@ -135,7 +135,12 @@ def sampled_full_size(sv, dev, M, d_in, d_out, seed, out_dtype, n_cols=48):
 # projection (128x256 and 256x256 tiles).
 FULL = [(5, 14336, 4096), (20, 14336, 4096), (80, 14336, 4096), (160, 14336, 4096),
         (301, 14336, 4096), (320, 14336, 4096), (1000, 14336, 4096), (1280, 14336, 4096),
-        (1280, 4096, 4096), (80, 28672, 8192), (160, 28672, 8192), (640, 8192, 10240)]
+        (1280, 4096, 4096), (80, 28672, 8192), (160, 28672, 8192), (640, 8192, 10240),
+        # partial tiles stored through the LDS staging block with d_out not
+        # a multiple of 4 (element by element at every row): 256x128,
+        # 256x256, 320x128, 320x256 and 128x256 tiles
+        (160, 8192, 8191), (160, 14336, 8191), (320, 8192, 4095), (320, 14336, 10239),
+        (640, 14336, 2047)]
 
 
 @pytest.mark.parametrize("M,d_in,d_out", FULL)
@@ -210,7 +215,10 @@ def test_w8_split_one_hot_exact(sv, dev):
 # projection at M = 160.
 W8_FULL = [(20, 14336, 4096), (80, 14336, 4096), (160, 14336, 4096), (301, 14336, 4096),
            (320, 14336, 4096), (1000, 14336, 4096), (1280, 14336, 4096), (80, 14400, 4096),
-           (333, 14400, 4096), (320, 4096, 4096), (80, 4096, 28672), (160, 28672, 8192)]
+           (333, 14400, 4096), (320, 4096, 4096), (80, 4096, 28672), (160, 28672, 8192),
+           # staged partial tiles with d_out not a multiple of 4: 128x256
+           # (128-element stages), 256x256, 320x128 and 320x256
+           (160, 8192, 4095), (160, 14336, 8191), (320, 8192, 8191), (320, 8192, 10239)]
 
 
 @pytest.mark.parametrize("M,d_in,d_out", W8_FULL)

@@ -121,7 +121,13 @@ W8_TILE_CASES = [(513, 256, 16400), (200, 192, 16400), (130, 384, 24000), (513, 
                  # 320x256 over two to four rounds, split by columns: the
                  # rest on 320x192 tiles (whose 52 load instructions per
                  # stage leave four spare ones for the eight waves)
-                 (1250, 64, 28000), (1900, 128, 28000), (1280, 64, 57344)]
+                 (1250, 64, 28000), (1900, 128, 28000), (1280, 64, 57344),
+                 # the forms that store through the LDS staging block
+                 # (256x256, 128x256 with 64- and 128-element stages, the
+                 # widen-once 320x128 and 320x256, the column split) with
+                 # d_out not a multiple of 8
+                 (480, 64, 28675), (1280, 64, 6147), (1280, 128, 6147), (301, 64, 24001),
+                 (640, 64, 28675), (1250, 64, 28003)]
 
 
 @pytest.mark.parametrize("M,d_in,d_out", W8_TILE_CASES)
