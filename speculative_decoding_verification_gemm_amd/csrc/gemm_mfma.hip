@@ -294,7 +294,8 @@ __device__ __forceinline__ void tile_emit_block(const float* stg, void* base, in
           return (uint32_t)f32_to_bf16_bits(__builtin_bit_cast(float, a)) |
                  ((uint32_t)f32_to_bf16_bits(__builtin_bit_cast(float, b)) << 16);
         };
-        tile_store16(base, off * 2, u32x4{pk(lo.x, lo.y), pk(lo.z, lo.w), pk(hi.x, hi.y), pk(hi.z, hi.w)});
+        tile_store16(base, off * 2,
+                     u32x4{pk(lo.x, lo.y), pk(lo.z, lo.w), pk(hi.x, hi.y), pk(hi.z, hi.w)});
       } else {
         tile_store16(base, off * 4, *reinterpret_cast<const u32x4*>(sp));
       }
@@ -533,7 +534,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_tile_kernel(
         const int col = out_col(j) - c0;
 #pragma unroll
         for (int e = 0; e < C::NACC; ++e)
-          stg[(out_row(i, e) - r0 - i * MF) * LDW + col] = W8 ? acc[i][j][e] * sc[j] : acc[i][j][e];
+          stg[(out_row(i, e) - r0 - i * MF) * LDW + col] =
+              W8 ? acc[i][j][e] * sc[j] : acc[i][j][e];
       }
       tile_wait_lgkm0();  // the block is in LDS (one wave writes and reads it)
       if (!partial && OUT_BF16) {
@@ -830,8 +832,9 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
       // CUs): the columns of the whole rounds keep 320x256 tiles, and the
       // rest run as a second launch of 320x192 tiles when those fit one
       // round, so the last round costs a 320x192 tile's time instead of a
-      // 320x256 one's. Measured at M = 1280 on that linear: 306 against
-      // 369 us (the whole linear on 320x256 tiles) and 327 (on 256x256).
+      // 320x256 one's. Measured at M = 1280 on that linear, with the 2x2
+      // 320-row forms of the time: 306 against 369 us (the whole linear on
+      // 320x256 tiles) and 327 (on 256x256).
       const int mt = (M + 319) / 320;
       const long tiles = (long)mt * ((N + 255) / 256);
       const long rounds = (tiles + cus - 1) / cus;
