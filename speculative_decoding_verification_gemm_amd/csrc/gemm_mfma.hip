@@ -708,11 +708,16 @@ static hipError_t launch_tile_t(const uint16_t* x, const void* w, const float* w
 // launch_gemm_mfma: the first seven and the two 320-row tiles use eight
 // waves; the four small ones (for linears with few positions) two or four,
 // so that several of them share a CU, or eight in k-groups when their tiles
-// fit one round.
+// fit one round. The last kExactFillShapes are candidates only where their
+// tiles number exactly one per CU: 80x64 (ten waves in two k-groups) and
+// 160x128 (eight waves). Measured on the Llama-3.1-8B O projection
+// (4096 -> 4096): at M = 320, 80x64 22.7 against 26.6 us (128x64); at
+// M = 1280, 160x128 48.3 against 55.8 (320x128 tiles, two splits).
 static const int kTileShapes[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128},
                                      {128, 64},  {64, 128},  {64, 64},   {64, 32},
                                      {32, 32},   {32, 16},   {32, 64},   {320, 128},
-                                     {320, 256}};
+                                     {320, 256}, {80, 64},   {160, 128}};
+constexpr int kExactFillShapes = 2;
 
 // Time model of one launch, per reduction element: a tile costs
 // a * (BM + wb BN) (operand lines into LDS and out to the matrix cores; wb
@@ -725,13 +730,15 @@ static const int kTileShapes[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 1
 // ten linears and one within 2 % for the tenth. At M = 20 to 256 it picks
 // what the earlier fit picked there, which was checked against every small
 // shape forced in turn at M = 20 to 128 (the fastest, or within about 10 %).
-static int pick_tile(int M, int N, int cus, const int (*shapes)[2], int n, double wb = 1.0) {
+static int pick_tile(int M, int N, int cus, const int (*shapes)[2], int n, double wb = 1.0,
+                     int n_exact = 0) {
   const double a = 2.5e-5, b = 1.88e-7;
   int best = 0;
   double best_t = 0.0;
   for (int i = 0; i < n; ++i) {
     const int bm = shapes[i][0], bn = shapes[i][1];
     const long tiles = (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    if (i >= n - n_exact && tiles != cus) continue;  // exact-fill shapes: one tile per CU only
     const long rounds = (tiles + cus - 1) / cus;
     const double t = rounds * (a * (bm + wb * bn) + b * (double)bm * bn);
     if (i == 0 || t < best_t) {
@@ -807,7 +814,7 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
   if (K % kTileKAlign == 0) {
     const int cus = device_cus();
     constexpr int n_shapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
-    int pick = pick_tile(M, N, cus, kTileShapes, n_shapes);
+    int pick = pick_tile(M, N, cus, kTileShapes, n_shapes, 1.0, kExactFillShapes);
 #if defined(SPECV_DIAGNOSTICS)
     if (const char* f = getenv("SPECV_TILE_PICK")) pick = max(0, min(atoi(f), n_shapes - 1));
 #endif
@@ -876,7 +883,11 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
       // 284-307), and so are the split forms below (down projection at
       // M = 1280 with sk = 4: 165-177 against 176-202 us).
       case 11: return launch_tile_t<320, 128, 2, 2, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
-      default: return launch_tile_t<320, 256, 4, 2, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 12: return launch_tile_t<320, 256, 4, 2, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      // exact-fill shapes (one tile per CU)
+      case 13: return launch_tile_t<80, 64, 5, 3, 64, 10, 2, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 14: return launch_tile_t<160, 128, 2, 4, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      default: return hipErrorInvalidValue;
     }
   }
   if (M <= 32) return launch_mfma_t<32, 64, 1>(x, w, y, out_bf16, M, K, N, s);
@@ -945,7 +956,12 @@ static SplitPlan split_plan(int M, int N, int K) {
   }
 #endif
   constexpr int n_shapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
-  const int base = pick_tile(M, N, kPlanCUs, kTileShapes, n_shapes);
+  // The exact-fill shapes stand as the unsplit pick only up to 4096 columns:
+  // at 8192 (the Llama-3.1-70B O projection at M = 160 and 640) they were
+  // 2-5 % slower than the split plans the model put behind them.
+  const int n_exact = N <= 4096 ? kExactFillShapes : 0;
+  const int base = pick_tile(M, N, kPlanCUs, kTileShapes, n_shapes - kExactFillShapes + n_exact,
+                             1.0, n_exact);
   const long base_tiles = (long)((M + kTileShapes[base][0] - 1) / kTileShapes[base][0]) *
                           ((N + kTileShapes[base][1] - 1) / kTileShapes[base][1]);
   // A split must beat the unsplit pick by 5 % of the model's time, or by

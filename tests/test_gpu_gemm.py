@@ -106,7 +106,8 @@ def test_mfma_kernel(sv, dev, M):
                                            (1900, 128, 28600), (1100, 64, 57344),
                                            (480, 64, 28675), (1280, 64, 6147), (80, 64, 50001),
                                            (301, 64, 24001), (640, 64, 28675), (1250, 64, 28003),
-                                           (1250, 64, 28004)])
+                                           (1250, 64, 28004), (300, 128, 4095), (1250, 64, 4095),
+                                           (320, 192, 4096), (1280, 128, 4096)])
 def test_tile_kernel(sv, dev, M, d_in, d_out):
     """The pipelined tile kernel (d_in a multiple of 64, M above 8): ragged
     M and N tails, one or many stages (d_in 64 leaves k-groups without a
@@ -120,7 +121,9 @@ def test_tile_kernel(sv, dev, M, d_in, d_out):
     column split: M = 480, 1280, 80, 301, 640, 1250 with d_out not a
     multiple of 8) also meet output rows whose 16-byte stores do not line
     up, stored element by element (d_out = 28004: bf16 rows element by
-    element, fp32 rows in 16-byte stores)."""
+    element, fp32 rows in 16-byte stores). The exact-fill tiles, taken where
+    their tiles number one per CU: 80x64 in two k-groups of five waves (M =
+    300, 320 with d_out = 4095, 4096) and 160x128 (M = 1250, 1280)."""
     import torch
     x, w = synth.linear_inputs(300 + M, f"tile{d_in}.{d_out}", M, d_in, d_out)
     ref = oracle.linear(x, w)

@@ -131,15 +131,16 @@ def sampled_full_size(sv, dev, M, d_in, d_out, seed, out_dtype, n_cols=48):
 # Full-size linears the plan splits: the Llama-3.1-8B down projection at
 # every swept M (32x64, 128x128, 256x128, 320x128 and 320x256 tiles), a
 # ragged 320-row tile (M = 301) and 256x256 tiles (M = 1000), the O
-# projection at M = 1280 (two splits), and the Llama-3.1-70B down
+# projection at M = 1100 (320x128 tiles, two splits; at M = 1280 an
+# exact-fill 160x128 tile runs unsplit), and the Llama-3.1-70B down
 # projection (128x256 and 256x256 tiles).
 FULL = [(5, 14336, 4096), (20, 14336, 4096), (80, 14336, 4096), (160, 14336, 4096),
         (301, 14336, 4096), (320, 14336, 4096), (1000, 14336, 4096), (1280, 14336, 4096),
-        (1280, 4096, 4096), (80, 28672, 8192), (160, 28672, 8192), (640, 8192, 10240),
+        (1100, 4096, 4096), (80, 28672, 8192), (160, 28672, 8192), (640, 8192, 10240),
         # partial tiles stored through the LDS staging block with d_out not
         # a multiple of 4 (element by element at every row): 256x128,
         # 256x256, 320x128, 320x256 and 128x256 tiles
-        (160, 8192, 8191), (160, 14336, 8191), (320, 8192, 4095), (320, 14336, 10239),
+        (160, 8192, 8191), (160, 14336, 8191), (320, 14336, 4095), (320, 14336, 10239),
         (640, 14336, 2047)]
 
 

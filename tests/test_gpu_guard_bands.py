@@ -55,10 +55,12 @@ def ptr(t):
 
 # (M, d_in, d_out): the streaming kernel (M <= 16), the skinny and two-buffer
 # MFMA kernels (d_in not a multiple of 64), the tile kernel with direct
-# stores, in k-groups, with the LDS staging epilogue at a ragged width, and
-# split by columns (a row stride wider than each launch's columns)
+# stores, in k-groups, with the LDS staging epilogue at a ragged width, split
+# by columns (a row stride wider than each launch's columns), and the
+# exact-fill 80x64 (ten waves) and 160x128 tiles
 GEMM = [(5, 4096, 777), (16, 1032, 300), (40, 1032, 777), (200, 1032, 777),
-        (20, 512, 4095), (20, 4096, 4096), (301, 64, 24001), (1250, 64, 28003)]
+        (20, 512, 4095), (20, 4096, 4096), (301, 64, 24001), (1250, 64, 28003),
+        (300, 128, 4095), (1250, 64, 4095)]
 
 
 @pytest.mark.parametrize("M,d_in,d_out", GEMM)
@@ -77,7 +79,7 @@ def test_gemm_guard_bands(sv, dev, M, d_in, d_out):
 # shapes the split plan splits: staged fp32 partials at a ragged width
 # (320x128 and 256x256 tiles), 64x128 tiles, and the split-sum kernel's
 # scalar tail (M * d_out not a multiple of 4)
-SPLIT = [(320, 8192, 4095), (160, 14336, 8191), (37, 8192, 2050), (9, 5120, 301)]
+SPLIT = [(320, 14336, 4095), (160, 14336, 8191), (37, 8192, 2050), (9, 5120, 301)]
 
 
 @pytest.mark.parametrize("M,d_in,d_out", SPLIT)
