@@ -710,19 +710,23 @@ static hipError_t launch_tile_t(const uint16_t* x, const void* w, const float* w
 // so that several of them share a CU, or eight in k-groups when their tiles
 // fit one round. The last kExactFillShapes are candidates only where their
 // tiles number exactly one per CU: 80x64 (ten waves in two k-groups),
-// 160x128 (eight waves), 160x224 (fourteen waves) and 160x192 (eight).
+// 160x128 (eight waves), 160x224 (fourteen waves), 160x192 (eight) and
+// 64x48 (eight waves in two k-groups).
 // Measured on the Llama-3.1-8B O projection (4096 -> 4096): at M = 320,
 // 80x64 22.7 against 26.6 us (128x64); at M = 1280, 160x128 48.3 against
 // 55.8 (320x128 tiles, two splits); on gate/up (4096 -> 28672) at M = 320,
 // 160x224 85-86 against 92-93 us (320x128), and on the Llama-3.1-70B
 // gate/up (8192 -> 57344) at M = 160, 195 against 242; 160x192 on QKV
-// (4096 -> 6144) at M = 1280, 66 against 67-69 us (256x128).
+// (4096 -> 6144) at M = 1280, 66 against 67-69 us (256x128); 64x48 on
+// QKV at M = 80 (B = 16 step 4.33 against 4.37 ms with 64x64 tiles). A
+// 32x112 exact fill for gate/up at M = 20 made the B = 4 step 6 % slower
+// and is not in the table.
 static const int kTileShapes[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128},
                                      {128, 64},  {64, 128},  {64, 64},   {64, 32},
                                      {32, 32},   {32, 16},   {32, 64},   {320, 128},
                                      {320, 256}, {80, 64},   {160, 128}, {160, 224},
-                                     {160, 192}};
-constexpr int kExactFillShapes = 4;
+                                     {160, 192}, {64, 48}};
+constexpr int kExactFillShapes = 5;
 
 // Time model of one launch, per reduction element: a tile costs
 // a * (BM + wb BN) (operand lines into LDS and out to the matrix cores; wb
@@ -894,6 +898,7 @@ hipError_t launch_gemm_mfma(const uint16_t* x, const uint16_t* w, void* y, bool 
       case 14: return launch_tile_t<160, 128, 2, 4, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
       case 15: return launch_tile_t<160, 224, 2, 3, 64, 14, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
       case 16: return launch_tile_t<160, 192, 2, 3, 64, 8, 1, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
+      case 17: return launch_tile_t<64, 48, 4, 4, 64, 8, 2, 16>(x, w, nullptr, y, out_bf16, M, K, N, s);
       default: return hipErrorInvalidValue;
     }
   }

@@ -108,7 +108,8 @@ def test_mfma_kernel(sv, dev, M):
                                            (301, 64, 24001), (640, 64, 28675), (1250, 64, 28003),
                                            (1250, 64, 28004), (300, 128, 4095), (1250, 64, 4095),
                                            (320, 192, 4096), (1280, 128, 4096), (300, 64, 28600),
-                                           (320, 128, 28672), (1250, 64, 6100)])
+                                           (320, 128, 28672), (1250, 64, 6100),
+                                           (100, 64, 6143), (128, 128, 6144)])
 def test_tile_kernel(sv, dev, M, d_in, d_out):
     """The pipelined tile kernel (d_in a multiple of 64, M above 8): ragged
     M and N tails, one or many stages (d_in 64 leaves k-groups without a
@@ -125,8 +126,9 @@ def test_tile_kernel(sv, dev, M, d_in, d_out):
     element, fp32 rows in 16-byte stores). The exact-fill tiles, taken where
     their tiles number one per CU: 80x64 in two k-groups of five waves (M =
     300, 320 with d_out = 4095, 4096), 160x128 (M = 1250, 1280), 160x224
-    on fourteen waves (M = 300, 320 with d_out = 28600, 28672) and 160x192
-    (M = 1250, d_out = 6100)."""
+    on fourteen waves (M = 300, 320 with d_out = 28600, 28672), 160x192
+    (M = 1250, d_out = 6100) and 64x48 in two k-groups of four waves (M =
+    100, 128 with d_out = 6143, 6144)."""
     import torch
     x, w = synth.linear_inputs(300 + M, f"tile{d_in}.{d_out}", M, d_in, d_out)
     ref = oracle.linear(x, w)

@@ -57,10 +57,11 @@ def ptr(t):
 # MFMA kernels (d_in not a multiple of 64), the tile kernel with direct
 # stores, in k-groups, with the LDS staging epilogue at a ragged width, split
 # by columns (a row stride wider than each launch's columns), and the
-# exact-fill 80x64 (ten waves), 160x128, 160x224 (fourteen waves) and 160x192 tiles
+# exact-fill 80x64 (ten waves), 160x128, 160x224 (fourteen waves), 160x192 and 64x48 tiles
 GEMM = [(5, 4096, 777), (16, 1032, 300), (40, 1032, 777), (200, 1032, 777),
         (20, 512, 4095), (20, 4096, 4096), (301, 64, 24001), (1250, 64, 28003),
-        (300, 128, 4095), (1250, 64, 4095), (300, 64, 28600), (1250, 64, 6100)]
+        (300, 128, 4095), (1250, 64, 4095), (300, 64, 28600), (1250, 64, 6100),
+        (90, 64, 6120)]
 
 
 @pytest.mark.parametrize("M,d_in,d_out", GEMM)
