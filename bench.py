@@ -342,6 +342,20 @@ def measure_ceilings(sv, dev, read_bytes=4 << 30, reps=5, mfma_iters=2048):
     best = max(shapes, key=shapes.get)
     out = {"read_gbs": shapes[best], "read_best_shape": best, "read_gbs_by_shape": shapes,
            "read_bytes": read_bytes}
+    # the same read with the loads going straight to LDS (the tile kernels'
+    # operand path), one workgroup per CU
+    lds = {}
+    for loads in (1, 2, 4, 8):
+        sv.probe_read_lds(buf, sink, loads)
+        e0.record()
+        for _ in range(reps):
+            sv.probe_read_lds(buf, sink, loads)
+        e1.record()
+        torch.cuda.synchronize()
+        lds[f"{8 * loads}KB_per_CU(1wg,{loads}ld)"] = \
+            read_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    out["read_lds_gbs"] = max(lds.values())
+    out["read_lds_gbs_by_shape"] = lds
     del buf
     for shape in (16, 32):
         flops = sv.probe_mfma(shape, mfma_iters, sink)

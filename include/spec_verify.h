@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 7
+#define SPEC_ABI_VERSION 8
 
 /* Status codes. */
 #define SPEC_OK 0
@@ -339,6 +339,14 @@ int spec_chain_error(void* workspace, int* error);
  * well above the 256 MB Infinity Cache (e.g. 4 GiB).
  *   buf   device, 16-byte aligned; bytes a positive multiple of 16.
  *
+ * spec_probe_read_lds -- the same front-to-back read, one workgroup of
+ * eight waves per compute unit, with the loads going straight to LDS
+ * (global_load_lds, the path that feeds the tile kernels' operand rings):
+ * each wave keeps `loads_per_lane` (1, 2, 4 or 8) one-kilobyte loads in
+ * flight into a ring of as many LDS slots. bytes / time is the read
+ * bandwidth that path can reach. Arguments, errors and sink as for
+ * spec_probe_read.
+ *
  * spec_probe_mfma -- independent chains of bf16 MFMAs on register operands
  * (no memory traffic): `iters` rounds per wave of eight independent
  * v_mfma_f32_16x16x32_bf16 (shape 16) or four v_mfma_f32_32x32x16_bf16
@@ -349,6 +357,8 @@ int spec_chain_error(void* workspace, int* error);
  */
 int spec_probe_read(const void* buf, size_t bytes, int loads_per_lane, int wgs_per_cu,
                     void* sink, void* stream);
+int spec_probe_read_lds(const void* buf, size_t bytes, int loads_per_lane, void* sink,
+                        void* stream);
 int spec_probe_mfma(int shape, int iters, void* sink, double* flops, void* stream);
 
 /*

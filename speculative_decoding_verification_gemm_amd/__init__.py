@@ -67,6 +67,7 @@ SIGNATURES = {
     "spec_chain_error": (_i, [_p, ctypes.POINTER(ctypes.c_int)]),
     "spec_chain_reset": (_i, [_p, ctypes.c_uint]),
     "spec_probe_read": (_i, [_p, _z, _i, _i, _p, _p]),
+    "spec_probe_read_lds": (_i, [_p, _z, _i, _p, _p]),
     "spec_probe_mfma": (_i, [_i, _i, _p, ctypes.POINTER(ctypes.c_double), _p]),
     "spec_verify": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _z, _p]),
     "spec_verify_warped": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _i, _i, _i, _f, _f, _p, _p, _p,
@@ -389,6 +390,13 @@ def probe_read(buf, sink, loads_per_lane=4, wgs_per_cu=1):
     a device tensor of at least 4 bytes."""
     check(lib.spec_probe_read(_ptr(buf), buf.numel() * buf.element_size(), int(loads_per_lane),
                               int(wgs_per_cu), _ptr(sink), _stream()))
+
+
+def probe_read_lds(buf, sink, loads_per_lane=4):
+    """spec_probe_read_lds over the whole of `buf` (a device tensor); `sink`
+    is a device tensor of at least 4 bytes."""
+    check(lib.spec_probe_read_lds(_ptr(buf), buf.numel() * buf.element_size(),
+                                  int(loads_per_lane), _ptr(sink), _stream()))
 
 
 def probe_mfma(shape, iters, sink):

@@ -524,6 +524,25 @@ int spec_probe_read(const void* buf, size_t bytes, int loads_per_lane, int wgs_p
                   "spec_probe_read");
 }
 
+int spec_probe_read_lds(const void* buf, size_t bytes, int loads_per_lane, void* sink,
+                        void* stream) {
+  clear_error();
+  if (!buf || !sink) return fail(SPEC_ERR_INVALID_ARGUMENT, "null buf or sink");
+  if (loads_per_lane != 1 && loads_per_lane != 2 && loads_per_lane != 4 && loads_per_lane != 8)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "loads_per_lane=%d (1, 2, 4 or 8)", loads_per_lane);
+  if (bytes < 16 || bytes % 16 != 0)
+    return fail(SPEC_ERR_INVALID_ARGUMENT, "bytes=%zu must be a positive multiple of 16", bytes);
+  if (!aligned(buf, 16) || !aligned(sink, 4))
+    return fail(SPEC_ERR_ALIGNMENT, "buf must be 16-byte and sink 4-byte aligned");
+  int cus = 0;
+  int rc = check_device(&cus);
+  if (rc != SPEC_OK) return rc;
+  return launched(specv::launch_probe_read_lds(buf, bytes, loads_per_lane,
+                                               static_cast<unsigned*>(sink), cus,
+                                               static_cast<hipStream_t>(stream)),
+                  "spec_probe_read_lds");
+}
+
 int spec_probe_mfma(int shape, int iters, void* sink, double* flops, void* stream) {
   clear_error();
   if (shape != 16 && shape != 32)

@@ -133,6 +133,8 @@ hipError_t launch_sample_probs(const float* p, const float* q, const int32_t* n_
 // grid * 4 waves * iters * 131072 (8 chains of 16x16x32 or 4 of 32x32x16).
 hipError_t launch_probe_read(const void* buf, size_t bytes, int loads, unsigned* sink, int grid,
                              hipStream_t s);
+hipError_t launch_probe_read_lds(const void* buf, size_t bytes, int loads, unsigned* sink,
+                                 int grid, hipStream_t s);
 hipError_t launch_probe_mfma(int shape, int iters, unsigned* sink, int grid, hipStream_t s);
 
 // Fused sampling stage of spec_verify (logits in, tokens out).

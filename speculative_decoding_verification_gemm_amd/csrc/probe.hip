@@ -42,6 +42,43 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(
   if (acc == never) sink[0] = acc;
 }
 
+// s_waitcnt vmcnt(N), the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void probe_wait_vmcnt() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// The same sweep with the loads going straight to LDS (global_load_lds, the
+// path the tile kernels feed their operand rings with): each wave keeps a
+// ring of U one-kilobyte slots and U loads in flight, waiting for the
+// oldest before its slot is loaded again. Every wave runs the same number
+// of iterations; lanes past the end reload the last unit.
+template <int U>
+__global__ __launch_bounds__(kProbeThreads) void probe_read_lds_kernel(
+    const u32x4* __restrict__ buf, size_t units, unsigned never, unsigned* sink) {
+  __shared__ u32x4 ring[kProbeThreads / 64 * U * 64];
+  const size_t T = blockDim.x, G = gridDim.x;
+  const size_t stride = G * T;
+  const size_t n_it = (units + stride - 1) / stride;
+  const size_t i0 = (size_t)blockIdx.x * T + threadIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const SPECV_PROBE_GLOBAL u32x4* src = (const SPECV_PROBE_GLOBAL u32x4*)buf;
+  for (size_t it = 0; it < n_it; ++it) {
+    if (it >= U) probe_wait_vmcnt<U - 1>();
+    const size_t i = min(i0 + it * stride, units - 1);
+    __attribute__((address_space(3))) void* dst =
+        (__attribute__((address_space(3))) void*)(ring + (wave * U + (int)(it % U)) * 64);
+    __builtin_amdgcn_global_load_lds((const SPECV_PROBE_GLOBAL void*)(src + i), dst, 16, 0, 0);
+  }
+  probe_wait_vmcnt<0>();
+  __syncthreads();
+  const u32x4 v = ring[threadIdx.x];
+  const unsigned acc = v.x ^ v.y ^ v.z ^ v.w;
+  if (acc == never) sink[0] = acc;
+}
+
 // NCH independent accumulator chains per wave, each `iters` MFMAs long, on
 // register operands only (no memory traffic inside the loop). The
 // accumulators are folded and stored only if they equal `never`.
@@ -92,6 +129,22 @@ hipError_t launch_probe_read(const void* buf, size_t bytes, int loads, unsigned*
                                bytes / 16, 0x9E3779B9u, sink); break;
     default: hipLaunchKernelGGL(probe_read_kernel<8>, dim3(grid), dim3(kProbeThreads), 0, s, b,
                                 bytes / 16, 0x9E3779B9u, sink); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_read_lds(const void* buf, size_t bytes, int loads, unsigned* sink,
+                                 int grid, hipStream_t s) {
+  const u32x4* b = static_cast<const u32x4*>(buf);
+  switch (loads) {
+    case 1: hipLaunchKernelGGL(probe_read_lds_kernel<1>, dim3(grid), dim3(kProbeThreads), 0, s,
+                               b, bytes / 16, 0x9E3779B9u, sink); break;
+    case 2: hipLaunchKernelGGL(probe_read_lds_kernel<2>, dim3(grid), dim3(kProbeThreads), 0, s,
+                               b, bytes / 16, 0x9E3779B9u, sink); break;
+    case 4: hipLaunchKernelGGL(probe_read_lds_kernel<4>, dim3(grid), dim3(kProbeThreads), 0, s,
+                               b, bytes / 16, 0x9E3779B9u, sink); break;
+    default: hipLaunchKernelGGL(probe_read_lds_kernel<8>, dim3(grid), dim3(kProbeThreads), 0, s,
+                                b, bytes / 16, 0x9E3779B9u, sink); break;
   }
   return hipGetLastError();
 }

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(sv):
     names = declared_functions()
-    assert len(names) == 27
+    assert len(names) == 28
     for n in names:
         assert hasattr(sv.lib, n), n
 
@@ -33,7 +33,7 @@ def test_binding_covers_exactly_the_header(sv):
 
 
 def test_version_and_status_strings(sv):
-    assert sv.abi_version() == 7
+    assert sv.abi_version() == 8
     for code, name in [(0, b"SPEC_OK"), (-1, b"SPEC_ERR_INVALID_ARGUMENT"),
                        (-2, b"SPEC_ERR_ALIGNMENT"), (-3, b"SPEC_ERR_UNSUPPORTED"),
                        (-4, b"SPEC_ERR_WORKSPACE"), (-5, b"SPEC_ERR_HIP")]:
@@ -164,6 +164,12 @@ def test_probe_rejects(sv):
     assert sv.lib.spec_probe_read(A, 1024, 3, 1, A, None) == -1
     assert sv.lib.spec_probe_read(A, 1024, 4, 0, A, None) == -1
     assert sv.lib.spec_probe_read(A + 8, 1024, 4, 1, A, None) == -2
+    assert sv.lib.spec_probe_read_lds(None, 1024, 4, A, None) == -1
+    assert sv.lib.spec_probe_read_lds(A, 1024, 4, None, None) == -1
+    assert sv.lib.spec_probe_read_lds(A, 1000, 4, A, None) == -1
+    assert sv.lib.spec_probe_read_lds(A, 1024, 3, A, None) == -1
+    assert sv.lib.spec_probe_read_lds(A + 8, 1024, 4, A, None) == -2
+    assert sv.lib.spec_probe_read_lds(A, 1024, 4, A + 2, None) == -2
     assert sv.lib.spec_probe_mfma(8, 10, A, ctypes.byref(f), None) == -1
     assert sv.lib.spec_probe_mfma(16, 0, A, ctypes.byref(f), None) == -1
     assert sv.lib.spec_probe_mfma(32, 10, None, ctypes.byref(f), None) == -1

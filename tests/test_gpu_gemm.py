@@ -215,3 +215,19 @@ def test_deterministic(sv, dev, M, d_out):
     b = sv.verify_gemm(x, w)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("loads", [1, 2, 4, 8])
+def test_read_probes_run(sv, dev, loads):
+    """The read probes (into registers, and straight to LDS) sweep a buffer
+    with a ragged tail (not a whole number of grid sweeps) and write nothing:
+    the sink keeps its value, and the buffer is unchanged."""
+    import torch
+    n = (48 << 20) + 16 * 37
+    buf = torch.arange(n // 4, dtype=torch.int32, device=dev)
+    sink = torch.full((4,), 7, dtype=torch.int32, device=dev)
+    sv.probe_read(buf, sink, loads, 1)
+    sv.probe_read_lds(buf, sink, loads)
+    torch.cuda.synchronize()
+    assert torch.equal(sink.cpu(), torch.full((4,), 7, dtype=torch.int32))
+    assert torch.equal(buf[-5:].cpu(), torch.arange(n // 4 - 5, n // 4, dtype=torch.int32))
